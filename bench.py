@@ -1,0 +1,367 @@
+#!/usr/bin/env python3
+"""Benchmark of the R-SWA hot path on one MI355X.
+
+A step is one decode step of the whole batch: K1 append of one new K/V row per sequence and head,
+then K2 split-K decode attention over prefix u window. The headline workload is the batched
+single-page decode (64 sequences, bf16 K/V with 1% x8 outliers, m = 272, n = 128, T = 6000):
+warmup steps t = 1..W, then K timed steps. Inputs for every step are resident in HBM before timing.
+
+Also reported: per-step latency vs t, the decode kernel's algorithmic HBM GB/s against the 8 TB/s
+peak (HIP events around every decode launch on the launch stream), the multi-page growth curve
+(R-SWA vs full causal, --growth), the masked prefill in TFLOP/s against the bf16 MFMA peak, and the
+fp64 oracle timed on a bounded sample on the host cores (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "R-SWA decode tok/s + HBM GB/s vs T (1 GPU); masked prefill TFLOP/s"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+H, D = 16, 128
+DECODE_SOURCES = ["windowed_attention_amd/csrc/decode.hip", "windowed_attention_amd/csrc/device.h",
+                  "windowed_attention_amd/csrc/kernels.h"]
+PREFILL_SOURCES = ["windowed_attention_amd/csrc/prefill.hip",
+                   "windowed_attention_amd/csrc/device.h", "windowed_attention_amd/csrc/kernels.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5800)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", choices=["batched", "single", "multipage", "ragged"],
+                    default="batched")
+    ap.add_argument("--mode", choices=["rswa", "full"], default="rswa")
+    ap.add_argument("--chunk", type=int, default=0, help="decode rows per split (0 = automatic)")
+    ap.add_argument("--grid", type=int, default=0, help="decode workgroups (0 = automatic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--growth", action="store_true", help="multi-page R-SWA vs full-causal curve")
+    ap.add_argument("--no-kernel-events", action="store_true")
+    ap.add_argument("--prefill-runs", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------------------------------------
+# decode
+# ------------------------------------------------------------------------------------------------
+def decode_workload(name: str):
+    import workloads as W
+    return {"single": lambda: W.decode_config(1), "batched": lambda: W.decode_config(2),
+            "multipage": lambda: W.decode_config(3), "ragged": lambda: W.varlen_config(0)}[name]()
+
+
+def upload(arr, dtype):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).cuda()
+
+
+def decode_bytes(wl, t: int, full: bool, out_elem: int) -> int:
+    """Algorithmic HBM bytes of one decode launch at step t: every live K and V row once, q read,
+    output written (the append's own traffic is counted separately)."""
+    e = 2 if wl.dtype == "bf16" else 4
+    act = wl.steps >= t
+    live = wl.prefix_len.astype(np.int64) + (np.minimum(t, wl.steps) if full else
+                                             np.minimum(wl.window, t))
+    rows = int(live[act].sum())
+    nb = int(act.sum())
+    return rows * 2 * H * D * e + nb * H * D * (e + out_elem)
+
+
+def append_bytes(wl, t: int) -> int:
+    e = 2 if wl.dtype == "bf16" else 4
+    return int((wl.steps >= t).sum()) * H * D * e * 4  # k, v read; k, v written
+
+
+def run_decode(args, wl, mode_full: bool, steps: int, warmup: int, kernel_events: bool):
+    import torch
+    import windowed_attention_amd as wa
+    lib = wa._lib
+    dev_q, dev_k, dev_v = upload(wl.q, wl.dtype), upload(wl.k, wl.dtype), upload(wl.v, wl.dtype)
+    pk, pv = upload(wl.prefix_k, wl.dtype), upload(wl.prefix_v, wl.dtype)
+    kvdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    mode = wa.MODE_FULL_CAUSAL if mode_full else wa.MODE_RSWA
+    ragged = bool((wl.steps != wl.steps.max()).any())
+    total = warmup + steps
+    if total > wl.T:
+        raise SystemExit(f"warmup + steps = {total} exceeds the workload's T = {wl.T}")
+    cache = wa.RswaCache(pk, pv, wl.prefix_len, None if mode_full else wl.window, mode=mode,
+                         max_steps=wl.steps if mode_full else None, kv_dtype=kvdt)
+    cache.set_decode_split(args.chunk, args.grid)
+    out_dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    out = torch.empty((wl.batch, H, D), dtype=out_dt, device="cuda")
+    out_code = wa.BF16 if out_dt == torch.bfloat16 else wa.F32
+    act = None
+    if ragged:
+        act = torch.from_numpy(np.stack([wl.active(t) for t in range(1, wl.T + 1)])).cuda()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    h = cache.handle
+    step_bytes = wl.batch * H * D * dev_q.element_size()
+    qb, kb, vb = dev_q.data_ptr(), dev_k.data_ptr(), dev_v.data_ptr()
+    ob = out.data_ptr()
+    ab = act.data_ptr() if act is not None else None
+
+    def step(t):  # t is 1-based
+        o = (t - 1) * step_bytes
+        a = None if ab is None else ab + (t - 1) * wl.batch
+        r = lib.rswa_append_kv(h, kb + o, vb + o, a, sp)
+        if r:
+            raise RuntimeError(f"append failed: {r} {lib.rswa_last_error()}")
+        return o, a
+
+    def decode(o, a):
+        r = lib.rswa_decode_attn(h, qb + o, ob, out_code, ctypes.c_float(0.0), a, sp)
+        if r:
+            raise RuntimeError(f"decode failed: {r} {lib.rswa_last_error()}")
+
+    for t in range(1, warmup + 1):
+        decode(*step(t))
+    torch.cuda.synchronize()
+
+    ev_k = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(steps)] if kernel_events else []
+    block = 64
+    ev_blk = [torch.cuda.Event(enable_timing=True) for _ in range(steps // block + 2)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    nb = 0
+    for i in range(steps):
+        t = warmup + 1 + i
+        if i % block == 0:
+            ev_blk[nb].record()
+            nb += 1
+        o, a = step(t)
+        if kernel_events:
+            ev_k[i][0].record()
+            decode(o, a)
+            ev_k[i][1].record()
+        else:
+            decode(o, a)
+    ev_blk[nb].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    elapsed_ms = start.elapsed_time(end)
+    steps_done = cache.steps()
+    cache.close()
+
+    kern_ms = np.array([a.elapsed_time(b) for a, b in ev_k]) if kernel_events else None
+    lat = []
+    for j in range(nb):
+        t_lo = warmup + 1 + j * block
+        n_in = min(block, warmup + steps - t_lo + 1)
+        lat.append((t_lo + n_in // 2, ev_blk[j].elapsed_time(ev_blk[j + 1]) * 1e3 / n_in))
+    out_elem = out.element_size()
+    ts = range(warmup + 1, warmup + steps + 1)
+    dec_bytes = np.array([decode_bytes(wl, t, mode_full, out_elem) for t in ts], dtype=np.float64)
+    app_bytes = np.array([append_bytes(wl, t) for t in ts], dtype=np.float64)
+    tokens = int(sum(int((wl.steps >= t).sum()) for t in ts))
+    return dict(elapsed_ms=elapsed_ms, wall_s=wall, kern_ms=kern_ms, lat=lat,
+                dec_bytes=dec_bytes, app_bytes=app_bytes, tokens=tokens,
+                steps_done=steps_done.tolist())
+
+
+def flatness(lat, n, T):
+    ts = np.array([t for t, _ in lat])
+    us = np.array([u for _, u in lat])
+    late = us[(ts >= T - 500) & (ts <= T)]
+    early = us[(ts >= n + 1) & (ts <= n + 500)]
+    if late.size == 0 or early.size == 0:
+        return None
+    return float(np.median(late) / np.median(early))
+
+
+def traffic_from_profile(kind: str, src_hash: str, per_launch_units: float | None = None):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE summaries, scaled by
+    the same counters' reading for a plain copy of known size; None if the kernel source changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------------------------------------------
+# prefill
+# ------------------------------------------------------------------------------------------------
+def visible_pairs(S: int, m: int, n: int, prefix_causal: bool = False) -> int:
+    """Visible (query, key) pairs of one sequence under the R-SWA prefill mask (closed form)."""
+    pre = m * (m + 1) // 2 if prefix_causal else m * m
+    outs = S - m
+    win = 0
+    for i in range(outs):  # output i sees min(n, i + 1) outputs
+        win += min(n, i + 1)
+    return pre + outs * m + win
+
+
+def run_prefill(args):
+    import torch
+    import windowed_attention_amd as wa
+    import workloads as W
+    pw = W.prefill_config()
+    q, k, v = upload(pw.q, "bf16"), upload(pw.k, "bf16"), upload(pw.v, "bf16")
+    cu = torch.tensor(pw.cu_seqlens, dtype=torch.int32, device="cuda")
+    m = torch.tensor(pw.prefix_len, dtype=torch.int32, device="cuda")
+    n = torch.tensor(pw.window, dtype=torch.int32, device="cuda")
+    S = int(pw.cu_seqlens[-1])
+    out = torch.empty((S, H, D), dtype=torch.bfloat16, device="cuda")
+    try:
+        wa.rswa_prefill_attn(q, k, v, cu, m, n, out=out, max_seqlen=S)
+    except wa.RswaError as e:
+        if e.status == -2:
+            return None
+        raise
+    for _ in range(3):
+        wa.rswa_prefill_attn(q, k, v, cu, m, n, out=out, max_seqlen=S)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(args.prefill_runs):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        wa.rswa_prefill_attn(q, k, v, cu, m, n, out=out, max_seqlen=S)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    med_ms = float(np.median(times))
+    pairs = visible_pairs(S, int(pw.prefix_len[0]), int(pw.window[0]))
+    flops = 4.0 * D * H * pairs
+    tflops = flops / (med_ms * 1e-3) / 1e12
+    return dict(workload=pw.name, ms=med_ms, tflops=tflops, flop=flops, visible_pairs_per_head=pairs,
+                roofline=dict(bound="mfma", achieved=tflops, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                              frac=tflops / PEAK_BF16_TFLOPS,
+                              traffic=traffic_from_profile("prefill",
+                                                           source_hash(PREFILL_SOURCES))))
+
+
+# ------------------------------------------------------------------------------------------------
+# cpu baseline: the fp64 oracle on a bounded sample
+# ------------------------------------------------------------------------------------------------
+def cpu_baseline(wl, seconds: float):
+    import oracle as O
+    from workloads import to_f64
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        return _cpu_baseline(wl, seconds, O, to_f64)
+
+
+def _cpu_baseline(wl, seconds, O, to_f64):
+    rng = np.random.default_rng(0)
+    n = int(wl.window[0])
+    cand = sorted({1, 2, n - 1, n, n + 1, 2 * n, 1000, wl.T - 1, wl.T} |
+                  set(rng.integers(1, wl.T + 1, size=16).tolist()))
+    cand = [t for t in cand if 1 <= t <= wl.T]
+    pre = {}
+    tokens = 0
+    t0 = time.perf_counter()
+    done = []
+    while time.perf_counter() - t0 < seconds:
+        t = cand[len(done) % len(cand)]
+        b = int(rng.integers(0, wl.batch))
+        if wl.steps[b] < t:
+            continue
+        if b not in pre:
+            pk, pv = wl.prefix(b)
+            pre[b] = (to_f64(pk, wl.dtype), to_f64(pv, wl.dtype))
+        O.decode_step(to_f64(wl.q[t - 1, b], wl.dtype), pre[b][0], pre[b][1],
+                      to_f64(wl.k[:t, b], wl.dtype), to_f64(wl.v[:t, b], wl.dtype), t,
+                      int(wl.window[b]))
+        tokens += 1
+        done.append(t)
+    el = time.perf_counter() - t0
+    return dict(value=tokens / el, unit="tok/s", cores=1, kind="oracle",
+                sample=f"{tokens} (sequence, step) decode outputs of this workload, steps drawn from "
+                       f"{{1,2,n-1,n,n+1,2n,1000,T-1,T}} + 16 seeded random, each computed "
+                       f"independently from the growing cache in fp64 ({el:.1f} s, 1 thread)")
+
+
+# ------------------------------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has no "
+              f"multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import windowed_attention_amd  # noqa: F401  (fails loudly if the HIP library is missing)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    res = dict(metric=METRIC, n_gpus=1, higher_is_better=True, scaling="weak", vs_baseline=None,
+               data="synthetic")
+    wl = None
+    if not args.no_decode:
+        t0 = time.perf_counter()
+        wl = decode_workload(args.workload)
+        log(f"[bench] generated {wl.name} in {time.perf_counter() - t0:.1f} s")
+        full = args.mode == "full"
+        warmup = args.warmup
+        steps = min(args.steps, wl.T - warmup)
+        r = run_decode(args, wl, full, steps, warmup, not args.no_kernel_events)
+        log(f"[bench] decode: {steps} steps in {r['elapsed_ms']:.1f} ms "
+            f"(host wall {r['wall_s']:.2f} s)")
+        ms_step = r["elapsed_ms"] / steps
+        tok_s = r["tokens"] / (r["elapsed_ms"] * 1e-3)
+        step_bytes = float((r["dec_bytes"] + r["app_bytes"]).mean())
+        res.update(value=tok_s, unit="tok/s", steps=steps, warmup=warmup, ms_per_step=ms_step,
+                   dtype="f32",
+                   config=dict(workload=wl.name, batch=wl.batch, prefix_len=int(wl.prefix_len[0]),
+                               window=int(wl.window[0]), T=int(wl.T), kv_dtype=wl.dtype,
+                               mode=args.mode, timed_t=[warmup + 1, warmup + steps]))
+        res["hbm_gbs_step"] = step_bytes / (ms_step * 1e-3) / 1e9
+        if r["kern_ms"] is not None:
+            kms = float(r["kern_ms"].mean())
+            ach = float(r["dec_bytes"].mean()) / (kms * 1e-3) / 1e9
+            res["roofline"] = dict(bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
+                                   frac=ach / PEAK_HBM_GBS,
+                                   traffic=traffic_from_profile("decode",
+                                                                source_hash(DECODE_SOURCES)),
+                                   kernel="rswa decode (split-K + merge)",
+                                   avg_launch_us=kms * 1e3,
+                                   bytes_per_launch=float(r["dec_bytes"].mean()))
+        res["latency_vs_t"] = [[int(t), round(u, 3)] for t, u in r["lat"]]
+        res["flatness"] = flatness(r["lat"], int(wl.window[0]), warmup + steps)
+    if not args.no_prefill:
+        p = run_prefill(args)
+        if p is not None:
+            res["prefill"] = p
+            log(f"[bench] prefill: {p['ms']:.3f} ms, {p['tflops']:.1f} TFLOP/s")
+    if wl is not None and not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

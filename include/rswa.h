@@ -1,0 +1,172 @@
+/*
+ * rswa.h - C ABI of the MI355X (gfx950) Reference Sliding Window Attention library.
+ *
+ * What is computed. Output token t of a sequence attends to the whole reference prefix P of
+ * L_m = m tokens (visual tokens plus prompt, always visible) and to its last n output tokens, the
+ * current one included: N(t) = P u D_n(t). The decode KV cache is therefore a constant
+ * m + min(n, t) rows: a static prefix region plus an n-slot ring that overwrites the oldest output
+ * on every append. Standard causal attention ("full causal" mode here) keeps all m + t rows.
+ *   - deep dive "Unlimited-OCR" (ai-news-5min): the N(t) code block and the cache-size formula
+ *     C(T) = L_m + min(n, T) <= L_m + n;
+ *   - GeekNews "Unlimited OCR": R-SWA section (two-segment window of size m + n), KV cache
+ *     management section (L_m + T vs L_m + min(n, T)), model architecture section (queue of
+ *     capacity m + n that evicts the oldest output KV on every new token).
+ *
+ * Conventions shared by every entry point.
+ *   - H = num_heads, D = head_dim. D must be 128 (RSWA_E_UNSUPPORTED otherwise).
+ *   - Pointers named *_dev are device pointers on the current HIP device (e.g. a torch tensor's
+ *     data_ptr()); pointers named *_host are host memory. The caller owns every buffer it passes
+ *     and must keep it alive until the stream has passed the call.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Every call only
+ *     enqueues work on that stream and returns; nothing blocks unless stated.
+ *   - Arguments are validated on the host before anything is enqueued: an invalid call returns an
+ *     error status and changes no state. No C++ exception crosses this ABI.
+ *   - Element types: RSWA_BF16 is bfloat16 (16-bit patterns), RSWA_F32 is IEEE float32. All
+ *     attention arithmetic is float32; a bf16 output is the round-to-nearest-even of the float32
+ *     result.
+ *   - Inputs are already position-encoded: the library does no position arithmetic, so the ring's
+ *     slot order never matters (softmax attention is invariant under key permutation).
+ *   - A cache is not thread-safe; distinct caches are independent.
+ */
+#ifndef RSWA_H
+#define RSWA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rswa_status {
+  RSWA_OK = 0,
+  RSWA_E_INVALID = -1,     /* bad argument or state; nothing was enqueued */
+  RSWA_E_UNSUPPORTED = -2, /* valid but not implemented (e.g. head_dim != 128) */
+  RSWA_E_CAPACITY = -3,    /* full-causal append past max_steps, or storage too small */
+  RSWA_E_OOM = -4,         /* device allocation failed */
+  RSWA_E_HIP = -5,         /* a HIP runtime call or kernel launch failed */
+  RSWA_E_INTERNAL = -6     /* unexpected internal failure */
+} rswa_status;
+
+typedef enum rswa_dtype { RSWA_BF16 = 0, RSWA_F32 = 1 } rswa_dtype;
+
+/* RSWA_MODE_RSWA: prefix + n-slot ring (constant m + n rows).
+ * RSWA_MODE_FULL_CAUSAL: prefix + every output (m + max_steps rows), the standard-attention
+ * reference whose per-step cost grows with t. */
+typedef enum rswa_mode { RSWA_MODE_RSWA = 0, RSWA_MODE_FULL_CAUSAL = 1 } rswa_mode;
+
+/* Description of a batch of B decode sequences sharing one cache object. */
+typedef struct rswa_cache_desc {
+  int32_t batch;              /* B >= 1 */
+  int32_t num_heads;          /* H >= 1 */
+  int32_t head_dim;           /* D, must be 128 */
+  int32_t kv_dtype;           /* rswa_dtype of the cache, of q and of appended k / v */
+  int32_t mode;               /* rswa_mode */
+  const int32_t* prefix_len;  /* host [B]: m_b >= 0 */
+  const int32_t* window;      /* host [B]: n_b >= 1 (RSWA mode; ignored in FULL_CAUSAL) */
+  const int32_t* max_steps;   /* host [B]: appends allowed per sequence in FULL_CAUSAL (>= 1);
+                                 may be NULL in RSWA mode */
+  void* storage_dev;          /* caller-owned device storage of at least rswa_cache_bytes()
+                                 bytes, or NULL: the library allocates (and frees) it */
+  uint64_t storage_bytes;     /* size of storage_dev; ignored when storage_dev is NULL */
+} rswa_cache_desc;
+
+typedef struct rswa_cache rswa_cache; /* opaque; owned by the library */
+
+/* Storage layout, for callers that inspect or snapshot the cache. Sequence b owns
+ * R_b = m_b + cap_b rows per head (cap_b = n_b in RSWA mode, max_steps_b in FULL_CAUSAL mode):
+ *   K[b][h][r][i] at element seq_offset[b] + (h * R_b + r) * D + i,
+ *   V[b][h][r][i] at element seq_offset[b] + H * R_b * D + (h * R_b + r) * D + i,
+ * elements of kv_dtype. Rows [0, m_b) hold the prefix; in RSWA mode output index j (0-based) lives
+ * in row m_b + (j mod n_b); in FULL_CAUSAL mode in row m_b + j.
+ * Pure host computation (no HIP call). Any output pointer may be NULL. */
+rswa_status rswa_cache_plan(const rswa_cache_desc* desc, int64_t* seq_offset_host /* [B] */,
+                            int32_t* rows_host /* [B] */, uint64_t* storage_bytes_host);
+
+/* Bytes of storage the description needs (0 if the description is invalid). Host only. */
+uint64_t rswa_cache_bytes(const rswa_cache_desc* desc);
+
+/* Create a cache: take or allocate storage, copy every sequence's prefix K / V into rows
+ * [0, m_b) (the static prefix region, written once and never updated; GeekNews "Unlimited OCR",
+ * DeepEncoder section: visual tokens are encoded once and stay static), set every step counter
+ * t_b to 0. prefix_k_dev / prefix_v_dev: packed token-major [sum_b m_b][H][D] of kv_dtype
+ * (sequence b's rows follow sequence b-1's); may be NULL only if every m_b is 0. The prefix is
+ * copied, not aliased. Rows beyond the prefix are not touched. Enqueued on `stream`.
+ * Errors: RSWA_E_INVALID (desc, pointers), RSWA_E_UNSUPPORTED (head_dim), RSWA_E_CAPACITY
+ * (storage_bytes too small), RSWA_E_OOM, RSWA_E_HIP. On error *out is NULL. */
+rswa_status rswa_cache_create(const rswa_cache_desc* desc, const void* prefix_k_dev,
+                              const void* prefix_v_dev, void* stream, rswa_cache** out);
+
+/* K1, append / evict. For every sequence b with active_dev[b] != 0 (or every b when active_dev
+ * is NULL): write k_dev[b] / v_dev[b] ([B][H][D], kv_dtype) to row m_b + (t_b mod n_b) of every
+ * head (RSWA: overwriting output t_b - n_b once the ring is full, i.e. the oldest output is
+ * evicted; deep dive N(t) code block, GeekNews model architecture section) or to row m_b + t_b
+ * (FULL_CAUSAL), then t_b += 1. The counters live on the device, so calls need no host sync.
+ * Errors: RSWA_E_INVALID; RSWA_E_CAPACITY when active_dev is NULL and a FULL_CAUSAL sequence
+ * already holds max_steps outputs (checked on the host before enqueuing). With an active mask the
+ * host cannot see which sequences append; a FULL_CAUSAL append past capacity is then skipped on
+ * the device and reported by rswa_cache_steps(). */
+rswa_status rswa_append_kv(rswa_cache* cache, const void* k_dev, const void* v_dev,
+                           const uint8_t* active_dev /* [B] or NULL */, void* stream);
+
+/* K2, decode attention (split-K flash decode + merge). For every active sequence b and head h:
+ *   out[b][h] = softmax(scale * K_L q[b][h]) V_L
+ * over the L_b = m_b + min(n_b, t_b) live rows (RSWA) or m_b + t_b rows (FULL_CAUSAL), i.e. the
+ * prefix and the last min(n_b, t_b) appended outputs, the latest one included. q_dev: [B][H][D] of
+ * kv_dtype; out_dev: [B][H][D] of out_dtype (rows of inactive sequences are left untouched).
+ * softmax_scale <= 0 selects 1/sqrt(D). active_dev: [B] or NULL (all).
+ * Errors: RSWA_E_INVALID (pointers, out_dtype, or a sequence with m_b = 0 that has had no append
+ * yet: its key set is empty), RSWA_E_HIP. */
+rswa_status rswa_decode_attn(rswa_cache* cache, const void* q_dev, void* out_dev, int32_t out_dtype,
+                             float softmax_scale, const uint8_t* active_dev, void* stream);
+
+/* K3, R-SWA-masked prefill / teacher-forced pass over packed sequences (bf16 MFMA, fp32 softmax).
+ * Sequence s occupies token rows [cu_seqlens[s], cu_seqlens[s+1]) of q/k/v/out, its first
+ * m_s = prefix_len[s] tokens being the prefix. Query p (position within the sequence) sees key k
+ * iff   k < m_s  and (prefix_causal == 0 or p >= m_s or k <= p)          (the reference prefix)
+ *    or m_s <= k <= p and p - k < n_s                                   (its own output window)
+ * so prefix queries never see outputs; with n_s >= the sequence length this is causal attention
+ * over the outputs (the full-causal comparison).
+ * q/k/v_dev: [total][H][D] bf16, token-major; out_dev: [total][H][D] of out_dtype.
+ * cu_seqlens_dev: device int32 [nseq + 1], nondecreasing, cu_seqlens[0] = 0;
+ * prefix_len_dev / window_dev: device int32 [nseq]; m_s in [0, S_s], n_s >= 1.
+ * max_seqlen (host) must be >= every S_s; it sizes the launch grid.
+ * Errors: RSWA_E_INVALID (host-checkable arguments), RSWA_E_UNSUPPORTED (head_dim), RSWA_E_HIP.
+ * Device-side metadata is trusted: the caller guarantees it matches the description above. */
+rswa_status rswa_prefill_attn(const void* q_dev, const void* k_dev, const void* v_dev,
+                              void* out_dev, int32_t out_dtype, const int32_t* cu_seqlens_dev,
+                              const int32_t* prefix_len_dev, const int32_t* window_dev,
+                              int32_t nseq, int32_t num_heads, int32_t head_dim, int32_t max_seqlen,
+                              int32_t prefix_causal, float softmax_scale, void* stream);
+
+/* Copy the per-sequence step counters t_b to steps_host [B]. BLOCKS until `stream` has passed
+ * all prior work. Returns RSWA_E_CAPACITY if a FULL_CAUSAL append past max_steps was skipped on
+ * the device since creation (the counters are still copied). */
+rswa_status rswa_cache_steps(rswa_cache* cache, int32_t* steps_host, void* stream);
+
+/* Storage base pointer and layout of a live cache (host only; see rswa_cache_plan).
+ * Any output pointer may be NULL. */
+rswa_status rswa_cache_info(const rswa_cache* cache, void** storage_dev,
+                            int64_t* seq_offset_host /* [B] */, int32_t* rows_host /* [B] */);
+
+/* Decode work split: each (b, h) key range is cut into chunks of chunk_rows rows (a multiple of
+ * 64, or 0 = automatic), processed by grid_blocks persistent workgroups (0 = automatic). Results
+ * do not depend on these except through float32 summation order. Host only. */
+rswa_status rswa_cache_set_decode_split(rswa_cache* cache, int32_t chunk_rows, int32_t grid_blocks);
+
+/* Release the cache: synchronizes the stream it was created on, frees library-owned memory.
+ * NULL is accepted. Caller-owned storage is left as is. */
+rswa_status rswa_cache_destroy(rswa_cache* cache);
+
+/* Human-readable name of a status code (static string). */
+const char* rswa_status_str(int32_t status);
+
+/* Detail message of the last error returned on the calling thread (static per thread; empty
+ * string if none). */
+const char* rswa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RSWA_H */

@@ -1,0 +1,112 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/rswa.h declares, and its
+host-only paths (layout planning, validation, status strings) behave as documented. No call here
+reaches the GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rswa.h")
+LIB = os.path.join(ROOT, "windowed_attention_amd", "librswa.so")
+
+
+@pytest.fixture(scope="module")
+def wa():
+    if not os.path.exists(LIB):  # build once if nothing is built yet
+        from windowed_attention_amd import _build
+        _build.build()
+    import windowed_attention_amd
+    return windowed_attention_amd
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rswa_\w+)\s*\(", text)))
+
+
+def test_exports_every_header_symbol(wa):
+    names = header_functions()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(LIB)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert sorted(wa.EXPORTS) == names
+
+
+def test_library_holds_gfx950_code_only():
+    data = open(LIB, "rb").read()
+    assert b"gfx950" in data
+    for other in (b"amdgcn-amd-amdhsa--gfx942", b"amdgcn-amd-amdhsa--gfx90a"):
+        assert other not in data
+
+
+def test_status_strings(wa):
+    for code, name in wa.STATUS.items():
+        assert wa.status_str(code) == name
+    assert wa.status_str(-99) == "RSWA_E_UNKNOWN"
+
+
+def test_plan_layout_matches_row_counts(wa):
+    m = [272, 0, 5155]
+    n = [128, 5, 64]
+    off, rows, nbytes = wa.rswa_cache_plan(m, n, num_heads=16, kv_dtype=torch.bfloat16)
+    np.testing.assert_array_equal(rows, [400, 5, 5219])
+    per_seq = 2 * 16 * rows.astype(np.int64) * 128  # K and V, elements
+    np.testing.assert_array_equal(off, np.concatenate([[0], np.cumsum(per_seq)[:-1]]))
+    assert nbytes == int(per_seq.sum()) * 2
+    # batched single-page decode: 64 sequences x (272 + 128) rows x 16 heads x 128 x K,V x bf16
+    assert wa.rswa_cache_bytes([272] * 64, [128] * 64) == 64 * 400 * 16 * 128 * 2 * 2
+    # full causal: m + max_steps rows, fp32
+    _, rows, nbytes = wa.rswa_cache_plan([7], None, [20], mode=wa.MODE_FULL_CAUSAL,
+                                         num_heads=2, kv_dtype=torch.float32)
+    assert rows.tolist() == [27] and nbytes == 2 * 2 * 27 * 128 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(prefix_len=[1], window=[0]), -1),
+    (dict(prefix_len=[-1], window=[4]), -1),
+    (dict(prefix_len=[4], window=[4], head_dim=64), -2),
+    (dict(prefix_len=[4], window=[4], head_dim=0), -1),
+    (dict(prefix_len=[4], window=[4], num_heads=0), -1),
+    (dict(prefix_len=[4], window=None), -1),
+    (dict(prefix_len=[4], window=[4], max_steps=None, mode=1), -1),
+    (dict(prefix_len=[4], window=None, max_steps=[0], mode=1), -1),
+    (dict(prefix_len=[4], window=[4], mode=7), -1),
+])
+def test_plan_rejects_invalid_descriptions(wa, kw, status):
+    kw = dict(kw)
+    args = (kw.pop("prefix_len"), kw.pop("window"), kw.pop("max_steps", None))
+    with pytest.raises(wa.RswaError) as e:
+        wa.rswa_cache_plan(*args, **kw)
+    assert e.value.status == status
+    assert wa.rswa_cache_bytes(*args, **kw) == 0
+
+
+def test_null_arguments_are_rejected_before_any_device_work(wa):
+    lib = wa._lib
+    null = ctypes.c_void_p(None)
+    assert lib.rswa_append_kv(null, null, null, null, null) == -1
+    assert lib.rswa_decode_attn(null, null, null, 1, 0.0, null, null) == -1
+    assert lib.rswa_cache_steps(null, None, null) == -1
+    assert lib.rswa_cache_info(null, None, None, None) == -1
+    assert lib.rswa_cache_set_decode_split(null, 64, 0) == -1
+    assert lib.rswa_cache_destroy(null) == 0
+    h = ctypes.c_void_p(None)
+    assert lib.rswa_cache_create(None, null, null, null, ctypes.byref(h)) == -1
+    assert h.value is None
+    assert b"NULL" in lib.rswa_last_error() or b"null" in lib.rswa_last_error()
+    # prefill: null pointers, bad head_dim, bad dtype
+    one = ctypes.c_void_p(16)
+    assert lib.rswa_prefill_attn(null, one, one, one, 1, one, one, one, 1, 16, 128, 8, 0, 0.0,
+                                 null) == -1
+    assert lib.rswa_prefill_attn(one, one, one, one, 1, one, one, one, 1, 16, 64, 8, 0, 0.0,
+                                 null) == -2
+    assert lib.rswa_prefill_attn(one, one, one, one, 3, one, one, one, 1, 16, 128, 8, 0, 0.0,
+                                 null) == -1
+    assert lib.rswa_prefill_attn(one, one, one, one, 1, one, one, one, 0, 16, 128, 8, 0, 0.0,
+                                 null) == -1

@@ -1,0 +1,256 @@
+"""GPU parity of K1 (ring append / evict) and K2 (split-K decode) against the fp64 oracle.
+
+K1 is checked bit-exactly: prefix rows, ring slots (output j in row m + j mod n), full-causal rows,
+step counters and untouched canary rows. K2 is checked element by element against the oracle
+fed the same stored inputs: max-abs error <= 1e-2 for bf16 inputs and <= 1e-5 for fp32 inputs,
+judged on the kernel's float32 output; its bf16 output must be exactly the round-to-nearest-even
+of that float32 output. Full-size workloads are checked at sampled steps, in the same launch
+configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_common import Trajectory, sample_steps, upload
+from workloads import to_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1e-2, "f32": 1e-5}
+CANARY = 0x5A5A
+
+
+@pytest.fixture(scope="module")
+def wa():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import windowed_attention_amd
+    return windowed_attention_amd
+
+
+def oracle_out(wl, t, b, mode):
+    pk, pv = wl.prefix(b)
+    o, c = O.decode_step(to_f64(wl.q[t - 1, b], wl.dtype), to_f64(pk, wl.dtype),
+                         to_f64(pv, wl.dtype), to_f64(wl.k[:t, b], wl.dtype),
+                         to_f64(wl.v[:t, b], wl.dtype), t, int(wl.window[b]),
+                         O.FULL if mode else O.RSWA)
+    return o, c
+
+
+def check_steps(wl, mode, got, seqs_per_step=None, seed=0):
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for t, out in sorted(got.items()):
+        seqs = [b for b in range(wl.batch) if wl.steps[b] >= t]
+        if seqs_per_step is not None and len(seqs) > seqs_per_step:
+            seqs = sorted(rng.choice(seqs, size=seqs_per_step, replace=False).tolist())
+        for b in seqs:
+            ref, _ = oracle_out(wl, t, b, mode)
+            err = float(np.abs(out[b] - ref).max())
+            worst = max(worst, err)
+            assert err <= TOL[wl.dtype], f"t={t} b={b}: max abs err {err}"
+    return worst
+
+
+def bf16_rne(x):
+    return W.bf16_bits(np.asarray(x, np.float32))
+
+
+# ---------------------------------------------------------------------------------------------
+# K1: bit-exact ring and canaries
+# ---------------------------------------------------------------------------------------------
+def read_storage(storage):
+    torch.cuda.synchronize()
+    return storage.cpu().numpy().view(np.uint16)
+
+
+def seq_blocks(wa, st, wl, mode, b, off, rows):
+    H, D = 16, 128
+    n_el = H * rows[b] * D
+    K = st[off[b]:off[b] + n_el].reshape(H, rows[b], D)
+    V = st[off[b] + n_el:off[b] + 2 * n_el].reshape(H, rows[b], D)
+    return K, V
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_append_rows_bit_exact(wa, mode):
+    m, n, T = [5, 0, 70], [4, 3, 64], [150, 150, 150]
+    wl = W.make_decode("ring", 91, "bf16", m, n, T, seed=1)
+    cap = n if mode == 0 else T
+    off, rows, nbytes = wa.rswa_cache_plan(m, n if mode == 0 else None, T if mode else None,
+                                           mode=mode)
+    storage = torch.full((nbytes // 2,), CANARY, dtype=torch.int16, device="cuda")
+    tr = Trajectory(wa, wl, mode, storage=storage)
+    check_at = set(range(0, 12)) | {63, 64, 65, 66, 128, 129, 130, 149, 150}
+    for t in range(0, 151):
+        if t > 0:
+            tr.cache.append(tr.k[t - 1], tr.v[t - 1])
+        if t not in check_at:
+            continue
+        st = read_storage(storage)
+        np.testing.assert_array_equal(tr.cache.steps(), [t, t, t])
+        for b in range(3):
+            K, V = seq_blocks(wa, st, wl, mode, b, off, rows)
+            pk, pv = wl.prefix(b)
+            np.testing.assert_array_equal(K[:, :m[b]], pk.transpose(1, 0, 2))
+            np.testing.assert_array_equal(V[:, :m[b]], pv.transpose(1, 0, 2))
+            if mode == 0:
+                occ = O.ring_occupants(n[b], t)
+                slots = [(m[b] + s, j) for s, j in enumerate(occ)]
+            else:
+                slots = [(O.full_row(m[b], j), j if j < t else -1) for j in range(cap[b])]
+            for r, j in slots:
+                if j >= 0:
+                    np.testing.assert_array_equal(K[:, r], wl.k[j, b])
+                    np.testing.assert_array_equal(V[:, r], wl.v[j, b])
+                else:
+                    assert (K[:, r] == CANARY).all() and (V[:, r] == CANARY).all(), (t, b, r)
+    # nothing outside the planned storage was written: the tensor is exactly the plan's size
+    assert storage.numel() * 2 == nbytes
+    tr.cache.close()
+
+
+def test_active_mask_and_capacity(wa):
+    m, T = [3, 4], [5, 5]
+    wl = W.make_decode("cap", 92, "bf16", m, [8, 8], T, seed=2)
+    tr = Trajectory(wa, wl, wa.MODE_FULL_CAUSAL)
+    act = torch.tensor([1, 0], dtype=torch.uint8, device="cuda")
+    for t in range(3):
+        tr.cache.append(tr.k[t], tr.v[t], act)
+    np.testing.assert_array_equal(tr.cache.steps(), [3, 0])
+    for t in range(3):  # host mirror counts calls: 3 more fill sequence 0 past max_steps = 5
+        tr.cache.append(tr.k[t], tr.v[t], act)
+    with pytest.raises(wa.RswaError) as e:
+        tr.cache.steps()
+    assert e.value.status == -3
+    with pytest.raises(wa.RswaError) as e:  # without a mask the host sees the overflow first
+        tr.cache.append(tr.k[0], tr.v[0])
+    assert e.value.status == -3
+    tr.cache.close()
+
+
+def test_empty_key_set_is_rejected(wa):
+    wl = W.make_decode("empty", 93, "bf16", [0], [4], [3], seed=3)
+    tr = Trajectory(wa, wl, wa.MODE_RSWA)
+    with pytest.raises(wa.RswaError) as e:
+        tr.cache.decode(tr.q[0])
+    assert e.value.status == -1
+    tr.cache.close()
+
+
+def test_single_visible_key_is_exact(wa):
+    """m = 0, n = 1: every output must be the latest value row, bit for bit."""
+    wl = W.make_decode("one", 94, "bf16", [0, 0], [1, 1], [20, 20], seed=4)
+    tr = Trajectory(wa, wl, wa.MODE_RSWA)
+    got = tr.run(range(1, 21))
+    for t, out in got.items():
+        np.testing.assert_array_equal(out, W.bf16_to_f32(wl.v[t - 1]))
+    tr.cache.close()
+
+
+# ---------------------------------------------------------------------------------------------
+# K2: small shapes, every step, several chunk settings
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("chunk", [0, 64, 128, 512])
+def test_decode_small_every_step(wa, dtype, chunk):
+    m, n, T = [272, 0, 37], [128, 5, 64], [300, 300, 300]
+    wl = W.make_decode("small", 95, dtype, m, n, T, seed=5, outlier_p=0.01)
+    tr = Trajectory(wa, wl, wa.MODE_RSWA)
+    tr.cache.set_decode_split(chunk, 0)
+    got = tr.run(range(1, 301))
+    check_steps(wl, 0, got)
+    tr.cache.close()
+
+
+@pytest.mark.parametrize("grid", [1, 7, 4096])
+def test_decode_grid_sizes(wa, grid):
+    m, n, T = [100, 300, 9, 64], [16, 128, 5, 64], [80, 80, 80, 80]
+    wl = W.make_decode("grid", 96, "bf16", m, n, T, seed=6)
+    tr = Trajectory(wa, wl, wa.MODE_RSWA)
+    tr.cache.set_decode_split(64, grid)
+    got = tr.run([1, 5, 16, 17, 63, 64, 65, 80])
+    check_steps(wl, 0, got)
+    tr.cache.close()
+
+
+def test_decode_full_causal_small(wa):
+    m, T = [50, 0, 130], [200, 200, 200]
+    wl = W.make_decode("full", 97, "bf16", m, [8, 8, 8], T, seed=7)
+    tr = Trajectory(wa, wl, wa.MODE_FULL_CAUSAL)
+    tr.cache.set_decode_split(64, 0)
+    got = tr.run(range(1, 201, 7))
+    check_steps(wl, 1, got)
+    tr.cache.close()
+
+
+def test_bf16_output_is_rne_of_f32_output(wa):
+    wl = W.make_decode("rne", 98, "bf16", [272, 40], [128, 16], [150, 150], seed=8,
+                       outlier_p=0.01)
+    a = Trajectory(wa, wl, wa.MODE_RSWA)
+    b = Trajectory(wa, wl, wa.MODE_RSWA)
+    steps = [1, 50, 128, 129, 150]
+    f32 = a.run(steps, out_dtype=torch.float32)
+    bf = b.run(steps, out_dtype=torch.bfloat16)
+    for t in steps:
+        np.testing.assert_array_equal(W.bf16_bits(bf[t]), bf16_rne(f32[t]))
+    a.cache.close()
+    b.cache.close()
+
+
+def test_ragged_small_one_launch(wa):
+    wl = W.varlen_config(0, batch=6, T_max=400)
+    # shrink the prefixes so the oracle stays quick, keep the ragged lengths / windows
+    wl2 = W.make_decode("ragged-small", 99, "bf16", np.minimum(wl.prefix_len, 300), wl.window,
+                        np.minimum(wl.steps, 400) - np.arange(6) * 37, seed=9)
+    tr = Trajectory(wa, wl2, wa.MODE_RSWA)
+    got = tr.run(sample_steps(int(wl2.T), 64, 0, extra=20))
+    check_steps(wl2, 0, got)
+    tr.cache.close()
+
+
+# ---------------------------------------------------------------------------------------------
+# full-size workloads, sampled steps, benchmark launch configuration
+# ---------------------------------------------------------------------------------------------
+def test_cfg_single_page_fp32_all_steps(wa):
+    wl = W.decode_config(1)
+    tr = Trajectory(wa, wl, wa.MODE_RSWA)
+    got = tr.run(range(1, wl.T + 1))
+    worst = check_steps(wl, 0, got)
+    print(f"single-page fp32 decode: worst max-abs error {worst:.3e} over {len(got)} steps")
+    tr.cache.close()
+
+
+@pytest.mark.slow
+def test_cfg_batched_single_page_sampled(wa):
+    wl = W.decode_config(2)
+    tr = Trajectory(wa, wl, wa.MODE_RSWA)
+    steps = sample_steps(wl.T, 128, 272)
+    got = tr.run(steps)
+    worst = check_steps(wl, 0, got, seqs_per_step=6)
+    print(f"batched decode: worst max-abs error {worst:.3e} at {len(steps)} steps")
+    tr.cache.close()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("mode", [0, 1])
+def test_cfg_multi_page_sampled(wa, mode):
+    wl = W.decode_config(3)
+    tr = Trajectory(wa, wl, mode)
+    steps = sample_steps(wl.T, 128, 5155, full=bool(mode), crossings=12, extra=8)
+    got = tr.run(steps)
+    worst = check_steps(wl, mode, got, seqs_per_step=2)
+    print(f"multi-page decode mode={mode}: worst max-abs error {worst:.3e}")
+    tr.cache.close()
+
+
+@pytest.mark.slow
+def test_cfg_ragged_sampled(wa):
+    wl = W.varlen_config(0)
+    tr = Trajectory(wa, wl, wa.MODE_RSWA)
+    steps = sample_steps(wl.T, 64, 272, extra=12)
+    got = tr.run(steps)
+    worst = check_steps(wl, 0, got, seqs_per_step=3)
+    print(f"ragged decode: worst max-abs error {worst:.3e}")
+    tr.cache.close()

@@ -1,0 +1,310 @@
+"""Python binding of the MI355X R-SWA library (librswa.so).
+
+Argument marshalling only: every step of the path runs in the HIP kernels behind the C ABI of
+include/rswa.h. torch supplies device memory and the stream (torch's current stream unless one is
+given). Importing this module fails loudly if the library has not been built.
+
+Functions carry the C names (rswa_cache_create, rswa_append_kv, rswa_decode_attn,
+rswa_prefill_attn, ...); `RswaCache` wraps the cache handle.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librswa.so")
+
+BF16, F32 = 0, 1
+MODE_RSWA, MODE_FULL_CAUSAL = 0, 1
+STATUS = {0: "RSWA_OK", -1: "RSWA_E_INVALID", -2: "RSWA_E_UNSUPPORTED", -3: "RSWA_E_CAPACITY",
+          -4: "RSWA_E_OOM", -5: "RSWA_E_HIP", -6: "RSWA_E_INTERNAL"}
+
+# Every symbol include/rswa.h declares.
+EXPORTS = ("rswa_cache_plan", "rswa_cache_bytes", "rswa_cache_create", "rswa_append_kv",
+           "rswa_decode_attn", "rswa_prefill_attn", "rswa_cache_steps", "rswa_cache_info",
+           "rswa_cache_set_decode_split", "rswa_cache_destroy", "rswa_status_str",
+           "rswa_last_error")
+
+
+class RswaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("mode", ctypes.c_int32), ("prefix_len", ctypes.POINTER(ctypes.c_int32)),
+                ("window", ctypes.POINTER(ctypes.c_int32)),
+                ("max_steps", ctypes.POINTER(ctypes.c_int32)),
+                ("storage_dev", ctypes.c_void_p), ("storage_bytes", ctypes.c_uint64)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+            f"g.build()'` (hipcc, gfx950). There is no fallback path.")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, u64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_float
+    pi32, pi64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    pdesc = ctypes.POINTER(CacheDesc)
+    sig = {
+        "rswa_cache_plan": (i32, [pdesc, pi64, pi32, ctypes.POINTER(u64)]),
+        "rswa_cache_bytes": (u64, [pdesc]),
+        "rswa_cache_create": (i32, [pdesc, vp, vp, vp, ctypes.POINTER(vp)]),
+        "rswa_append_kv": (i32, [vp, vp, vp, vp, vp]),
+        "rswa_decode_attn": (i32, [vp, vp, vp, i32, f32, vp, vp]),
+        "rswa_prefill_attn": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                    vp]),
+        "rswa_cache_steps": (i32, [vp, pi32, vp]),
+        "rswa_cache_info": (i32, [vp, ctypes.POINTER(vp), pi64, pi32]),
+        "rswa_cache_set_decode_split": (i32, [vp, i32, i32]),
+        "rswa_cache_destroy": (i32, [vp]),
+        "rswa_status_str": (ctypes.c_char_p, [i32]),
+        "rswa_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        detail = _lib.rswa_last_error().decode()
+        raise RswaError(status, f"{what}: {STATUS.get(status, status)} ({detail})")
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return BF16
+    if dt == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {dt}: use torch.bfloat16 or torch.float32")
+
+
+def _torch_dtype(code: int) -> torch.dtype:
+    return torch.bfloat16 if code == BF16 else torch.float32
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor | None, name: str, dtype=None, shape=None) -> ctypes.c_void_p:
+    if t is None:
+        return ctypes.c_void_p(None)
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _i32_array(x, n: int, name: str):
+    arr = np.ascontiguousarray(np.asarray(x, dtype=np.int32).reshape(-1))
+    if arr.size != n:
+        raise ValueError(f"{name} must have {n} entries")
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _desc(prefix_len, window, max_steps, num_heads, head_dim, kv_dtype, mode, storage=None):
+    m = np.ascontiguousarray(np.asarray(prefix_len, dtype=np.int32).reshape(-1))
+    B = m.size
+    keep = [m]
+    d = CacheDesc()
+    d.batch, d.num_heads, d.head_dim = B, num_heads, head_dim
+    d.kv_dtype, d.mode = _dtype_code(kv_dtype), mode
+    d.prefix_len = m.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    if window is not None:
+        w, d.window = _i32_array(window, B, "window")
+        keep.append(w)
+    if max_steps is not None:
+        s, d.max_steps = _i32_array(max_steps, B, "max_steps")
+        keep.append(s)
+    if storage is not None:
+        d.storage_dev = storage.data_ptr()
+        d.storage_bytes = storage.numel() * storage.element_size()
+    return d, keep
+
+
+def rswa_cache_plan(prefix_len, window=None, max_steps=None, *, num_heads=16, head_dim=128,
+                    kv_dtype=torch.bfloat16, mode=MODE_RSWA):
+    """Host-only layout: (seq_offset elements [B] int64, rows [B] int32, storage bytes)."""
+    d, keep = _desc(prefix_len, window, max_steps, num_heads, head_dim, kv_dtype, mode)
+    B = d.batch
+    off = np.zeros(max(B, 1), dtype=np.int64)
+    rows = np.zeros(max(B, 1), dtype=np.int32)
+    nbytes = ctypes.c_uint64(0)
+    _check(_lib.rswa_cache_plan(ctypes.byref(d), off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                ctypes.byref(nbytes)), "rswa_cache_plan")
+    return off[:B], rows[:B], int(nbytes.value)
+
+
+def rswa_cache_bytes(prefix_len, window=None, max_steps=None, *, num_heads=16, head_dim=128,
+                     kv_dtype=torch.bfloat16, mode=MODE_RSWA) -> int:
+    d, keep = _desc(prefix_len, window, max_steps, num_heads, head_dim, kv_dtype, mode)
+    return int(_lib.rswa_cache_bytes(ctypes.byref(d)))
+
+
+class RswaCache:
+    """A batch of B decode sequences: static prefix rows plus an n-slot ring per sequence
+    (mode MODE_RSWA) or a growing cache (MODE_FULL_CAUSAL)."""
+
+    def __init__(self, prefix_k: torch.Tensor | None, prefix_v: torch.Tensor | None, prefix_len,
+                 window=None, *, mode=MODE_RSWA, max_steps=None, num_heads=16, head_dim=128,
+                 kv_dtype=None, storage: torch.Tensor | None = None, stream=None):
+        m = np.asarray(prefix_len, dtype=np.int64).reshape(-1)
+        if kv_dtype is None:
+            if prefix_k is None:
+                raise ValueError("kv_dtype is required when there is no prefix tensor")
+            kv_dtype = prefix_k.dtype
+        total_m = int(m.sum())
+        shape = (total_m, num_heads, head_dim)
+        pk = _dev(prefix_k, "prefix_k", kv_dtype, shape) if prefix_k is not None else None
+        pv = _dev(prefix_v, "prefix_v", kv_dtype, shape) if prefix_v is not None else None
+        if storage is not None:
+            _dev(storage, "storage")
+        d, keep = _desc(m, window, max_steps, num_heads, head_dim, kv_dtype, mode, storage)
+        h = ctypes.c_void_p(None)
+        _check(_lib.rswa_cache_create(ctypes.byref(d), pk or ctypes.c_void_p(None),
+                                      pv or ctypes.c_void_p(None), _stream(stream),
+                                      ctypes.byref(h)), "rswa_cache_create")
+        self._h = h
+        self._storage = storage
+        self.batch = int(m.size)
+        self.num_heads = num_heads
+        self.head_dim = head_dim
+        self.kv_dtype = kv_dtype
+        self.mode = mode
+        self.prefix_len = m.astype(np.int32)
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if self._h is None:
+            raise RuntimeError("cache has been destroyed")
+        return self._h
+
+    def _bhd(self):
+        return (self.batch, self.num_heads, self.head_dim)
+
+    def append(self, k: torch.Tensor, v: torch.Tensor, active: torch.Tensor | None = None,
+               stream=None) -> None:
+        rswa_append_kv(self, k, v, active, stream)
+
+    def decode(self, q: torch.Tensor, out: torch.Tensor | None = None,
+               out_dtype: torch.dtype = torch.float32, scale: float = 0.0,
+               active: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        if out is None:
+            out = torch.empty(self._bhd(), dtype=out_dtype, device=q.device)
+        rswa_decode_attn(self, q, out, scale, active, stream)
+        return out
+
+    def steps(self, stream=None) -> np.ndarray:
+        s = np.zeros(self.batch, dtype=np.int32)
+        _check(_lib.rswa_cache_steps(self.handle, s.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                     _stream(stream)), "rswa_cache_steps")
+        return s
+
+    def info(self):
+        p = ctypes.c_void_p(None)
+        off = np.zeros(self.batch, dtype=np.int64)
+        rows = np.zeros(self.batch, dtype=np.int32)
+        _check(_lib.rswa_cache_info(self.handle, ctypes.byref(p),
+                                    off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                    rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))),
+               "rswa_cache_info")
+        return p.value, off, rows
+
+    def set_decode_split(self, chunk_rows: int = 0, grid_blocks: int = 0) -> None:
+        _check(_lib.rswa_cache_set_decode_split(self.handle, chunk_rows, grid_blocks),
+               "rswa_cache_set_decode_split")
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None:
+            _check(_lib.rswa_cache_destroy(self._h), "rswa_cache_destroy")
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+def rswa_cache_create(prefix_k, prefix_v, prefix_len, window=None, **kw) -> RswaCache:
+    return RswaCache(prefix_k, prefix_v, prefix_len, window, **kw)
+
+
+def rswa_append_kv(cache: RswaCache, k: torch.Tensor, v: torch.Tensor,
+                   active: torch.Tensor | None = None, stream=None) -> None:
+    shape = cache._bhd()
+    _check(_lib.rswa_append_kv(cache.handle, _dev(k, "k", cache.kv_dtype, shape),
+                               _dev(v, "v", cache.kv_dtype, shape),
+                               _dev(active, "active", torch.uint8, (cache.batch,)),
+                               _stream(stream)), "rswa_append_kv")
+
+
+def rswa_decode_attn(cache: RswaCache, q: torch.Tensor, out: torch.Tensor, scale: float = 0.0,
+                     active: torch.Tensor | None = None, stream=None) -> None:
+    shape = cache._bhd()
+    _check(_lib.rswa_decode_attn(cache.handle, _dev(q, "q", cache.kv_dtype, shape),
+                                 _dev(out, "out", None, shape), _dtype_code(out.dtype),
+                                 ctypes.c_float(scale),
+                                 _dev(active, "active", torch.uint8, (cache.batch,)),
+                                 _stream(stream)), "rswa_decode_attn")
+
+
+def rswa_cache_destroy(cache: RswaCache) -> None:
+    cache.close()
+
+
+def rswa_prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                      prefix_len: torch.Tensor, window: torch.Tensor, *, out=None,
+                      out_dtype: torch.dtype = torch.float32, prefix_causal: bool = False,
+                      scale: float = 0.0, max_seqlen: int | None = None,
+                      stream=None) -> torch.Tensor:
+    """R-SWA-masked attention over packed sequences; q/k/v [total][H][D] bf16 on the device,
+    cu_seqlens / prefix_len / window int32 device tensors. max_seqlen defaults to the largest
+    sequence (computed on the host from cu_seqlens, which costs a device sync)."""
+    total, H, D = q.shape
+    nseq = prefix_len.numel()
+    if max_seqlen is None:
+        cs = cu_seqlens.cpu().numpy()
+        max_seqlen = int(np.diff(cs).max()) if cs.size > 1 else 0
+    if out is None:
+        out = torch.empty((total, H, D), dtype=out_dtype, device=q.device)
+    shape = (total, H, D)
+    _check(_lib.rswa_prefill_attn(
+        _dev(q, "q", torch.bfloat16, shape), _dev(k, "k", torch.bfloat16, shape),
+        _dev(v, "v", torch.bfloat16, shape), _dev(out, "out", None, shape),
+        _dtype_code(out.dtype), _dev(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,)),
+        _dev(prefix_len, "prefix_len", torch.int32, (nseq,)),
+        _dev(window, "window", torch.int32, (nseq,)), nseq, H, D, int(max_seqlen),
+        int(bool(prefix_causal)), ctypes.c_float(scale), _stream(stream)), "rswa_prefill_attn")
+    return out
+
+
+def status_str(code: int) -> str:
+    return _lib.rswa_status_str(code).decode()

@@ -1,0 +1,102 @@
+// K1: ring append / evict, and the one-time prefix copy of cache creation.
+//
+// The pages hold the decode cache as a queue of capacity m + n from which every new token evicts
+// the oldest output KV (deep dive "Unlimited-OCR", N(t) code block; GeekNews "Unlimited OCR",
+// model architecture section). Here the queue's output part is an n-slot ring: output index j
+// (0-based) is written to row m + (j mod n), overwriting output j - n, so an append is one row
+// write per head with no data movement, and the live rows are always the contiguous range
+// [0, m + min(n, t)). Full-causal mode writes row m + j (the cache grows, standard attention).
+// The prefix rows [0, m) are written once at creation and never again (GeekNews, DeepEncoder
+// section: visual tokens are encoded once and stay static).
+#include "device.h"
+#include "kernels.h"
+
+namespace rswa {
+namespace {
+
+constexpr int kThreads = 256;
+
+// One workgroup per sequence: every thread reads t_b before the barrier, thread 0 advances it
+// after, so the counter update needs no atomics.
+template <int ELEM>
+__global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
+  const int b = blockIdx.x;
+  if (a.active && !a.active[b]) return;
+  const int t = a.meta.steps[b];
+  const int cap = a.meta.cap[b];
+  if (a.full_causal && t >= cap) {
+    if (threadIdx.x == 0) *a.meta.err = 1;
+    return;
+  }
+  const int m = a.meta.prefix_len[b];
+  const int64_t row = a.full_causal ? (int64_t)m + t : (int64_t)m + t % cap;
+  const int64_t R = a.meta.rows[b];
+  constexpr int CH = kHeadDim * ELEM / 16;  // 16-byte pieces per row
+  const int H = a.heads;
+  char* seq = reinterpret_cast<char*>(a.storage) + a.meta.seq_off[b] * ELEM;
+  const char* kin = reinterpret_cast<const char*>(a.k_new);
+  const char* vin = reinterpret_cast<const char*>(a.v_new);
+  for (int i = threadIdx.x; i < H * CH; i += kThreads) {
+    const int h = i / CH, c = i - (i / CH) * CH;
+    const int64_t src = ((int64_t)b * H + h) * kHeadDim * ELEM + c * 16;
+    const int64_t dk = ((int64_t)h * R + row) * kHeadDim * ELEM + c * 16;
+    const int64_t dv = ((int64_t)(H + h) * R + row) * kHeadDim * ELEM + c * 16;
+    const uint4 kx = *reinterpret_cast<const uint4*>(kin + src);
+    const uint4 vx = *reinterpret_cast<const uint4*>(vin + src);
+    *reinterpret_cast<uint4*>(seq + dk) = kx;
+    *reinterpret_cast<uint4*>(seq + dv) = vx;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) a.meta.steps[b] = t + 1;
+}
+
+// Packed token-major prefix [sum m][H][D] -> head-major rows [0, m_b) of sequence b.
+template <int ELEM>
+__global__ __launch_bounds__(kThreads) void prefix_copy_kernel(PrefixCopyArgs a) {
+  const int b = blockIdx.y;
+  const int64_t m = a.meta.prefix_len[b];
+  const int64_t R = a.meta.rows[b];
+  constexpr int CH = kHeadDim * ELEM / 16;
+  const int H = a.heads;
+  const int64_t total = m * H * CH;
+  const int64_t row0 = a.prefix_row0[b];
+  char* seq = reinterpret_cast<char*>(a.storage) + a.meta.seq_off[b] * ELEM;
+  const char* pk = reinterpret_cast<const char*>(a.pk);
+  const char* pv = reinterpret_cast<const char*>(a.pv);
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * kThreads) {
+    const int64_t r = i / (H * CH);
+    const int rem = (int)(i - r * (H * CH));
+    const int h = rem / CH, c = rem - (rem / CH) * CH;
+    const int64_t src = ((row0 + r) * H + h) * kHeadDim * ELEM + c * 16;
+    const int64_t dk = ((int64_t)h * R + r) * kHeadDim * ELEM + c * 16;
+    const int64_t dv = ((int64_t)(H + h) * R + r) * kHeadDim * ELEM + c * 16;
+    *reinterpret_cast<uint4*>(seq + dk) = *reinterpret_cast<const uint4*>(pk + src);
+    *reinterpret_cast<uint4*>(seq + dv) = *reinterpret_cast<const uint4*>(pv + src);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& a, int batch, int kv_f32, hipStream_t s) {
+  if (kv_f32)
+    hipLaunchKernelGGL(append_kernel<4>, dim3(batch), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(append_kernel<2>, dim3(batch), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefix_copy(const PrefixCopyArgs& a, int kv_f32, int max_rows, hipStream_t s) {
+  if (max_rows <= 0) return hipSuccess;
+  const int elem = kv_f32 ? 4 : 2;
+  const int64_t pieces = (int64_t)max_rows * a.heads * (kHeadDim * elem / 16);
+  int64_t gx = (pieces + kThreads - 1) / kThreads;
+  if (gx > 4096) gx = 4096;
+  if (kv_f32)
+    hipLaunchKernelGGL(prefix_copy_kernel<4>, dim3((unsigned)gx, a.batch), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(prefix_copy_kernel<2>, dim3((unsigned)gx, a.batch), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace rswa

@@ -1,0 +1,78 @@
+// Internal launch interface between the C-ABI host code and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rswa {
+
+// Per-sequence metadata of a decode cache, resident on the device (written once at creation,
+// except `steps`, which the append kernel advances).
+struct CacheMeta {
+  const int64_t* seq_off;    // [B] element offset of sequence b's K block
+  const int32_t* rows;       // [B] R_b = m_b + cap_b rows per head
+  const int32_t* prefix_len; // [B] m_b
+  const int32_t* cap;        // [B] n_b (R-SWA ring slots) or max_steps_b (full causal)
+  int32_t* steps;            // [B] t_b, outputs appended so far
+  int32_t* err;              // [1] sticky flag: a full-causal append found no free row
+};
+
+struct AppendArgs {
+  void* storage;
+  CacheMeta meta;
+  const void* k_new;        // [B][H][D]
+  const void* v_new;        // [B][H][D]
+  const uint8_t* active;    // [B] or nullptr
+  int32_t heads;
+  int32_t full_causal;
+};
+
+struct DecodeArgs {
+  const void* storage;
+  CacheMeta meta;
+  const void* q;            // [B][H][D]
+  void* out;                // [B][H][D]
+  const uint8_t* active;    // [B] or nullptr
+  float* ws_acc;            // [B*H*smax][D] split partial numerators
+  float2* ws_ml;            // [B*H*smax] split partial (max, sum), log2 domain
+  int32_t batch;
+  int32_t heads;
+  int32_t chunk;            // rows per split (multiple of 64)
+  int32_t smax;             // split slots per (b, h) in the workspace
+  int32_t full_causal;
+  float scale_log2;         // softmax scale * log2(e)
+};
+
+struct PrefixCopyArgs {
+  void* storage;
+  CacheMeta meta;
+  const void* pk;           // [sum m][H][D]
+  const void* pv;
+  const int64_t* prefix_row0; // [B] first packed row of sequence b
+  int32_t heads;
+  int32_t batch;
+};
+
+struct PrefillArgs {
+  const uint16_t* q;        // [total][H][D] bf16
+  const uint16_t* k;
+  const uint16_t* v;
+  void* out;                // [total][H][D]
+  const int32_t* cu_seqlens;
+  const int32_t* prefix_len;
+  const int32_t* window;
+  int32_t nseq;
+  int32_t heads;
+  int32_t max_seqlen;
+  int32_t prefix_causal;
+  float scale_log2;
+};
+
+// Launchers (return the hipError_t of the launch).
+hipError_t launch_prefix_copy(const PrefixCopyArgs& a, int kv_f32, int max_rows, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, int batch, int kv_f32, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int kv_f32, int out_f32, int grid_blocks,
+                         bool need_merge, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, int out_f32, hipStream_t s);
+
+}  // namespace rswa

@@ -1,0 +1,437 @@
+// C ABI of the R-SWA library (declared in include/rswa.h): argument validation, cache ownership,
+// per-sequence metadata on the device, and kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "plan.h"
+#include "rswa.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+rswa_status fail(rswa_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+rswa_status hip_fail(hipError_t e, const char* what) {
+  return fail(RSWA_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  bool switched = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) == hipSuccess && prev != dev) {
+      switched = hipSetDevice(dev) == hipSuccess;
+    }
+  }
+  ~DeviceGuard() {
+    if (switched) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+struct rswa_cache {
+  int32_t B = 0, H = 0, D = 0, kv_dtype = 0, mode = 0;
+  rswa::Plan plan;
+  std::vector<int64_t> calls;  // appends enqueued per sequence: an upper bound of t_b
+  void* storage = nullptr;
+  bool owns_storage = false;
+  void* meta_dev = nullptr;
+  rswa::CacheMeta meta{};
+  int64_t* prefix_row0_dev = nullptr;
+  void* ws_dev = nullptr;
+  float* ws_acc = nullptr;
+  float2* ws_ml = nullptr;
+  int32_t smax = 0;      // workspace split slots per (b, h) (sized for 64-row chunks)
+  int32_t chunk = 0;     // current decode chunk rows
+  int32_t grid_user = 0; // 0 = automatic
+  int device = 0;
+  int num_cus = 0;
+
+  bool full() const { return mode == RSWA_MODE_FULL_CAUSAL; }
+  // Upper bound of each sequence's live rows, from the host count of append calls.
+  std::vector<int64_t> live_upper() const {
+    std::vector<int64_t> L(B);
+    for (int b = 0; b < B; ++b)
+      L[b] = plan.prefix[b] + std::min<int64_t>(plan.cap[b], calls[b]);
+    return L;
+  }
+};
+
+namespace {
+
+void release(rswa_cache* c) {
+  if (!c) return;
+  if (c->owns_storage && c->storage) (void)hipFree(c->storage);
+  if (c->meta_dev) (void)hipFree(c->meta_dev);
+  if (c->ws_dev) (void)hipFree(c->ws_dev);
+  delete c;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+const char* rswa_status_str(int32_t s) {
+  switch (s) {
+    case RSWA_OK: return "RSWA_OK";
+    case RSWA_E_INVALID: return "RSWA_E_INVALID";
+    case RSWA_E_UNSUPPORTED: return "RSWA_E_UNSUPPORTED";
+    case RSWA_E_CAPACITY: return "RSWA_E_CAPACITY";
+    case RSWA_E_OOM: return "RSWA_E_OOM";
+    case RSWA_E_HIP: return "RSWA_E_HIP";
+    case RSWA_E_INTERNAL: return "RSWA_E_INTERNAL";
+    default: return "RSWA_E_UNKNOWN";
+  }
+}
+
+const char* rswa_last_error(void) { return g_last_error.c_str(); }
+
+rswa_status rswa_cache_plan(const rswa_cache_desc* desc, int64_t* seq_offset_host,
+                            int32_t* rows_host, uint64_t* storage_bytes_host) {
+  try {
+    rswa::Plan p;
+    std::string why;
+    const rswa_status s = rswa::make_plan(desc, &p, &why);
+    if (s != RSWA_OK) return fail(s, why);
+    for (int b = 0; b < desc->batch; ++b) {
+      if (seq_offset_host) seq_offset_host[b] = p.seq_off[b];
+      if (rows_host) rows_host[b] = p.rows[b];
+    }
+    if (storage_bytes_host) *storage_bytes_host = p.bytes;
+    return RSWA_OK;
+  } catch (...) {
+    return fail(RSWA_E_INTERNAL, "exception in rswa_cache_plan");
+  }
+}
+
+uint64_t rswa_cache_bytes(const rswa_cache_desc* desc) {
+  uint64_t bytes = 0;
+  if (rswa_cache_plan(desc, nullptr, nullptr, &bytes) != RSWA_OK) return 0;
+  return bytes;
+}
+
+rswa_status rswa_cache_create(const rswa_cache_desc* desc, const void* prefix_k_dev,
+                              const void* prefix_v_dev, void* stream, rswa_cache** out) {
+  if (!out) return fail(RSWA_E_INVALID, "out is NULL");
+  *out = nullptr;
+  rswa_cache* c = nullptr;
+  try {
+    rswa::Plan p;
+    std::string why;
+    rswa_status s = rswa::make_plan(desc, &p, &why);
+    if (s != RSWA_OK) return fail(s, why);
+    if (p.total_prefix_rows > 0 && (!prefix_k_dev || !prefix_v_dev))
+      return fail(RSWA_E_INVALID, "prefix_k_dev / prefix_v_dev are NULL but some m_b > 0");
+    if (desc->storage_dev && desc->storage_bytes < p.bytes)
+      return fail(RSWA_E_CAPACITY, "storage_bytes smaller than rswa_cache_bytes()");
+    if (desc->storage_dev && (reinterpret_cast<uintptr_t>(desc->storage_dev) % 16) != 0)
+      return fail(RSWA_E_INVALID, "storage_dev must be 16-byte aligned");
+
+    c = new rswa_cache();
+    c->B = desc->batch;
+    c->H = desc->num_heads;
+    c->D = desc->head_dim;
+    c->kv_dtype = desc->kv_dtype;
+    c->mode = desc->mode;
+    c->plan = p;
+    c->calls.assign(c->B, 0);
+    hipError_t e = hipGetDevice(&c->device);
+    if (e != hipSuccess) {
+      release(c);
+      return hip_fail(e, "hipGetDevice");
+    }
+    e = hipDeviceGetAttribute(&c->num_cus, hipDeviceAttributeMultiprocessorCount, c->device);
+    if (e != hipSuccess || c->num_cus <= 0) {
+      release(c);
+      return hip_fail(e, "hipDeviceGetAttribute(multiProcessorCount)");
+    }
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+    // storage
+    if (desc->storage_dev) {
+      c->storage = desc->storage_dev;
+    } else {
+      e = hipMalloc(&c->storage, std::max<uint64_t>(p.bytes, 256));
+      if (e != hipSuccess) {
+        c->storage = nullptr;
+        release(c);
+        return fail(RSWA_E_OOM, std::string("hipMalloc(storage): ") + hipGetErrorString(e));
+      }
+      c->owns_storage = true;
+      e = hipMemsetAsync(c->storage, 0, p.bytes, st);
+      if (e != hipSuccess) {
+        release(c);
+        return hip_fail(e, "hipMemsetAsync(storage)");
+      }
+    }
+
+    // device metadata: seq_off[B], prefix_row0[B] (int64); rows, prefix, cap, steps [B], err[1]
+    const int B = c->B;
+    const size_t off_i64 = 0;
+    const size_t off_row0 = align_up(off_i64 + 8 * (size_t)B, 256);
+    const size_t off_rows = align_up(off_row0 + 8 * (size_t)B, 256);
+    const size_t off_pref = align_up(off_rows + 4 * (size_t)B, 256);
+    const size_t off_cap = align_up(off_pref + 4 * (size_t)B, 256);
+    const size_t off_steps = align_up(off_cap + 4 * (size_t)B, 256);
+    const size_t off_err = align_up(off_steps + 4 * (size_t)B, 256);
+    const size_t meta_bytes = off_err + 256;
+    std::vector<unsigned char> host(meta_bytes, 0);
+    std::memcpy(host.data() + off_i64, p.seq_off.data(), 8 * (size_t)B);
+    std::memcpy(host.data() + off_row0, p.prefix_row0.data(), 8 * (size_t)B);
+    std::memcpy(host.data() + off_rows, p.rows.data(), 4 * (size_t)B);
+    std::memcpy(host.data() + off_pref, p.prefix.data(), 4 * (size_t)B);
+    std::memcpy(host.data() + off_cap, p.cap.data(), 4 * (size_t)B);
+    e = hipMalloc(&c->meta_dev, meta_bytes);
+    if (e != hipSuccess) {
+      c->meta_dev = nullptr;
+      release(c);
+      return fail(RSWA_E_OOM, std::string("hipMalloc(meta): ") + hipGetErrorString(e));
+    }
+    e = hipMemcpyAsync(c->meta_dev, host.data(), meta_bytes, hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) {
+      release(c);
+      return hip_fail(e, "hipMemcpyAsync(meta)");
+    }
+    unsigned char* mb = reinterpret_cast<unsigned char*>(c->meta_dev);
+    c->meta.seq_off = reinterpret_cast<const int64_t*>(mb + off_i64);
+    c->prefix_row0_dev = reinterpret_cast<int64_t*>(mb + off_row0);
+    c->meta.rows = reinterpret_cast<const int32_t*>(mb + off_rows);
+    c->meta.prefix_len = reinterpret_cast<const int32_t*>(mb + off_pref);
+    c->meta.cap = reinterpret_cast<const int32_t*>(mb + off_cap);
+    c->meta.steps = reinterpret_cast<int32_t*>(mb + off_steps);
+    c->meta.err = reinterpret_cast<int32_t*>(mb + off_err);
+
+    // decode split policy and workspace (sized for the smallest chunk so that
+    // rswa_cache_set_decode_split never reallocates)
+    c->chunk = rswa::auto_chunk(p, c->H, 4LL * c->num_cus);
+    c->smax = rswa::split_slots(p, 64);
+    const size_t ws_slots = (size_t)B * c->H * c->smax;
+    const size_t ws_acc_bytes = align_up(ws_slots * rswa::kPlanHeadDim * sizeof(float), 256);
+    e = hipMalloc(&c->ws_dev, ws_acc_bytes + ws_slots * sizeof(float2));
+    if (e != hipSuccess) {
+      c->ws_dev = nullptr;
+      release(c);
+      return fail(RSWA_E_OOM, std::string("hipMalloc(workspace): ") + hipGetErrorString(e));
+    }
+    c->ws_acc = reinterpret_cast<float*>(c->ws_dev);
+    c->ws_ml = reinterpret_cast<float2*>(reinterpret_cast<unsigned char*>(c->ws_dev) + ws_acc_bytes);
+
+    // prefix rows
+    rswa::PrefixCopyArgs pa{};
+    pa.storage = c->storage;
+    pa.meta = c->meta;
+    pa.pk = prefix_k_dev;
+    pa.pv = prefix_v_dev;
+    pa.prefix_row0 = c->prefix_row0_dev;
+    pa.heads = c->H;
+    pa.batch = B;
+    e = rswa::launch_prefix_copy(pa, c->kv_dtype == RSWA_F32, p.max_prefix, st);
+    if (e != hipSuccess) {
+      release(c);
+      return hip_fail(e, "prefix copy launch");
+    }
+    // the host metadata buffer must outlive the async copy
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) {
+      release(c);
+      return hip_fail(e, "hipStreamSynchronize(create)");
+    }
+    *out = c;
+    return RSWA_OK;
+  } catch (const std::bad_alloc&) {
+    release(c);
+    return fail(RSWA_E_OOM, "host allocation failed");
+  } catch (...) {
+    release(c);
+    return fail(RSWA_E_INTERNAL, "exception in rswa_cache_create");
+  }
+}
+
+rswa_status rswa_append_kv(rswa_cache* c, const void* k_dev, const void* v_dev,
+                           const uint8_t* active_dev, void* stream) {
+  if (!c) return fail(RSWA_E_INVALID, "cache is NULL");
+  if (!k_dev || !v_dev) return fail(RSWA_E_INVALID, "k_dev / v_dev is NULL");
+  try {
+    if (c->full() && !active_dev) {
+      for (int b = 0; b < c->B; ++b)
+        if (c->calls[b] >= c->plan.cap[b])
+          return fail(RSWA_E_CAPACITY, "full-causal append past max_steps");
+    }
+    DeviceGuard g(c->device);
+    rswa::AppendArgs a{};
+    a.storage = c->storage;
+    a.meta = c->meta;
+    a.k_new = k_dev;
+    a.v_new = v_dev;
+    a.active = active_dev;
+    a.heads = c->H;
+    a.full_causal = c->full();
+    const hipError_t e = rswa::launch_append(a, c->B, c->kv_dtype == RSWA_F32,
+                                             reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "append launch");
+    for (int b = 0; b < c->B; ++b) c->calls[b] += 1;
+    return RSWA_OK;
+  } catch (...) {
+    return fail(RSWA_E_INTERNAL, "exception in rswa_append_kv");
+  }
+}
+
+rswa_status rswa_decode_attn(rswa_cache* c, const void* q_dev, void* out_dev, int32_t out_dtype,
+                             float softmax_scale, const uint8_t* active_dev, void* stream) {
+  if (!c) return fail(RSWA_E_INVALID, "cache is NULL");
+  if (!q_dev || !out_dev) return fail(RSWA_E_INVALID, "q_dev / out_dev is NULL");
+  if (out_dtype != RSWA_BF16 && out_dtype != RSWA_F32)
+    return fail(RSWA_E_INVALID, "out_dtype must be RSWA_BF16 or RSWA_F32");
+  if (!(softmax_scale <= 0.f) && !std::isfinite(softmax_scale))
+    return fail(RSWA_E_INVALID, "softmax_scale must be finite");
+  try {
+    const std::vector<int64_t> L = c->live_upper();
+    if (!active_dev) {
+      for (int b = 0; b < c->B; ++b)
+        if (L[b] == 0)
+          return fail(RSWA_E_INVALID, "empty key set: a sequence with m = 0 has no output yet");
+    }
+    DeviceGuard g(c->device);
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)c->D);
+    rswa::DecodeArgs a{};
+    a.storage = c->storage;
+    a.meta = c->meta;
+    a.q = q_dev;
+    a.out = out_dev;
+    a.active = active_dev;
+    a.ws_acc = c->ws_acc;
+    a.ws_ml = c->ws_ml;
+    a.batch = c->B;
+    a.heads = c->H;
+    a.chunk = c->chunk;
+    a.smax = c->smax;
+    a.full_causal = c->full();
+    a.scale_log2 = scale * 1.4426950408889634f;
+    const int64_t items = rswa::decode_items(L, c->H, c->chunk);
+    int64_t grid = c->grid_user > 0 ? c->grid_user : 8LL * c->num_cus;
+    grid = std::min<int64_t>(grid, items);
+    bool need_merge = false;
+    for (int b = 0; b < c->B; ++b) need_merge = need_merge || L[b] > c->chunk;
+    const hipError_t e = rswa::launch_decode(a, c->kv_dtype == RSWA_F32, out_dtype == RSWA_F32,
+                                             (int)grid, need_merge,
+                                             reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return RSWA_OK;
+  } catch (...) {
+    return fail(RSWA_E_INTERNAL, "exception in rswa_decode_attn");
+  }
+}
+
+rswa_status rswa_cache_steps(rswa_cache* c, int32_t* steps_host, void* stream) {
+  if (!c || !steps_host) return fail(RSWA_E_INVALID, "cache / steps_host is NULL");
+  try {
+    DeviceGuard g(c->device);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    int32_t err = 0;
+    hipError_t e = hipMemcpyAsync(steps_host, c->meta.steps, 4 * (size_t)c->B,
+                                  hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(&err, c->meta.err, 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "reading step counters");
+    if (err) return fail(RSWA_E_CAPACITY, "a full-causal append past max_steps was skipped");
+    return RSWA_OK;
+  } catch (...) {
+    return fail(RSWA_E_INTERNAL, "exception in rswa_cache_steps");
+  }
+}
+
+rswa_status rswa_cache_info(const rswa_cache* c, void** storage_dev, int64_t* seq_offset_host,
+                            int32_t* rows_host) {
+  if (!c) return fail(RSWA_E_INVALID, "cache is NULL");
+  if (storage_dev) *storage_dev = c->storage;
+  for (int b = 0; b < c->B; ++b) {
+    if (seq_offset_host) seq_offset_host[b] = c->plan.seq_off[b];
+    if (rows_host) rows_host[b] = c->plan.rows[b];
+  }
+  return RSWA_OK;
+}
+
+rswa_status rswa_cache_set_decode_split(rswa_cache* c, int32_t chunk_rows, int32_t grid_blocks) {
+  if (!c) return fail(RSWA_E_INVALID, "cache is NULL");
+  if (chunk_rows < 0 || chunk_rows % 64 != 0)
+    return fail(RSWA_E_INVALID, "chunk_rows must be 0 or a positive multiple of 64");
+  if (grid_blocks < 0) return fail(RSWA_E_INVALID, "grid_blocks must be >= 0");
+  c->chunk = chunk_rows ? chunk_rows : rswa::auto_chunk(c->plan, c->H, 4LL * c->num_cus);
+  c->grid_user = grid_blocks;
+  return RSWA_OK;
+}
+
+rswa_status rswa_cache_destroy(rswa_cache* c) {
+  if (!c) return RSWA_OK;
+  DeviceGuard g(c->device);
+  const hipError_t e = hipDeviceSynchronize();
+  release(c);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize(destroy)");
+  return RSWA_OK;
+}
+
+rswa_status rswa_prefill_attn(const void* q_dev, const void* k_dev, const void* v_dev,
+                              void* out_dev, int32_t out_dtype, const int32_t* cu_seqlens_dev,
+                              const int32_t* prefix_len_dev, const int32_t* window_dev,
+                              int32_t nseq, int32_t num_heads, int32_t head_dim,
+                              int32_t max_seqlen, int32_t prefix_causal, float softmax_scale,
+                              void* stream) {
+  if (!q_dev || !k_dev || !v_dev || !out_dev)
+    return fail(RSWA_E_INVALID, "q/k/v/out pointer is NULL");
+  if (!cu_seqlens_dev || !prefix_len_dev || !window_dev)
+    return fail(RSWA_E_INVALID, "sequence metadata pointer is NULL");
+  if (nseq < 1) return fail(RSWA_E_INVALID, "nseq must be >= 1");
+  if (num_heads < 1 || num_heads > rswa::kMaxHeads)
+    return fail(RSWA_E_INVALID, "num_heads out of range");
+  if (head_dim < 1) return fail(RSWA_E_INVALID, "head_dim must be positive");
+  if (head_dim != rswa::kPlanHeadDim) return fail(RSWA_E_UNSUPPORTED, "head_dim must be 128");
+  if (max_seqlen < 0) return fail(RSWA_E_INVALID, "max_seqlen must be >= 0");
+  if (out_dtype != RSWA_BF16 && out_dtype != RSWA_F32)
+    return fail(RSWA_E_INVALID, "out_dtype must be RSWA_BF16 or RSWA_F32");
+  if (prefix_causal != 0 && prefix_causal != 1)
+    return fail(RSWA_E_INVALID, "prefix_causal must be 0 or 1");
+  if (!(softmax_scale <= 0.f) && !std::isfinite(softmax_scale))
+    return fail(RSWA_E_INVALID, "softmax_scale must be finite");
+  if (max_seqlen == 0) return RSWA_OK;
+  try {
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+    rswa::PrefillArgs a{};
+    a.q = reinterpret_cast<const uint16_t*>(q_dev);
+    a.k = reinterpret_cast<const uint16_t*>(k_dev);
+    a.v = reinterpret_cast<const uint16_t*>(v_dev);
+    a.out = out_dev;
+    a.cu_seqlens = cu_seqlens_dev;
+    a.prefix_len = prefix_len_dev;
+    a.window = window_dev;
+    a.nseq = nseq;
+    a.heads = num_heads;
+    a.max_seqlen = max_seqlen;
+    a.prefix_causal = prefix_causal;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    const hipError_t e = rswa::launch_prefill(a, out_dtype == RSWA_F32,
+                                              reinterpret_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported) return fail(RSWA_E_UNSUPPORTED, "prefill kernel not built");
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    return RSWA_OK;
+  } catch (...) {
+    return fail(RSWA_E_INTERNAL, "exception in rswa_prefill_attn");
+  }
+}
+
+}  // extern "C"
