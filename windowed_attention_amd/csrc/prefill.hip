@@ -1,8 +1,284 @@
-// K3: R-SWA-masked prefill (bf16 MFMA). Not built yet: the launcher reports "not supported".
+// K3: R-SWA-masked prefill / teacher-forced attention on bf16 MFMA (gfx950).
+//
+// Mask (deep dive "Unlimited-OCR", N(t) code block; GeekNews "Unlimited OCR", R-SWA section and the
+// training section's packed multi-page sequences): in a sequence of S tokens whose first m are the
+// reference prefix, query p sees
+//   prefix key k < m: always (or only k <= p for prefix queries when the prefix is causal);
+//   output key k >= m: iff k <= p and p - k < n (its own window of n outputs, itself included).
+// A query tile therefore visits two key segments only: the prefix [0, m) and the window
+// [max(m, q_first - n + 1), q_last]; every other key tile is skipped without being loaded. Element
+// masks are applied only on tiles that need them (the prefix's ragged last tile, the causal-prefix
+// diagonal, and the window tiles).
+//
+// Tiling. A 256-thread workgroup owns 128 queries of one (sequence, head); each wave owns 32.
+// Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: the accumulator puts one
+// query per lane (lane % 32) and 16 of the block's 32 keys in that lane's registers, so the softmax
+// max/sum over keys is in-lane plus one exchange with lane ^ 32. The output is also formed
+// transposed, O^T = V^T P^T: the score accumulator registers, rounded to bf16, are already the B
+// operand of the second MFMA (the key order inside a 16-key step is a permutation that the V^T
+// operand follows), so P never leaves registers. K tiles (64 keys x 128) and V^T tiles
+// (128 x 64 keys) are double-buffered in LDS; Q stays in registers for the whole key loop.
+// Softmax runs in the log2 domain in float32; P is rounded to bf16 for the PV product and the
+// output is normalised by the float32 row sum.
+#include "device.h"
 #include "kernels.h"
 
 namespace rswa {
+namespace {
 
-hipError_t launch_prefill(const PrefillArgs&, int, hipStream_t) { return hipErrorNotSupported; }
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int BM = 128;                 // queries per workgroup
+constexpr int BN = 64;                  // keys per tile
+constexpr int KSTR = kHeadDim + 8;      // K tile row stride (bf16): 272 B rows
+constexpr int VSTR = BN + 4;            // V^T tile row stride (bf16): 136 B rows
+constexpr int K_TILE = BN * KSTR;       // bf16 elements per K buffer
+constexpr int V_TILE = kHeadDim * VSTR; // bf16 elements per V^T buffer
+
+__device__ __forceinline__ floatx16 mfma32(const uint4& a, const uint4& b, const floatx16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2v_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+struct TileSched {
+  int n_pre;   // tiles over the prefix segment [0, pre_end)
+  int pre_end;
+  int ws;      // first key of the window segment
+  int ntiles;
+  __device__ __forceinline__ int start(int j) const { return j < n_pre ? j * BN : ws + (j - n_pre) * BN; }
+};
+
+// Global -> registers: thread t loads 4 consecutive keys x 8 dims of K and of V.
+__device__ __forceinline__ void load_tile(uint4 (&rk)[4], uint4 (&rv)[4], const uint16_t* kbase,
+                                          const uint16_t* vbase, int64_t row_stride, int k0,
+                                          int kmax) {
+  const int t = threadIdx.x;
+  const int c = t & 15, kg = t >> 4;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int key = min(k0 + kg * 4 + u, kmax);
+    rk[u] = *reinterpret_cast<const uint4*>(kbase + key * row_stride + c * 8);
+    rv[u] = *reinterpret_cast<const uint4*>(vbase + key * row_stride + c * 8);
+  }
+}
+
+__device__ __forceinline__ uint32_t word(const uint4& v, int w) {
+  return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
+}
+
+__device__ __forceinline__ void store_tile(const uint4 (&rk)[4], const uint4 (&rv)[4], uint16_t* sk,
+                                           uint16_t* svt) {
+  const int t = threadIdx.x;
+  const int c = t & 15, kg = t >> 4;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    *reinterpret_cast<uint4*>(sk + (kg * 4 + u) * KSTR + c * 8) = rk[u];
+  // transpose 4 keys x 8 dims -> 8 dims x 4 keys
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t x0 = word(rv[0], w), x1 = word(rv[1], w);
+    const uint32_t x2 = word(rv[2], w), x3 = word(rv[3], w);
+    const uint2 lo = make_uint2((x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16));
+    const uint2 hi = make_uint2((x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u));
+    *reinterpret_cast<uint2*>(svt + (c * 8 + 2 * w) * VSTR + kg * 4) = lo;
+    *reinterpret_cast<uint2*>(svt + (c * 8 + 2 * w + 1) * VSTR + kg * 4) = hi;
+  }
+}
+
+template <typename OUT>
+__device__ __forceinline__ void store_out4(OUT* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store_out4<float>(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+template <>
+__device__ __forceinline__ void store_out4<uint16_t>(uint16_t* p, float a, float b, float c, float d) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16),
+                                            f32_to_bf16_bits(c) | (f32_to_bf16_bits(d) << 16));
+}
+
+template <typename OUT>
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2 * K_TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sVt[2 * V_TILE];
+
+  const int s = blockIdx.z, h = blockIdx.y;
+  const int cu0 = a.cu_seqlens[s];
+  const int S = a.cu_seqlens[s + 1] - cu0;
+  const int q0 = blockIdx.x * BM;
+  if (q0 >= S) return;
+  const int q1 = min(q0 + BM, S);
+  const int m = a.prefix_len[s];
+  const int n = a.window[s];
+  const bool pc = a.prefix_causal != 0;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lq = lane & 31, half = lane >> 5;
+  const int64_t rs = (int64_t)a.heads * kHeadDim;  // token row stride (elements)
+  const uint16_t* qbase = a.q + ((int64_t)cu0 * a.heads + h) * kHeadDim;
+  const uint16_t* kbase = a.k + ((int64_t)cu0 * a.heads + h) * kHeadDim;
+  const uint16_t* vbase = a.v + ((int64_t)cu0 * a.heads + h) * kHeadDim;
+
+  // this lane's query and its Q^T operand (8 d-steps of 16)
+  const int p = q0 + wave * 32 + lq;
+  const int pq = min(p, S - 1);
+  uint4 qf[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st)
+    qf[st] = *reinterpret_cast<const uint4*>(qbase + pq * rs + st * 16 + half * 8);
+
+  // key tiles: the prefix segment, then the output window segment
+  TileSched ts;
+  ts.pre_end = (pc && q1 <= m) ? q1 : m;
+  ts.n_pre = (ts.pre_end + BN - 1) / BN;
+  int n_win = 0;
+  ts.ws = 0;
+  if (q1 > m) {
+    ts.ws = max(m, max(q0, m) - n + 1);
+    n_win = (q1 - ts.ws + BN - 1) / BN;
+  }
+  ts.ntiles = ts.n_pre + n_win;
+
+  const float c = a.scale_log2;
+  float m_run = kNegBig, l_run = 0.f;
+  floatx16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+
+  uint4 rk[4], rv[4];
+  load_tile(rk, rv, kbase, vbase, rs, ts.start(0), S - 1);
+  store_tile(rk, rv, sK, sVt);
+  __syncthreads();
+
+  for (int j = 0; j < ts.ntiles; ++j) {
+    const int buf = j & 1;
+    const bool more = j + 1 < ts.ntiles;
+    if (more) load_tile(rk, rv, kbase, vbase, rs, ts.start(j + 1), S - 1);
+    const uint16_t* sk = sK + buf * K_TILE;
+    const uint16_t* svt = sVt + buf * V_TILE;
+    const int k0 = ts.start(j);
+    const bool is_pre = j < ts.n_pre;
+
+    // S^T = K Q^T for two 32-key blocks
+    floatx16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const uint4 ka =
+            *reinterpret_cast<const uint4*>(sk + (kb * 32 + lq) * KSTR + st * 16 + half * 8);
+        sacc[kb] = mfma32(ka, qf[st], sacc[kb]);
+      }
+    }
+
+    // element mask where the tile is not fully visible
+    const bool need_mask = is_pre ? (k0 + BN > m || (pc && q0 < m && k0 + BN - 1 > q0)) : true;
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int k = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          bool vis;
+          if (is_pre)
+            vis = k < m && (!pc || p >= m || k <= p);
+          else
+            vis = k >= m && k <= p && p - k < n;
+          if (!vis) sacc[kb][r] = -INFINITY;
+        }
+    }
+
+    // online softmax (log2 domain), one query per lane, keys split across lane and lane ^ 32
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * c);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+    uint4 pb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float pr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        pr[r] = fast_exp2(fmaf(sacc[kb][r], c, -m_new));
+        psum += pr[r];
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+        pb[kb][st] = make_uint4(pack_bf16(pr[8 * st + 0], pr[8 * st + 1]),
+                                pack_bf16(pr[8 * st + 2], pr[8 * st + 3]),
+                                pack_bf16(pr[8 * st + 4], pr[8 * st + 5]),
+                                pack_bf16(pr[8 * st + 6], pr[8 * st + 7]));
+    }
+    l_run = fmaf(l_run, alpha, psum);
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+
+    // O^T += V^T P^T: for d block db, key step (kb, st) the A operand holds
+    // V[key = kb*32 + 16 st + 8 (e / 4) + 4 half + e % 4][d = db*32 + lq], e = 0..7
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const uint16_t* vrow = svt + (db * 32 + lq) * VSTR + half * 4;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kb * 32 + 16 * st);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + kb * 32 + 16 * st + 8);
+          o[db] = mfma32(make_uint4(lo.x, lo.y, hi.x, hi.y), pb[kb][st], o[db]);
+        }
+    }
+
+    if (more) store_tile(rk, rv, sK + (buf ^ 1) * K_TILE, sVt + (buf ^ 1) * V_TILE);
+    __syncthreads();
+  }
+
+  // normalise and write: lane holds query p, dims db*32 + 8 g + 4 half + (0..3)
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (p < q1) {
+    const float inv = 1.f / l_tot;
+    OUT* orow = reinterpret_cast<OUT*>(a.out) + ((int64_t)(cu0 + p) * a.heads + h) * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store_out4<OUT>(orow + db * 32 + 8 * g + 4 * half, o[db][4 * g] * inv,
+                        o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, int out_f32, hipStream_t s) {
+  const dim3 grid((a.max_seqlen + BM - 1) / BM, a.heads, a.nseq);
+  if (out_f32)
+    hipLaunchKernelGGL(prefill_kernel<float>, grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(prefill_kernel<uint16_t>, grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
 
 }  // namespace rswa
