@@ -29,6 +29,8 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in VGPRs
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int BM = 128;                 // queries per workgroup
@@ -38,7 +40,7 @@ constexpr int VSTR = BN + 4;            // V^T tile row stride (bf16): 136 B row
 constexpr int K_TILE = BN * KSTR;       // bf16 elements per K buffer
 constexpr int V_TILE = kHeadDim * VSTR; // bf16 elements per V^T buffer
 
-__device__ __forceinline__ floatx16 mfma32(const uint4& a, const uint4& b, const floatx16& c) {
+__device__ __forceinline__ floatx16 mfma32(const u32x4& a, const u32x4& b, const floatx16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
@@ -59,7 +61,7 @@ struct TileSched {
 };
 
 // Global -> registers: thread t loads 4 consecutive keys x 8 dims of K and of V.
-__device__ __forceinline__ void load_tile(uint4 (&rk)[4], uint4 (&rv)[4], const uint16_t* kbase,
+__device__ __forceinline__ void load_tile(u32x4 (&rk)[4], u32x4 (&rv)[4], const uint16_t* kbase,
                                           const uint16_t* vbase, int64_t row_stride, int k0,
                                           int kmax) {
   const int t = threadIdx.x;
@@ -67,31 +69,31 @@ __device__ __forceinline__ void load_tile(uint4 (&rk)[4], uint4 (&rv)[4], const 
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int key = min(k0 + kg * 4 + u, kmax);
-    rk[u] = *reinterpret_cast<const uint4*>(kbase + key * row_stride + c * 8);
-    rv[u] = *reinterpret_cast<const uint4*>(vbase + key * row_stride + c * 8);
+    rk[u] = *reinterpret_cast<const u32x4*>(kbase + key * row_stride + c * 8);
+    rv[u] = *reinterpret_cast<const u32x4*>(vbase + key * row_stride + c * 8);
   }
 }
 
-__device__ __forceinline__ uint32_t word(const uint4& v, int w) {
+__device__ __forceinline__ uint32_t word(const u32x4& v, int w) {
   return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
 }
 
-__device__ __forceinline__ void store_tile(const uint4 (&rk)[4], const uint4 (&rv)[4], uint16_t* sk,
+__device__ __forceinline__ void store_tile(const u32x4 (&rk)[4], const u32x4 (&rv)[4], uint16_t* sk,
                                            uint16_t* svt) {
   const int t = threadIdx.x;
   const int c = t & 15, kg = t >> 4;
 #pragma unroll
   for (int u = 0; u < 4; ++u)
-    *reinterpret_cast<uint4*>(sk + (kg * 4 + u) * KSTR + c * 8) = rk[u];
+    *reinterpret_cast<u32x4*>(sk + (kg * 4 + u) * KSTR + c * 8) = rk[u];
   // transpose 4 keys x 8 dims -> 8 dims x 4 keys
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     const uint32_t x0 = word(rv[0], w), x1 = word(rv[1], w);
     const uint32_t x2 = word(rv[2], w), x3 = word(rv[3], w);
-    const uint2 lo = make_uint2((x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16));
-    const uint2 hi = make_uint2((x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u));
-    *reinterpret_cast<uint2*>(svt + (c * 8 + 2 * w) * VSTR + kg * 4) = lo;
-    *reinterpret_cast<uint2*>(svt + (c * 8 + 2 * w + 1) * VSTR + kg * 4) = hi;
+    const u32x2 lo = u32x2{(x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16)};
+    const u32x2 hi = u32x2{(x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u)};
+    *reinterpret_cast<u32x2*>(svt + (c * 8 + 2 * w) * VSTR + kg * 4) = lo;
+    *reinterpret_cast<u32x2*>(svt + (c * 8 + 2 * w + 1) * VSTR + kg * 4) = hi;
   }
 }
 
@@ -103,8 +105,8 @@ __device__ __forceinline__ void store_out4<float>(float* p, float a, float b, fl
 }
 template <>
 __device__ __forceinline__ void store_out4<uint16_t>(uint16_t* p, float a, float b, float c, float d) {
-  *reinterpret_cast<uint2*>(p) = make_uint2(f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16),
-                                            f32_to_bf16_bits(c) | (f32_to_bf16_bits(d) << 16));
+  *reinterpret_cast<u32x2*>(p) = u32x2{f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16),
+                                       f32_to_bf16_bits(c) | (f32_to_bf16_bits(d) << 16)};
 }
 
 template <typename OUT>
@@ -132,10 +134,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   // this lane's query and its Q^T operand (8 d-steps of 16)
   const int p = q0 + wave * 32 + lq;
   const int pq = min(p, S - 1);
-  uint4 qf[8];
+  u32x4 qf[8];
 #pragma unroll
   for (int st = 0; st < 8; ++st)
-    qf[st] = *reinterpret_cast<const uint4*>(qbase + pq * rs + st * 16 + half * 8);
+    qf[st] = *reinterpret_cast<const u32x4*>(qbase + pq * rs + st * 16 + half * 8);
 
   // key tiles: the prefix segment, then the output window segment
   TileSched ts;
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
 
-  uint4 rk[4], rv[4];
+  u32x4 rk[4], rv[4];
   load_tile(rk, rv, kbase, vbase, rs, ts.start(0), S - 1);
   store_tile(rk, rv, sK, sVt);
   __syncthreads();
@@ -179,8 +181,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        const uint4 ka =
-            *reinterpret_cast<const uint4*>(sk + (kb * 32 + lq) * KSTR + st * 16 + half * 8);
+        const u32x4 ka =
+            *reinterpret_cast<const u32x4*>(sk + (kb * 32 + lq) * KSTR + st * 16 + half * 8);
         sacc[kb] = mfma32(ka, qf[st], sacc[kb]);
       }
     }
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
     float psum = 0.f;
-    uint4 pb[2][2];
+    u32x4 pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float pr[16];
@@ -224,10 +226,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       }
 #pragma unroll
       for (int st = 0; st < 2; ++st)
-        pb[kb][st] = make_uint4(pack_bf16(pr[8 * st + 0], pr[8 * st + 1]),
-                                pack_bf16(pr[8 * st + 2], pr[8 * st + 3]),
-                                pack_bf16(pr[8 * st + 4], pr[8 * st + 5]),
-                                pack_bf16(pr[8 * st + 6], pr[8 * st + 7]));
+        pb[kb][st] = u32x4{pack_bf16(pr[8 * st + 0], pr[8 * st + 1]),
+                           pack_bf16(pr[8 * st + 2], pr[8 * st + 3]),
+                           pack_bf16(pr[8 * st + 4], pr[8 * st + 5]),
+                           pack_bf16(pr[8 * st + 6], pr[8 * st + 7])};
     }
     l_run = fmaf(l_run, alpha, psum);
     if (__any(alpha != 1.f)) {
@@ -246,9 +248,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kb * 32 + 16 * st);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + kb * 32 + 16 * st + 8);
-          o[db] = mfma32(make_uint4(lo.x, lo.y, hi.x, hi.y), pb[kb][st], o[db]);
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kb * 32 + 16 * st);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + kb * 32 + 16 * st + 8);
+          o[db] = mfma32(u32x4{lo.x, lo.y, hi.x, hi.y}, pb[kb][st], o[db]);
         }
     }
 
