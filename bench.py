@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--growth", action="store_true", help="multi-page R-SWA vs full-causal curve")
     ap.add_argument("--no-kernel-events", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time rswa_append_kv + rswa_decode_attn instead of rswa_decode_step")
     ap.add_argument("--prefill-runs", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     return ap.parse_args()
@@ -130,16 +132,23 @@ def run_decode(args, wl, mode_full: bool, steps: int, warmup: int, kernel_events
     ob = out.data_ptr()
     ab = act.data_ptr() if act is not None else None
 
-    def step(t):  # t is 1-based
+    fused = not args.unfused
+
+    def step(t):  # t is 1-based; the separate path's append (the fused path appends in decode)
         o = (t - 1) * step_bytes
         a = None if ab is None else ab + (t - 1) * wl.batch
-        r = lib.rswa_append_kv(h, kb + o, vb + o, a, sp)
-        if r:
-            raise RuntimeError(f"append failed: {r} {lib.rswa_last_error()}")
+        if not fused:
+            r = lib.rswa_append_kv(h, kb + o, vb + o, a, sp)
+            if r:
+                raise RuntimeError(f"append failed: {r} {lib.rswa_last_error()}")
         return o, a
 
     def decode(o, a):
-        r = lib.rswa_decode_attn(h, qb + o, ob, out_code, ctypes.c_float(0.0), a, sp)
+        if fused:
+            r = lib.rswa_decode_step(h, qb + o, kb + o, vb + o, ob, out_code, ctypes.c_float(0.0),
+                                     a, sp)
+        else:
+            r = lib.rswa_decode_attn(h, qb + o, ob, out_code, ctypes.c_float(0.0), a, sp)
         if r:
             raise RuntimeError(f"decode failed: {r} {lib.rswa_last_error()}")
 
@@ -187,9 +196,11 @@ def run_decode(args, wl, mode_full: bool, steps: int, warmup: int, kernel_events
     dec_bytes = np.array([decode_bytes(wl, t, mode_full, out_elem) for t in ts], dtype=np.float64)
     app_bytes = np.array([append_bytes(wl, t) for t in ts], dtype=np.float64)
     tokens = int(sum(int((wl.steps >= t).sum()) for t in ts))
+    # bytes of the launch the events bracket: the fused step also moves the append's rows
+    launch_bytes = dec_bytes + app_bytes if fused else dec_bytes
     return dict(elapsed_ms=elapsed_ms, wall_s=wall, kern_ms=kern_ms, lat=lat,
-                dec_bytes=dec_bytes, app_bytes=app_bytes, tokens=tokens,
-                steps_done=steps_done.tolist())
+                dec_bytes=dec_bytes, app_bytes=app_bytes, launch_bytes=launch_bytes,
+                tokens=tokens, fused=fused, steps_done=steps_done.tolist())
 
 
 def flatness(lat, n, T):
@@ -343,14 +354,15 @@ def main():
         res["hbm_gbs_step"] = step_bytes / (ms_step * 1e-3) / 1e9
         if r["kern_ms"] is not None:
             kms = float(r["kern_ms"].mean())
-            ach = float(r["dec_bytes"].mean()) / (kms * 1e-3) / 1e9
+            ach = float(r["launch_bytes"].mean()) / (kms * 1e-3) / 1e9
             res["roofline"] = dict(bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
                                    frac=ach / PEAK_HBM_GBS,
                                    traffic=traffic_from_profile("decode",
                                                                 source_hash(DECODE_SOURCES)),
-                                   kernel="rswa decode (split-K + merge)",
+                                   kernel=("fused append + decode step" if r["fused"] else
+                                           "decode (separate append)"),
                                    avg_launch_us=kms * 1e3,
-                                   bytes_per_launch=float(r["dec_bytes"].mean()))
+                                   bytes_per_launch=float(r["launch_bytes"].mean()))
         res["latency_vs_t"] = [[int(t), round(u, 3)] for t, u in r["lat"]]
         res["flatness"] = flatness(r["lat"], int(wl.window[0]), warmup + steps)
     if not args.no_prefill:

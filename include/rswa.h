@@ -120,6 +120,16 @@ rswa_status rswa_append_kv(rswa_cache* cache, const void* k_dev, const void* v_d
 rswa_status rswa_decode_attn(rswa_cache* cache, const void* q_dev, void* out_dev, int32_t out_dtype,
                              float softmax_scale, const uint8_t* active_dev, void* stream);
 
+/* K1 + K2 fused: one decode step in one launch. Equivalent to rswa_append_kv(k_dev, v_dev,
+ * active_dev) followed by rswa_decode_attn(q_dev, ...), with the same results bit for bit: the
+ * workgroup whose share of the key range holds the new row takes it from k_dev / v_dev and writes it
+ * into the ring slot, so the evicted output is never read and no second launch is needed for the
+ * append. Same arguments, layouts and errors as the two calls it replaces (RSWA_E_CAPACITY as in
+ * rswa_append_kv). */
+rswa_status rswa_decode_step(rswa_cache* cache, const void* q_dev, const void* k_dev,
+                             const void* v_dev, void* out_dev, int32_t out_dtype,
+                             float softmax_scale, const uint8_t* active_dev, void* stream);
+
 /* K3, R-SWA-masked prefill / teacher-forced pass over packed sequences (bf16 MFMA, fp32 softmax).
  * Sequence s occupies token rows [cu_seqlens[s], cu_seqlens[s+1]) of q/k/v/out, its first
  * m_s = prefix_len[s] tokens being the prefix. Query p (position within the sequence) sees key k
@@ -149,9 +159,12 @@ rswa_status rswa_cache_steps(rswa_cache* cache, int32_t* steps_host, void* strea
 rswa_status rswa_cache_info(const rswa_cache* cache, void** storage_dev,
                             int64_t* seq_offset_host /* [B] */, int32_t* rows_host /* [B] */);
 
-/* Decode work split: each (b, h) key range is cut into chunks of chunk_rows rows (a multiple of
- * 64, or 0 = automatic), processed by grid_blocks persistent workgroups (0 = automatic). Results
- * do not depend on these except through float32 summation order. Host only. */
+/* Decode work split. By default a batch of equal key ranges that about fills one round of
+ * resident workgroups gets one workgroup per (b, h) range; otherwise the concatenated key ranges
+ * are cut into equal contiguous pieces, one per resident workgroup, and split ranges are merged in a
+ * second kernel. chunk_rows (> 0) sets the fewest rows a piece may hold and grid_blocks (> 0) the
+ * number of pieces; either one forces the piece layout. 0 restores the automatic choice. Results
+ * depend on these only through float32 summation order. Host only. */
 rswa_status rswa_cache_set_decode_split(rswa_cache* cache, int32_t chunk_rows, int32_t grid_blocks);
 
 /* Release the cache: synchronizes the stream it was created on, frees library-owned memory.

@@ -63,8 +63,10 @@ class Trajectory:
                                   max_steps=max_steps, kv_dtype=kv_torch_dtype(wl.dtype),
                                   storage=storage)
 
-    def run(self, checkpoints, out_dtype=torch.float32, t_end: int | None = None):
-        """Append + decode every step 1..t_end; return {t: out [B, H, D] float32 numpy}."""
+    def run(self, checkpoints, out_dtype=torch.float32, t_end: int | None = None,
+            fused: bool = False, raw: bool = False):
+        """Run steps 1..t_end (append then decode, or the fused step); return
+        {t: out [B, H, D]} at the checkpoints (float32 numpy, or the raw output tensor copy)."""
         wl = self.wl
         t_end = wl.T if t_end is None else t_end
         out = torch.zeros((wl.batch, 16, 128), dtype=out_dtype, device="cuda")
@@ -72,9 +74,12 @@ class Trajectory:
         res = {}
         for t in range(1, t_end + 1):
             act = None if self.active is None else self.active[t - 1]
-            self.cache.append(self.k[t - 1], self.v[t - 1], act)
-            self.cache.decode(self.q[t - 1], out, active=act)
+            if fused:
+                self.cache.step(self.q[t - 1], self.k[t - 1], self.v[t - 1], out, active=act)
+            else:
+                self.cache.append(self.k[t - 1], self.v[t - 1], act)
+                self.cache.decode(self.q[t - 1], out, active=act)
             if t in keep:
-                res[t] = out.float().cpu().numpy()
+                res[t] = out.clone() if raw else out.float().cpu().numpy()
         torch.cuda.synchronize()
         return res

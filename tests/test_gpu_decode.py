@@ -213,12 +213,63 @@ def test_ragged_small_one_launch(wa):
 
 
 # ---------------------------------------------------------------------------------------------
+# K1 + K2 fused in one launch: bit-identical to append then decode
+# ---------------------------------------------------------------------------------------------
+FUSED_CASES = [
+    # (prefix lengths, windows, steps, mode, split setting)
+    ([272] * 4, [128] * 4, [300] * 4, 0, (0, 0)),          # equal ranges
+    ([272, 0, 37, 600], [128, 5, 64, 16], [300, 300, 250, 120], 0, (0, 0)),  # ragged + mask
+    ([100, 9], [16, 5], [200, 200], 0, (64, 7)),             # pieces forced, 7 workgroups
+    ([50, 0, 130], [8, 8, 8], [150, 150, 150], 1, (0, 0)),  # full causal
+    ([5155], [128], [200], 0, (0, 0)),                       # one long range over many pieces
+]
+
+
+@pytest.mark.parametrize("case", range(len(FUSED_CASES)))
+def test_fused_step_equals_append_then_decode(wa, case):
+    m, n, T, mode, split = FUSED_CASES[case]
+    wl = W.make_decode("fused", 80 + case, "bf16", m, n, T, seed=20 + case, outlier_p=0.01)
+    off, rows, nbytes = wa.rswa_cache_plan(m, n if mode == 0 else None, T if mode else None,
+                                           mode=mode)
+    sa = torch.full((nbytes // 2,), CANARY, dtype=torch.int16, device="cuda")
+    sb = torch.full((nbytes // 2,), CANARY, dtype=torch.int16, device="cuda")
+    a = Trajectory(wa, wl, mode, storage=sa)
+    b = Trajectory(wa, wl, mode, storage=sb)
+    a.cache.set_decode_split(*split)
+    b.cache.set_decode_split(*split)
+    steps = range(1, wl.T + 1)
+    ra = a.run(steps, raw=True)
+    rb = b.run(steps, fused=True, raw=True)
+    for t in steps:
+        live = wl.steps >= t
+        assert torch.equal(ra[t][torch.from_numpy(live).cuda()],
+                           rb[t][torch.from_numpy(live).cuda()]), f"step {t}"
+    assert torch.equal(sa, sb)
+    np.testing.assert_array_equal(a.cache.steps(), b.cache.steps())
+    np.testing.assert_array_equal(b.cache.steps(), wl.steps)
+    check_steps(wl, mode, {t: rb[t].float().cpu().numpy() for t in [1, 2, 17, 64, 65, 128, 129,
+                                                                   int(wl.T)] if t <= wl.T})
+    a.cache.close()
+    b.cache.close()
+
+
+def test_fused_step_capacity(wa):
+    wl = W.make_decode("cap2", 85, "bf16", [3], [8], [4], seed=25)
+    tr = Trajectory(wa, wl, wa.MODE_FULL_CAUSAL)
+    tr.run(range(1, 5), fused=True)
+    with pytest.raises(wa.RswaError) as e:
+        tr.cache.step(tr.q[0], tr.k[0], tr.v[0])
+    assert e.value.status == -3
+    tr.cache.close()
+
+
+# ---------------------------------------------------------------------------------------------
 # full-size workloads, sampled steps, benchmark launch configuration
 # ---------------------------------------------------------------------------------------------
 def test_cfg_single_page_fp32_all_steps(wa):
     wl = W.decode_config(1)
     tr = Trajectory(wa, wl, wa.MODE_RSWA)
-    got = tr.run(range(1, wl.T + 1))
+    got = tr.run(range(1, wl.T + 1), fused=True)
     worst = check_steps(wl, 0, got)
     print(f"single-page fp32 decode: worst max-abs error {worst:.3e} over {len(got)} steps")
     tr.cache.close()
@@ -229,7 +280,7 @@ def test_cfg_batched_single_page_sampled(wa):
     wl = W.decode_config(2)
     tr = Trajectory(wa, wl, wa.MODE_RSWA)
     steps = sample_steps(wl.T, 128, 272)
-    got = tr.run(steps)
+    got = tr.run(steps, fused=True)
     worst = check_steps(wl, 0, got, seqs_per_step=6)
     print(f"batched decode: worst max-abs error {worst:.3e} at {len(steps)} steps")
     tr.cache.close()
@@ -241,7 +292,7 @@ def test_cfg_multi_page_sampled(wa, mode):
     wl = W.decode_config(3)
     tr = Trajectory(wa, wl, mode)
     steps = sample_steps(wl.T, 128, 5155, full=bool(mode), crossings=12, extra=8)
-    got = tr.run(steps)
+    got = tr.run(steps, fused=True)
     worst = check_steps(wl, mode, got, seqs_per_step=2)
     print(f"multi-page decode mode={mode}: worst max-abs error {worst:.3e}")
     tr.cache.close()
@@ -252,7 +303,7 @@ def test_cfg_ragged_sampled(wa):
     wl = W.varlen_config(0)
     tr = Trajectory(wa, wl, wa.MODE_RSWA)
     steps = sample_steps(wl.T, 64, 272, extra=12)
-    got = tr.run(steps)
+    got = tr.run(steps, fused=True)
     worst = check_steps(wl, 0, got, seqs_per_step=3)
     print(f"ragged decode: worst max-abs error {worst:.3e}")
     tr.cache.close()

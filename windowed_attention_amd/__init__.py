@@ -24,7 +24,7 @@ STATUS = {0: "RSWA_OK", -1: "RSWA_E_INVALID", -2: "RSWA_E_UNSUPPORTED", -3: "RSW
 
 # Every symbol include/rswa.h declares.
 EXPORTS = ("rswa_cache_plan", "rswa_cache_bytes", "rswa_cache_create", "rswa_append_kv",
-           "rswa_decode_attn", "rswa_prefill_attn", "rswa_cache_steps", "rswa_cache_info",
+           "rswa_decode_attn", "rswa_decode_step", "rswa_prefill_attn", "rswa_cache_steps", "rswa_cache_info",
            "rswa_cache_set_decode_split", "rswa_cache_destroy", "rswa_status_str",
            "rswa_last_error")
 
@@ -59,6 +59,7 @@ def _load():
         "rswa_cache_create": (i32, [pdesc, vp, vp, vp, ctypes.POINTER(vp)]),
         "rswa_append_kv": (i32, [vp, vp, vp, vp, vp]),
         "rswa_decode_attn": (i32, [vp, vp, vp, i32, f32, vp, vp]),
+        "rswa_decode_step": (i32, [vp, vp, vp, vp, vp, i32, f32, vp, vp]),
         "rswa_prefill_attn": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                                     vp]),
         "rswa_cache_steps": (i32, [vp, pi32, vp]),
@@ -215,6 +216,15 @@ class RswaCache:
         rswa_decode_attn(self, q, out, scale, active, stream)
         return out
 
+    def step(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+             out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
+             scale: float = 0.0, active: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """Append (k, v) and attend with q in one launch (same result as append + decode)."""
+        if out is None:
+            out = torch.empty(self._bhd(), dtype=out_dtype, device=q.device)
+        rswa_decode_step(self, q, k, v, out, scale, active, stream)
+        return out
+
     def steps(self, stream=None) -> np.ndarray:
         s = np.zeros(self.batch, dtype=np.int32)
         _check(_lib.rswa_cache_steps(self.handle, s.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
@@ -274,6 +284,19 @@ def rswa_decode_attn(cache: RswaCache, q: torch.Tensor, out: torch.Tensor, scale
                                  ctypes.c_float(scale),
                                  _dev(active, "active", torch.uint8, (cache.batch,)),
                                  _stream(stream)), "rswa_decode_attn")
+
+
+def rswa_decode_step(cache: RswaCache, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     out: torch.Tensor, scale: float = 0.0, active: torch.Tensor | None = None,
+                     stream=None) -> None:
+    shape = cache._bhd()
+    _check(_lib.rswa_decode_step(cache.handle, _dev(q, "q", cache.kv_dtype, shape),
+                                 _dev(k, "k", cache.kv_dtype, shape),
+                                 _dev(v, "v", cache.kv_dtype, shape),
+                                 _dev(out, "out", None, shape), _dtype_code(out.dtype),
+                                 ctypes.c_float(scale),
+                                 _dev(active, "active", torch.uint8, (cache.batch,)),
+                                 _stream(stream)), "rswa_decode_step")
 
 
 def rswa_cache_destroy(cache: RswaCache) -> None:

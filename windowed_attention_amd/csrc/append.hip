@@ -16,16 +16,22 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One workgroup per sequence: every thread reads t_b before the barrier, thread 0 advances it
-// after, so the counter update needs no atomics.
+// One workgroup per sequence. Counters are double-buffered: t_b is read from steps_in and
+// t_b + (appended) written to steps_out, so no workgroup of this launch races on them.
 template <int ELEM>
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
   const int b = blockIdx.x;
-  if (a.active && !a.active[b]) return;
-  const int t = a.meta.steps[b];
+  const int t = a.steps_in[b];
+  if (a.active && !a.active[b]) {
+    if (threadIdx.x == 0) a.steps_out[b] = t;
+    return;
+  }
   const int cap = a.meta.cap[b];
   if (a.full_causal && t >= cap) {
-    if (threadIdx.x == 0) *a.meta.err = 1;
+    if (threadIdx.x == 0) {
+      *a.meta.err = 1;
+      a.steps_out[b] = t;
+    }
     return;
   }
   const int m = a.meta.prefix_len[b];
@@ -46,8 +52,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     *reinterpret_cast<uint4*>(seq + dk) = kx;
     *reinterpret_cast<uint4*>(seq + dv) = vx;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) a.meta.steps[b] = t + 1;
+  if (threadIdx.x == 0) a.steps_out[b] = t + 1;
 }
 
 // Packed token-major prefix [sum m][H][D] -> head-major rows [0, m_b) of sequence b.

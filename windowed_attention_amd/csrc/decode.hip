@@ -1,4 +1,5 @@
-// K2: split-K flash decode over the R-SWA key set (prefix u window), and its cross-split merge.
+// K2: flash decode over the R-SWA key set (prefix u window), optionally fused with K1's append,
+// and the merge of split partial results.
 //
 // For sequence b and head h the live keys are the contiguous cache rows [0, L_b), with
 // L_b = m_b + min(n_b, t_b) in R-SWA mode (the static prefix then the ring slots in use) or
@@ -6,65 +7,104 @@
 // invariant under key permutation. (Key set: deep dive "Unlimited-OCR", N(t) code block; cache
 // size: GeekNews "Unlimited OCR", KV cache management section.)
 //
-// Work decomposition. Each (b, h) key range is cut into chunks of `chunk` rows; an item is one
-// (b, h, chunk). A fixed grid of persistent 256-thread workgroups walks the item list, which every
-// workgroup derives on the device from the step counters (so no host sync and no per-step table
-// upload), with chunk counts a smooth function of L_b.
+// Work decomposition. Every workgroup derives the plan on the device from the step counters, so a
+// step needs no host sync and no table upload:
+//  * aligned: one 256-thread workgroup per (b, h) key range, used when the batch's ranges are
+//    equal and about fill one round of resident workgroups;
+//  * stream-K: the concatenation of all (b, h) key ranges is cut into equal contiguous pieces, one
+//    per resident workgroup, so every workgroup streams the same number of rows (no tail round,
+//    balanced for ragged batches). A piece may cover parts of several ranges; a range split over
+//    several pieces leaves float32 partials (max, sum, numerator[128]) that a second kernel merges:
+//      o = sum_s 2^(M_s - M) A_s / sum_s 2^(M_s - M) l_s,   M = max_s M_s.
 //
-// Inside an item. A row of K or V is 256 B (bf16) or 512 B (fp32): 16 or 32 lanes each load 16 B
-// of it, so a wave streams 4 (bf16) or 2 (fp32) rows per load instruction, 1 KiB contiguous.
-// Each lane group keeps its own float32 online-softmax state (running max in the log2 domain,
-// running sum, and its 8 or 4 output dims); q.k partial dots are summed across the group with DPP
-// row operations. At the end of the item the 16 (or 8) group states are merged through LDS; a
-// single-chunk (b, h) writes its output directly, otherwise the item leaves a partial
-// (max, sum, numerator[128]) in the workspace and a second kernel merges the partials:
-//   o = sum_s 2^(M_s - M) A_s / sum_s 2^(M_s - M) l_s,   M = max_s M_s.
-// All arithmetic after the bf16 loads is float32.
+// Inside a piece. A row of K or V is 256 B (bf16) or 512 B (fp32): 16 or 32 lanes each load 16 B of
+// it, so a wave streams 4 (bf16) or 2 (fp32) rows per load instruction, 1 KiB contiguous, and the
+// next tile's rows are loaded while the current one is reduced. Each lane group keeps its own
+// float32 online-softmax state (running max in the log2 domain, running sum, 8 or 4 output dims);
+// q.k partial dot products are summed across the group with DPP row operations. At the end of a
+// range the group states are merged through LDS.
+//
+// Fused append (K1 inside K2). When the launch carries the new k/v rows, the new row's slot
+// r = m_b + (t_b mod n_b) (or m_b + t_b) is part of the live range after the append; the lane group
+// that meets this row in its piece takes k/v from the input instead of the cache and writes them
+// into the slot, so no other workgroup reads the slot during the launch and the evicted output is
+// never seen.
 #include "device.h"
 #include "kernels.h"
 
 namespace rswa {
 namespace {
 
+#ifndef RSWA_DECODE_PREFETCH
+#define RSWA_DECODE_PREFETCH 0  // 1: load the next row tile while reducing the current one
+#endif
+
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxGroups = kWaves * 4;  // bf16: 4 row groups per wave
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename KV> struct Lanes;
 template <> struct Lanes<uint16_t> { static constexpr int VEC = 8, GL = 16; };
 template <> struct Lanes<float> { static constexpr int VEC = 4, GL = 32; };
 
-__device__ __forceinline__ int live_rows(const DecodeArgs& a, int b) {
-  if (a.active && !a.active[b]) return 0;
-  return a.meta.prefix_len[b] + min(a.meta.steps[b], a.meta.cap[b]);
+// Live rows of sequence b after this launch's append (0 if inactive), and whether it appends.
+struct SeqState {
+  int L;
+  int t;       // step counter before the launch
+  bool app;    // this launch appends for b
+};
+
+__device__ __forceinline__ SeqState seq_state(const DecodeArgs& a, int b) {
+  SeqState st;
+  const bool act = !a.active || a.active[b];
+  st.t = a.steps_in[b];
+  const int cap = a.meta.cap[b];
+  st.app = act && a.k_new != nullptr && (!a.full_causal || st.t < cap);
+  const int t_after = st.app ? st.t + 1 : st.t;
+  st.L = act ? a.meta.prefix_len[b] + min(t_after, cap) : 0;
+  return st;
 }
 
-// s_cum[0..B] = exclusive prefix sums of items per sequence, s_len[b] = live rows of b.
-__device__ void build_work_table(const DecodeArgs& a, int* s_cum, int* s_len) {
-  __shared__ int s_wave_tot[kWaves];
-  __shared__ int s_carry;
+// Work table in LDS: s_len[b] = live rows, s_new[b] = cache row of this launch's new k/v (or -1),
+// s_cum[b] = sum over b' < b of H * L_b' (int64). Block 0 also publishes the plan for the merge
+// kernel and advances the step counters.
+__device__ void build_work_table(const DecodeArgs& a, int* s_len, int* s_new, int64_t* s_cum) {
+  __shared__ int64_t s_wave_tot[kWaves];
+  __shared__ int64_t s_carry;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   if (tid == 0) {
     s_carry = 0;
     s_cum[0] = 0;
   }
+  __syncthreads();
   for (int base = 0; base < a.batch; base += kThreads) {
     const int b = base + tid;
-    int items = 0;
+    int64_t rows = 0;
     if (b < a.batch) {
-      const int L = live_rows(a, b);
-      s_len[b] = L;
-      items = a.heads * ((L + a.chunk - 1) / a.chunk);
+      const SeqState st = seq_state(a, b);
+      s_len[b] = st.L;
+      rows = (int64_t)a.heads * st.L;
+      int rnew = -1;
+      const int m = a.meta.prefix_len[b];
+      if (st.app) rnew = a.full_causal ? m + st.t : m + st.t % a.meta.cap[b];
+      s_new[b] = rnew;
+      if (blockIdx.x == 0) {
+        if (a.steps_out) a.steps_out[b] = st.app ? st.t + 1 : st.t;
+        if (a.k_new && a.full_causal && (!a.active || a.active[b]) && st.t >= a.meta.cap[b])
+          *a.meta.err = 1;
+      }
     }
-    int x = items;
+    int64_t x = rows;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
-      const int y = __shfl_up(x, off);
+      const int64_t y = __shfl_up(x, off);
       if (lane >= off) x += y;
     }
     if (lane == kWave - 1) s_wave_tot[wave] = x;
     __syncthreads();
-    int prefix = s_carry;
+    int64_t prefix = s_carry;
     for (int w = 0; w < wave; ++w) prefix += s_wave_tot[w];
     if (b < a.batch) s_cum[b + 1] = prefix + x;
     __syncthreads();
@@ -73,29 +113,32 @@ __device__ void build_work_table(const DecodeArgs& a, int* s_cum, int* s_len) {
   __syncthreads();
 }
 
+__device__ __forceinline__ int64_t piece_rows(const DecodeArgs& a, int64_t total) {
+  const int64_t g = gridDim.x;
+  return max((int64_t)a.min_rows, (total + g - 1) / g);
+}
+
 template <typename KV>
-__device__ __forceinline__ float partial_dot(const uint4& q, const uint4& k);
+__device__ __forceinline__ float partial_dot(const u32x4& q, const u32x4& k);
 
 template <>
-__device__ __forceinline__ float partial_dot<uint16_t>(const uint4& q, const uint4& k) {
+__device__ __forceinline__ float partial_dot<uint16_t>(const u32x4& q, const u32x4& k) {
   float s = 0.f;
-  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.x),
-                                      __builtin_bit_cast(bf16x2_t, k.x), s, false);
-  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.y),
-                                      __builtin_bit_cast(bf16x2_t, k.y), s, false);
-  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.z),
-                                      __builtin_bit_cast(bf16x2_t, k.z), s, false);
-  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w),
-                                      __builtin_bit_cast(bf16x2_t, k.w), s, false);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // copy each element out first: a bit_cast of the element lvalue q[i] reads element 0
+    const uint32_t qi = q[i], ki = k[i];
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qi),
+                                        __builtin_bit_cast(bf16x2_t, ki), s, false);
+  }
   return s;
 }
 
 template <>
-__device__ __forceinline__ float partial_dot<float>(const uint4& q, const uint4& k) {
-  float s = __uint_as_float(q.x) * __uint_as_float(k.x);
-  s = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), s);
-  s = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), s);
-  s = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), s);
+__device__ __forceinline__ float partial_dot<float>(const u32x4& q, const u32x4& k) {
+  float s = __uint_as_float(q[0]) * __uint_as_float(k[0]);
+#pragma unroll
+  for (int i = 1; i < 4; ++i) s = fmaf(__uint_as_float(q[i]), __uint_as_float(k[i]), s);
   return s;
 }
 
@@ -107,61 +150,77 @@ template <>
 __device__ __forceinline__ float group_sum<float>(float x) { return lane32_sum(x); }
 
 template <typename KV>
-__device__ __forceinline__ void unpack_v(const uint4& v, float* f);
+__device__ __forceinline__ void unpack_v(const u32x4& v, float* f);
 template <>
-__device__ __forceinline__ void unpack_v<uint16_t>(const uint4& v, float* f) {
-  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
-  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
-  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
-  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+__device__ __forceinline__ void unpack_v<uint16_t>(const u32x4& v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_lo(v[i]);
+    f[2 * i + 1] = bf16_hi(v[i]);
+  }
 }
 template <>
-__device__ __forceinline__ void unpack_v<float>(const uint4& v, float* f) {
-  f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
-  f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+__device__ __forceinline__ void unpack_v<float>(const u32x4& v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
 }
 
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Stream rows [r0, r1) of range (b, h); finish with the group merge through LDS, then either the
+// output (the range is not split) or a partial in workspace slot `slot`.
 template <typename KV, typename OUT, int U>
-__device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int h, int c, int L,
-                                            int nch, float* s_m, float* s_l, float* s_acc) {
+__device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int h, int r0, int r1,
+                                             int rnew, bool direct, int64_t slot, float* s_m,
+                                             float* s_l, float* s_acc) {
   constexpr int VEC = Lanes<KV>::VEC, GL = Lanes<KV>::GL, G = kWave / GL, NG = kWaves * G;
+  constexpr int STEP = kWaves * G * U;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int g = lane / GL, li = lane % GL;
   const int H = a.heads;
   const int64_t R = a.meta.rows[b];
-  const KV* seq = reinterpret_cast<const KV*>(a.storage) + a.meta.seq_off[b];
-  const KV* Kp = seq + (int64_t)h * R * kHeadDim + li * VEC;
-  const KV* Vp = seq + (int64_t)(H + h) * R * kHeadDim + li * VEC;
-  const int r0 = c * a.chunk;
-  const int r1 = min(r0 + a.chunk, L);
-  const uint4 qv = *reinterpret_cast<const uint4*>(reinterpret_cast<const KV*>(a.q) +
-                                                   ((int64_t)b * H + h) * kHeadDim + li * VEC);
+  KV* seq = reinterpret_cast<KV*>(a.storage) + a.meta.seq_off[b];
+  KV* Kp = seq + (int64_t)h * R * kHeadDim + li * VEC;
+  KV* Vp = seq + (int64_t)(H + h) * R * kHeadDim + li * VEC;
+  const int64_t bh = (int64_t)b * H + h;
+  const u32x4 qv = ld16(reinterpret_cast<const KV*>(a.q) + bh * kHeadDim + li * VEC);
+  const KV* kin = a.k_new ? reinterpret_cast<const KV*>(a.k_new) + bh * kHeadDim + li * VEC : nullptr;
+  const KV* vin = a.v_new ? reinterpret_cast<const KV*>(a.v_new) + bh * kHeadDim + li * VEC : nullptr;
+
   float m_run = kNegBig, l_run = 0.f;
   float acc[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
 
-  for (int rb = r0 + wave * (G * U); rb < r1; rb += kWaves * G * U) {
-    uint4 kr[U], vr[U];
-    int row[U];
+  u32x4 kc[U], vc[U];
+  int rb = r0 + wave * (G * U);
+  auto load = [&](int base, u32x4* kr, u32x4* vr) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      row[u] = rb + u * G + g;
-      const int rr = min(row[u], r1 - 1);
-      kr[u] = *reinterpret_cast<const uint4*>(Kp + (int64_t)rr * kHeadDim);
+      const int row = base + u * G + g;
+      const int rr = min(row, r1 - 1);
+      const bool fresh = rr == rnew;
+      kr[u] = ld16(fresh ? kin : Kp + (int64_t)rr * kHeadDim);
+      vr[u] = ld16(fresh ? vin : Vp + (int64_t)rr * kHeadDim);
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int rr = min(row[u], r1 - 1);
-      vr[u] = *reinterpret_cast<const uint4*>(Vp + (int64_t)rr * kHeadDim);
-    }
+  };
+  if (rb < r1) load(rb, kc, vc);
+  for (; rb < r1; rb += STEP) {
+    u32x4 kn[U], vn[U];
+    const bool more = rb + STEP < r1;
+    if (RSWA_DECODE_PREFETCH && more) load(rb + STEP, kn, vn);
     float s[U];
     float mx = -INFINITY;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float d = group_sum<KV>(partial_dot<KV>(qv, kr[u]));
-      s[u] = row[u] < r1 ? d * a.scale_log2 : -INFINITY;
+      const int row = rb + u * G + g;
+      const float d = group_sum<KV>(partial_dot<KV>(qv, kc[u]));
+      s[u] = row < r1 ? d * a.scale_log2 : -INFINITY;
       mx = fmaxf(mx, s[u]);
+      if (row == rnew && row < r1) {  // the new row: store it into its slot
+        *reinterpret_cast<u32x4*>(Kp + (int64_t)row * kHeadDim) = kc[u];
+        *reinterpret_cast<u32x4*>(Vp + (int64_t)row * kHeadDim) = vc[u];
+      }
     }
     const float m_new = fmaxf(m_run, mx);
     const float alpha = fast_exp2(m_run - m_new);
@@ -173,11 +232,19 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int h, i
       const float p = fast_exp2(s[u] - m_new);
       l_run += p;
       float vf[VEC];
-      unpack_v<KV>(vr[u], vf);
+      unpack_v<KV>(vc[u], vf);
 #pragma unroll
       for (int i = 0; i < VEC; ++i) acc[i] = fmaf(p, vf[i], acc[i]);
     }
     m_run = m_new;
+    if (more) {
+      if (!RSWA_DECODE_PREFETCH) load(rb + STEP, kn, vn);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        kc[u] = kn[u];
+        vc[u] = vn[u];
+      }
+    }
   }
 
   const int gid = wave * G + g;
@@ -199,11 +266,9 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int h, i
       lsum = fmaf(s_l[k], w, lsum);
       num = fmaf(s_acc[k * kHeadDim + tid], w, num);
     }
-    const int64_t bh = (int64_t)b * H + h;
-    if (nch == 1) {
+    if (direct) {
       store_out(reinterpret_cast<OUT*>(a.out) + bh * kHeadDim + tid, num / lsum);
     } else {
-      const int64_t slot = bh * a.smax + c;
       a.ws_acc[slot * kHeadDim + tid] = num;
       if (tid == 0) a.ws_ml[slot] = make_float2(M, lsum);
     }
@@ -213,55 +278,88 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int h, i
 
 template <typename KV, typename OUT, int U>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
-  extern __shared__ int s_dyn[];
+  extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
   __shared__ float s_m[kMaxGroups], s_l[kMaxGroups];
   __shared__ float s_acc[kMaxGroups * kHeadDim];
-  int* s_cum = s_dyn;
-  int* s_len = s_dyn + a.batch + 1;
-  build_work_table(a, s_cum, s_len);
-  const int total = s_cum[a.batch];
-  for (int w = blockIdx.x; w < total; w += gridDim.x) {
-    int lo = 0, hi = a.batch - 1;
+  int64_t* s_cum = reinterpret_cast<int64_t*>(s_dyn);
+  int* s_len = reinterpret_cast<int*>(s_cum + a.batch + 1);
+  int* s_new = s_len + a.batch;
+  build_work_table(a, s_len, s_new, s_cum);
+  const int H = a.heads;
+  const int64_t total = s_cum[a.batch];
+
+  if (a.aligned) {
+    const int s = blockIdx.x;
+    const int b = s / H, h = s - (s / H) * H;
+    if (b >= a.batch || s_len[b] == 0) return;
+    decode_range<KV, OUT, U>(a, b, h, 0, s_len[b], s_new[b], true, 0, s_m, s_l, s_acc);
+    return;
+  }
+
+  const int64_t W = piece_rows(a, total);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    for (int b = 0; b <= a.batch; ++b) a.ws_cum[b] = s_cum[b];
+    a.ws_cum[a.batch + 1] = W;
+  }
+  int64_t pos = (int64_t)blockIdx.x * W;
+  const int64_t end = min(pos + W, total);
+  while (pos < end) {
+    int lo = 0, hi = a.batch - 1;  // last b with s_cum[b] <= pos
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (s_cum[mid] <= w) lo = mid; else hi = mid - 1;
+      if (s_cum[mid] <= pos) lo = mid; else hi = mid - 1;
     }
     const int b = lo;
     const int L = s_len[b];
-    const int nch = (L + a.chunk - 1) / a.chunk;
-    const int local = w - s_cum[b];
-    const int h = local / nch;
-    const int c = local - h * nch;
-    decode_item<KV, OUT, U>(a, b, h, c, L, nch, s_m, s_l, s_acc);
+    const int64_t off = pos - s_cum[b];
+    const int h = (int)(off / L);
+    const int r0 = (int)(off - (int64_t)h * L);
+    const int r1 = (int)min((int64_t)L, r0 + (end - pos));
+    const int s = b * H + h;
+    const int64_t A = s_cum[b] + (int64_t)h * L;
+    const bool direct = A / W == (A + L - 1) / W;
+    decode_range<KV, OUT, U>(a, b, h, r0, r1, s_new[b], direct, (int64_t)blockIdx.x + s, s_m,
+                             s_l, s_acc);
+    pos += r1 - r0;
   }
 }
 
+// One workgroup per (b, h): combine the partials of a range split over several pieces.
 template <typename OUT>
 __global__ __launch_bounds__(kHeadDim) void decode_merge_kernel(DecodeArgs a) {
-  const int bh = blockIdx.x;
-  const int b = bh / a.heads;
-  const int L = live_rows(a, b);
-  const int nch = (L + a.chunk - 1) / a.chunk;
-  if (nch <= 1) return;  // inactive (L = 0) or written directly by decode_kernel
+  const int s = blockIdx.x;
+  const int b = s / a.heads, h = s - (s / a.heads) * a.heads;
+  const int64_t c0 = a.ws_cum[b], c1 = a.ws_cum[b + 1];
+  const int64_t L = (c1 - c0) / a.heads;
+  if (L == 0) return;
+  const int64_t W = a.ws_cum[a.batch + 1];
+  const int64_t A = c0 + h * L;
+  const int64_t f = A / W, l = (A + L - 1) / W;
+  if (f == l) return;  // written directly by the decode kernel
   const int tid = threadIdx.x;
-  const int64_t slot0 = (int64_t)bh * a.smax;
   float M = kNegBig;
-  for (int s = 0; s < nch; ++s) M = fmaxf(M, a.ws_ml[slot0 + s].x);
+  for (int64_t i = f; i <= l; ++i) M = fmaxf(M, a.ws_ml[i + s].x);
   float lsum = 0.f, num = 0.f;
-  for (int s = 0; s < nch; ++s) {
-    const float2 ml = a.ws_ml[slot0 + s];
+  for (int64_t i = f; i <= l; ++i) {
+    const float2 ml = a.ws_ml[i + s];
     const float w = fast_exp2(ml.x - M);
     lsum = fmaf(ml.y, w, lsum);
-    num = fmaf(a.ws_acc[(slot0 + s) * kHeadDim + tid], w, num);
+    num = fmaf(a.ws_acc[(i + s) * kHeadDim + tid], w, num);
   }
-  store_out(reinterpret_cast<OUT*>(a.out) + (int64_t)bh * kHeadDim + tid, num / lsum);
+  store_out(reinterpret_cast<OUT*>(a.out) + (int64_t)s * kHeadDim + tid, num / lsum);
 }
+
+#ifndef RSWA_DECODE_ROWS
+#define RSWA_DECODE_ROWS 2
+#endif
+constexpr int kRowsPerLane = RSWA_DECODE_ROWS;  // U: rows each lane group loads per tile
 
 template <typename KV, typename OUT>
 hipError_t launch_typed(const DecodeArgs& a, int grid, bool need_merge, hipStream_t s) {
-  const size_t smem = (size_t)(2 * a.batch + 1) * sizeof(int);
+  const size_t smem = decode_lds_bytes(a.batch);
   if (grid > 0) {
-    hipLaunchKernelGGL((decode_kernel<KV, OUT, 4>), dim3(grid), dim3(kThreads), smem, s, a);
+    hipLaunchKernelGGL((decode_kernel<KV, OUT, kRowsPerLane>), dim3(grid), dim3(kThreads), smem,
+                       s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -271,6 +369,15 @@ hipError_t launch_typed(const DecodeArgs& a, int grid, bool need_merge, hipStrea
     return hipGetLastError();
   }
   return hipSuccess;
+}
+
+template <typename KV, typename OUT>
+int occupancy_typed(int batch) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<KV, OUT, kRowsPerLane>,
+                                                   kThreads, decode_lds_bytes(batch)) != hipSuccess)
+    return 1;
+  return n > 0 ? n : 1;
 }
 
 }  // namespace
@@ -283,6 +390,17 @@ hipError_t launch_decode(const DecodeArgs& a, int kv_f32, int out_f32, int grid_
   }
   return out_f32 ? launch_typed<uint16_t, float>(a, grid_blocks, need_merge, s)
                  : launch_typed<uint16_t, uint16_t>(a, grid_blocks, need_merge, s);
+}
+
+size_t decode_lds_bytes(int batch) {
+  return (size_t)(batch + 1) * sizeof(int64_t) + (size_t)2 * batch * sizeof(int);
+}
+
+int decode_blocks_per_cu(int kv_f32, int out_f32, int batch) {
+  if (kv_f32)
+    return out_f32 ? occupancy_typed<float, float>(batch) : occupancy_typed<float, uint16_t>(batch);
+  return out_f32 ? occupancy_typed<uint16_t, float>(batch)
+                 : occupancy_typed<uint16_t, uint16_t>(batch);
 }
 
 }  // namespace rswa

@@ -6,20 +6,23 @@
 
 namespace rswa {
 
-// Per-sequence metadata of a decode cache, resident on the device (written once at creation,
-// except `steps`, which the append kernel advances).
+// Per-sequence metadata of a decode cache, resident on the device (written once at creation).
 struct CacheMeta {
   const int64_t* seq_off;    // [B] element offset of sequence b's K block
   const int32_t* rows;       // [B] R_b = m_b + cap_b rows per head
   const int32_t* prefix_len; // [B] m_b
   const int32_t* cap;        // [B] n_b (R-SWA ring slots) or max_steps_b (full causal)
-  int32_t* steps;            // [B] t_b, outputs appended so far
   int32_t* err;              // [1] sticky flag: a full-causal append found no free row
 };
 
+// Step counters t_b are double-buffered: a launch that appends reads steps_in and writes
+// steps_out (= steps_in + appended), so no workgroup of that launch races on them; the host
+// swaps the two buffers after every appending launch.
 struct AppendArgs {
   void* storage;
   CacheMeta meta;
+  const int32_t* steps_in;
+  int32_t* steps_out;
   const void* k_new;        // [B][H][D]
   const void* v_new;        // [B][H][D]
   const uint8_t* active;    // [B] or nullptr
@@ -28,18 +31,23 @@ struct AppendArgs {
 };
 
 struct DecodeArgs {
-  const void* storage;
+  void* storage;
   CacheMeta meta;
+  const int32_t* steps_in;
+  int32_t* steps_out;       // nullptr unless this launch appends
+  const void* k_new;        // [B][H][D] or nullptr: decode only, no append
+  const void* v_new;
   const void* q;            // [B][H][D]
   void* out;                // [B][H][D]
   const uint8_t* active;    // [B] or nullptr
-  float* ws_acc;            // [B*H*smax][D] split partial numerators
-  float2* ws_ml;            // [B*H*smax] split partial (max, sum), log2 domain
+  float* ws_acc;            // [slots][D] partial numerators
+  float2* ws_ml;            // [slots] partial (max, sum), log2 domain
+  int64_t* ws_cum;          // [B + 2]: row prefix sums (stream-K plan) and rows per workgroup
   int32_t batch;
   int32_t heads;
-  int32_t chunk;            // rows per split (multiple of 64)
-  int32_t smax;             // split slots per (b, h) in the workspace
   int32_t full_causal;
+  int32_t aligned;          // 1: one workgroup per (b, h) key range; 0: balanced stream-K ranges
+  int32_t min_rows;         // stream-K: fewest rows a workgroup takes
   float scale_log2;         // softmax scale * log2(e)
 };
 
@@ -74,5 +82,8 @@ hipError_t launch_append(const AppendArgs& a, int batch, int kv_f32, hipStream_t
 hipError_t launch_decode(const DecodeArgs& a, int kv_f32, int out_f32, int grid_blocks,
                          bool need_merge, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int out_f32, hipStream_t s);
+// Resident 256-thread decode workgroups per CU (occupancy of the decode kernel for a batch of B).
+int decode_blocks_per_cu(int kv_f32, int out_f32, int batch);
+size_t decode_lds_bytes(int batch);
 
 }  // namespace rswa

@@ -63,24 +63,31 @@ rswa_status make_plan(const rswa_cache_desc* d, Plan* p, std::string* why) {
   return RSWA_OK;
 }
 
-int64_t decode_items(const std::vector<int64_t>& live_rows, int32_t heads, int32_t chunk) {
-  int64_t n = 0;
-  for (int64_t L : live_rows) n += (int64_t)heads * ((L + chunk - 1) / chunk);
-  return n;
-}
-
-int32_t auto_chunk(const Plan& p, int32_t heads, int64_t min_items) {
-  std::vector<int64_t> full(p.rows.begin(), p.rows.end());
-  for (int32_t c : {512, 256, 128}) {
-    if (decode_items(full, heads, c) >= min_items) return c;
+DecodePlan plan_decode(const std::vector<int64_t>& live_rows, int32_t heads, int64_t resident,
+                       int64_t grid_max, int32_t min_rows, int32_t grid_user, bool masked) {
+  DecodePlan p;
+  const int64_t nseg = (int64_t)live_rows.size() * heads;
+  int64_t total = 0;
+  bool uniform = !masked;
+  for (size_t b = 0; b < live_rows.size(); ++b) {
+    total += (int64_t)heads * live_rows[b];
+    if (live_rows[b] != live_rows[0]) uniform = false;
   }
-  return 64;
-}
-
-int32_t split_slots(const Plan& p, int32_t chunk) {
-  int32_t s = 1;
-  for (int32_t R : p.rows) s = std::max<int32_t>(s, (R + chunk - 1) / chunk);
-  return s;
+  if (total == 0) return p;
+  resident = std::max<int64_t>(1, std::min(resident, grid_max));
+  const bool user = min_rows > 0 || grid_user > 0;
+  if (!user && uniform && nseg <= resident && 2 * nseg >= resident) {
+    p.aligned = true;
+    p.grid = nseg;
+    p.rows_per_piece = live_rows[0];
+    return p;
+  }
+  const int64_t g_req = grid_user > 0 ? std::min<int64_t>(grid_user, grid_max) : resident;
+  const int64_t w_min = min_rows > 0 ? min_rows : 64;
+  p.rows_per_piece = std::max<int64_t>(w_min, (total + g_req - 1) / g_req);
+  p.grid = (total + p.rows_per_piece - 1) / p.rows_per_piece;
+  p.need_merge = true;
+  return p;
 }
 
 }  // namespace rswa

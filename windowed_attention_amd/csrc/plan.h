@@ -11,7 +11,7 @@
 
 namespace rswa {
 
-constexpr int32_t kMaxBatch = 4096;
+constexpr int32_t kMaxBatch = 2048;
 constexpr int32_t kMaxHeads = 1024;
 constexpr int32_t kPlanHeadDim = 128;
 
@@ -30,14 +30,19 @@ struct Plan {
 // Validates `d` and fills `p`. On failure returns the status and a reason in `why`.
 rswa_status make_plan(const rswa_cache_desc* d, Plan* p, std::string* why);
 
-// Decode items (one per (b, h, chunk)) for the given live row counts.
-int64_t decode_items(const std::vector<int64_t>& live_rows, int32_t heads, int32_t chunk);
+// How one decode launch splits its work (see decode.hip).
+struct DecodePlan {
+  bool aligned = false;  // one workgroup per (b, h) key range
+  int64_t grid = 0;      // workgroups to launch (0: nothing to do)
+  int64_t rows_per_piece = 0;  // stream-K piece size for the host's row counts
+  bool need_merge = false;
+};
 
-// Automatic chunk size: the largest of 512, 256, 128, 64 rows that still yields at least
-// `min_items` items at the cache's full size, else 64.
-int32_t auto_chunk(const Plan& p, int32_t heads, int64_t min_items);
-
-// Split slots per (b, h) that the workspace must hold for chunks of `chunk` rows.
-int32_t split_slots(const Plan& p, int32_t chunk);
+// live_rows: per-sequence live rows (upper bounds) after the launch's append; resident: decode
+// workgroups that fit the GPU at once; grid_max: workgroups the workspace holds; min_rows /
+// grid_user: user settings (0 = automatic); masked: an active mask is in use (row counts are then
+// only upper bounds, so the aligned layout, which needs equal ranges, is not chosen).
+DecodePlan plan_decode(const std::vector<int64_t>& live_rows, int32_t heads, int64_t resident,
+                       int64_t grid_max, int32_t min_rows, int32_t grid_user, bool masked);
 
 }  // namespace rswa

@@ -50,22 +50,27 @@ struct rswa_cache {
   bool owns_storage = false;
   void* meta_dev = nullptr;
   rswa::CacheMeta meta{};
+  int32_t* steps_dev[2] = {nullptr, nullptr};  // double-buffered step counters
+  int cur = 0;                                 // steps_dev[cur] holds the current t_b
   int64_t* prefix_row0_dev = nullptr;
   void* ws_dev = nullptr;
   float* ws_acc = nullptr;
   float2* ws_ml = nullptr;
-  int32_t smax = 0;      // workspace split slots per (b, h) (sized for 64-row chunks)
-  int32_t chunk = 0;     // current decode chunk rows
-  int32_t grid_user = 0; // 0 = automatic
+  int64_t* ws_cum = nullptr;
+  int32_t grid_max = 0;  // stream-K workgroups the workspace is sized for
+  int32_t min_rows = 0;  // user setting (0 = automatic)
+  int32_t grid_user = 0; // user setting (0 = automatic)
   int device = 0;
   int num_cus = 0;
+  int blocks_per_cu = 0; // resident decode workgroups per CU
 
   bool full() const { return mode == RSWA_MODE_FULL_CAUSAL; }
-  // Upper bound of each sequence's live rows, from the host count of append calls.
-  std::vector<int64_t> live_upper() const {
+  // Upper bound of each sequence's live rows after `extra` more appends, from the host count of
+  // append calls (exact when no active mask has been used).
+  std::vector<int64_t> live_upper(int extra) const {
     std::vector<int64_t> L(B);
     for (int b = 0; b < B; ++b)
-      L[b] = plan.prefix[b] + std::min<int64_t>(plan.cap[b], calls[b]);
+      L[b] = plan.prefix[b] + std::min<int64_t>(plan.cap[b], calls[b] + extra);
     return L;
   }
 };
@@ -188,7 +193,8 @@ rswa_status rswa_cache_create(const rswa_cache_desc* desc, const void* prefix_k_
     const size_t off_pref = align_up(off_rows + 4 * (size_t)B, 256);
     const size_t off_cap = align_up(off_pref + 4 * (size_t)B, 256);
     const size_t off_steps = align_up(off_cap + 4 * (size_t)B, 256);
-    const size_t off_err = align_up(off_steps + 4 * (size_t)B, 256);
+    const size_t off_steps2 = align_up(off_steps + 4 * (size_t)B, 256);
+    const size_t off_err = align_up(off_steps2 + 4 * (size_t)B, 256);
     const size_t meta_bytes = off_err + 256;
     std::vector<unsigned char> host(meta_bytes, 0);
     std::memcpy(host.data() + off_i64, p.seq_off.data(), 8 * (size_t)B);
@@ -213,23 +219,28 @@ rswa_status rswa_cache_create(const rswa_cache_desc* desc, const void* prefix_k_
     c->meta.rows = reinterpret_cast<const int32_t*>(mb + off_rows);
     c->meta.prefix_len = reinterpret_cast<const int32_t*>(mb + off_pref);
     c->meta.cap = reinterpret_cast<const int32_t*>(mb + off_cap);
-    c->meta.steps = reinterpret_cast<int32_t*>(mb + off_steps);
+    c->steps_dev[0] = reinterpret_cast<int32_t*>(mb + off_steps);
+    c->steps_dev[1] = reinterpret_cast<int32_t*>(mb + off_steps2);
     c->meta.err = reinterpret_cast<int32_t*>(mb + off_err);
 
-    // decode split policy and workspace (sized for the smallest chunk so that
-    // rswa_cache_set_decode_split never reallocates)
-    c->chunk = rswa::auto_chunk(p, c->H, 4LL * c->num_cus);
-    c->smax = rswa::split_slots(p, 64);
-    const size_t ws_slots = (size_t)B * c->H * c->smax;
+    // decode plan: resident workgroups per CU, and a workspace sized for the largest stream-K
+    // grid (partial slot = workgroup index + (b, h) index, see decode.hip)
+    c->blocks_per_cu = rswa::decode_blocks_per_cu(c->kv_dtype == RSWA_F32, 1, B);
+    c->grid_max = std::max(1, c->num_cus * std::max(c->blocks_per_cu, 8));
+    const size_t ws_slots = (size_t)c->grid_max + (size_t)B * c->H;
     const size_t ws_acc_bytes = align_up(ws_slots * rswa::kPlanHeadDim * sizeof(float), 256);
-    e = hipMalloc(&c->ws_dev, ws_acc_bytes + ws_slots * sizeof(float2));
+    const size_t ws_ml_bytes = align_up(ws_slots * sizeof(float2), 256);
+    const size_t ws_cum_bytes = align_up(((size_t)B + 2) * sizeof(int64_t), 256);
+    e = hipMalloc(&c->ws_dev, ws_acc_bytes + ws_ml_bytes + ws_cum_bytes);
     if (e != hipSuccess) {
       c->ws_dev = nullptr;
       release(c);
       return fail(RSWA_E_OOM, std::string("hipMalloc(workspace): ") + hipGetErrorString(e));
     }
-    c->ws_acc = reinterpret_cast<float*>(c->ws_dev);
-    c->ws_ml = reinterpret_cast<float2*>(reinterpret_cast<unsigned char*>(c->ws_dev) + ws_acc_bytes);
+    unsigned char* wb = reinterpret_cast<unsigned char*>(c->ws_dev);
+    c->ws_acc = reinterpret_cast<float*>(wb);
+    c->ws_ml = reinterpret_cast<float2*>(wb + ws_acc_bytes);
+    c->ws_cum = reinterpret_cast<int64_t*>(wb + ws_acc_bytes + ws_ml_bytes);
 
     // prefix rows
     rswa::PrefixCopyArgs pa{};
@@ -276,6 +287,8 @@ rswa_status rswa_append_kv(rswa_cache* c, const void* k_dev, const void* v_dev,
     rswa::AppendArgs a{};
     a.storage = c->storage;
     a.meta = c->meta;
+    a.steps_in = c->steps_dev[c->cur];
+    a.steps_out = c->steps_dev[c->cur ^ 1];
     a.k_new = k_dev;
     a.v_new = v_dev;
     a.active = active_dev;
@@ -284,6 +297,7 @@ rswa_status rswa_append_kv(rswa_cache* c, const void* k_dev, const void* v_dev,
     const hipError_t e = rswa::launch_append(a, c->B, c->kv_dtype == RSWA_F32,
                                              reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "append launch");
+    c->cur ^= 1;
     for (int b = 0; b < c->B; ++b) c->calls[b] += 1;
     return RSWA_OK;
   } catch (...) {
@@ -291,16 +305,26 @@ rswa_status rswa_append_kv(rswa_cache* c, const void* k_dev, const void* v_dev,
   }
 }
 
-rswa_status rswa_decode_attn(rswa_cache* c, const void* q_dev, void* out_dev, int32_t out_dtype,
-                             float softmax_scale, const uint8_t* active_dev, void* stream) {
+namespace {
+
+// Shared body of rswa_decode_attn (k_dev == NULL) and rswa_decode_step (append fused in).
+rswa_status decode_launch(rswa_cache* c, const void* q_dev, const void* k_dev, const void* v_dev,
+                          void* out_dev, int32_t out_dtype, float softmax_scale,
+                          const uint8_t* active_dev, void* stream, const char* what) {
   if (!c) return fail(RSWA_E_INVALID, "cache is NULL");
   if (!q_dev || !out_dev) return fail(RSWA_E_INVALID, "q_dev / out_dev is NULL");
   if (out_dtype != RSWA_BF16 && out_dtype != RSWA_F32)
     return fail(RSWA_E_INVALID, "out_dtype must be RSWA_BF16 or RSWA_F32");
   if (!(softmax_scale <= 0.f) && !std::isfinite(softmax_scale))
     return fail(RSWA_E_INVALID, "softmax_scale must be finite");
+  const bool append = k_dev != nullptr;
   try {
-    const std::vector<int64_t> L = c->live_upper();
+    if (append && c->full() && !active_dev) {
+      for (int b = 0; b < c->B; ++b)
+        if (c->calls[b] >= c->plan.cap[b])
+          return fail(RSWA_E_CAPACITY, "full-causal append past max_steps");
+    }
+    const std::vector<int64_t> L = c->live_upper(append ? 1 : 0);
     if (!active_dev) {
       for (int b = 0; b < c->B; ++b)
         if (L[b] == 0)
@@ -311,30 +335,56 @@ rswa_status rswa_decode_attn(rswa_cache* c, const void* q_dev, void* out_dev, in
     rswa::DecodeArgs a{};
     a.storage = c->storage;
     a.meta = c->meta;
+    a.steps_in = c->steps_dev[c->cur];
+    a.steps_out = append ? c->steps_dev[c->cur ^ 1] : nullptr;
+    a.k_new = k_dev;
+    a.v_new = v_dev;
     a.q = q_dev;
     a.out = out_dev;
     a.active = active_dev;
     a.ws_acc = c->ws_acc;
     a.ws_ml = c->ws_ml;
+    a.ws_cum = c->ws_cum;
     a.batch = c->B;
     a.heads = c->H;
-    a.chunk = c->chunk;
-    a.smax = c->smax;
     a.full_causal = c->full();
+    a.min_rows = c->min_rows > 0 ? c->min_rows : 64;
     a.scale_log2 = scale * 1.4426950408889634f;
-    const int64_t items = rswa::decode_items(L, c->H, c->chunk);
-    int64_t grid = c->grid_user > 0 ? c->grid_user : 8LL * c->num_cus;
-    grid = std::min<int64_t>(grid, items);
-    bool need_merge = false;
-    for (int b = 0; b < c->B; ++b) need_merge = need_merge || L[b] > c->chunk;
+
+    const int64_t resident = (int64_t)c->num_cus * c->blocks_per_cu;
+    const rswa::DecodePlan plan = rswa::plan_decode(L, c->H, resident, c->grid_max, c->min_rows,
+                                                    c->grid_user, active_dev != nullptr);
+    a.aligned = plan.aligned ? 1 : 0;
+    const int64_t grid = plan.grid;
+    const bool need_merge = plan.need_merge;
     const hipError_t e = rswa::launch_decode(a, c->kv_dtype == RSWA_F32, out_dtype == RSWA_F32,
                                              (int)grid, need_merge,
                                              reinterpret_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    if (e != hipSuccess) return hip_fail(e, what);
+    if (append) {
+      c->cur ^= 1;
+      for (int b = 0; b < c->B; ++b) c->calls[b] += 1;
+    }
     return RSWA_OK;
   } catch (...) {
-    return fail(RSWA_E_INTERNAL, "exception in rswa_decode_attn");
+    return fail(RSWA_E_INTERNAL, std::string("exception in ") + what);
   }
+}
+
+}  // namespace
+
+rswa_status rswa_decode_attn(rswa_cache* c, const void* q_dev, void* out_dev, int32_t out_dtype,
+                             float softmax_scale, const uint8_t* active_dev, void* stream) {
+  return decode_launch(c, q_dev, nullptr, nullptr, out_dev, out_dtype, softmax_scale, active_dev,
+                       stream, "rswa_decode_attn");
+}
+
+rswa_status rswa_decode_step(rswa_cache* c, const void* q_dev, const void* k_dev,
+                             const void* v_dev, void* out_dev, int32_t out_dtype,
+                             float softmax_scale, const uint8_t* active_dev, void* stream) {
+  if (c && (!k_dev || !v_dev)) return fail(RSWA_E_INVALID, "k_dev / v_dev is NULL");
+  return decode_launch(c, q_dev, k_dev, v_dev, out_dev, out_dtype, softmax_scale, active_dev,
+                       stream, "rswa_decode_step");
 }
 
 rswa_status rswa_cache_steps(rswa_cache* c, int32_t* steps_host, void* stream) {
@@ -343,7 +393,7 @@ rswa_status rswa_cache_steps(rswa_cache* c, int32_t* steps_host, void* stream) {
     DeviceGuard g(c->device);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     int32_t err = 0;
-    hipError_t e = hipMemcpyAsync(steps_host, c->meta.steps, 4 * (size_t)c->B,
+    hipError_t e = hipMemcpyAsync(steps_host, c->steps_dev[c->cur], 4 * (size_t)c->B,
                                   hipMemcpyDeviceToHost, st);
     if (e == hipSuccess)
       e = hipMemcpyAsync(&err, c->meta.err, 4, hipMemcpyDeviceToHost, st);
@@ -369,10 +419,9 @@ rswa_status rswa_cache_info(const rswa_cache* c, void** storage_dev, int64_t* se
 
 rswa_status rswa_cache_set_decode_split(rswa_cache* c, int32_t chunk_rows, int32_t grid_blocks) {
   if (!c) return fail(RSWA_E_INVALID, "cache is NULL");
-  if (chunk_rows < 0 || chunk_rows % 64 != 0)
-    return fail(RSWA_E_INVALID, "chunk_rows must be 0 or a positive multiple of 64");
+  if (chunk_rows < 0) return fail(RSWA_E_INVALID, "chunk_rows must be >= 0");
   if (grid_blocks < 0) return fail(RSWA_E_INVALID, "grid_blocks must be >= 0");
-  c->chunk = chunk_rows ? chunk_rows : rswa::auto_chunk(c->plan, c->H, 4LL * c->num_cus);
+  c->min_rows = chunk_rows;
   c->grid_user = grid_blocks;
   return RSWA_OK;
 }
