@@ -65,6 +65,14 @@ def parse():
     ap.add_argument("--no-kernel-events", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="time rswa_append_kv + rswa_decode_attn instead of rswa_decode_step")
+    ap.add_argument("--no-growth", action="store_true",
+                    help="skip the multi-page R-SWA vs full-causal growth curve")
+    ap.add_argument("--no-ragged", action="store_true", help="skip the ragged-batch decode")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also time a plain 1 GiB device copy (bandwidth reference, PMC scale)")
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL"),
+                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs into "
+                         "profiles/<KERNEL>_traffic.json and exit (no GPU use)")
     ap.add_argument("--prefill-runs", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     return ap.parse_args()
@@ -227,6 +235,59 @@ def traffic_from_profile(kind: str, src_hash: str, per_launch_units: float | Non
     return rec.get("bytes_per_launch")
 
 
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
+    """A plain device-to-device copy of `nbytes` (torch's copy kernel): the practical bandwidth
+    reference, and the known-size dispatch the PMC byte counters are scaled by."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ms = float(np.median(ts))
+    return dict(bytes_moved=2 * nbytes, ms=ms, gbs=2 * nbytes / (ms * 1e-3) / 1e9)
+
+
+def pmc_summary(fetch_csv: str, write_csv: str, kernel: str):
+    """Scale the decode/prefill kernels' FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the same
+    counters read for the 1 GiB calibration copy (1 GiB read, 1 GiB written)."""
+    import csv
+    def per_kernel(path, counter):
+        rows = list(csv.DictReader(open(path)))
+        out = {}
+        for r in rows:
+            if r.get("Counter_Name", counter) != counter:
+                continue
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return out
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    copy_k = [k for k in fetch if "copy" in k.lower() and "elementwise" in k.lower()] or \
+             [k for k in fetch if "copy" in k.lower()]
+    big = lambda vals: max(vals)
+    cf = (1 << 30) / (big(fetch[copy_k[0]]) * 1024.0)
+    cw = (1 << 30) / (big(write[copy_k[0]]) * 1024.0)
+    names = [k for k in fetch if kernel in k]
+    rec = dict(kernel_names=names, copy_kernel=copy_k[0], fetch_scale=cf, write_scale=cw)
+    for k in names:
+        f = np.array(fetch[k]) * 1024.0 * cf
+        w = np.array(write.get(k, [0.0])) * 1024.0 * cw
+        rec[k] = dict(dispatches=int(f.size), fetch_bytes_median=float(np.median(f)),
+                      write_bytes_median=float(np.median(w)))
+    main = max(names, key=lambda k: rec[k]["fetch_bytes_median"])
+    rec["bytes_per_launch"] = rec[main]["fetch_bytes_median"] + rec[main]["write_bytes_median"]
+    src = DECODE_SOURCES if kernel.startswith("decode") else PREFILL_SOURCES
+    rec["source_hash"] = source_hash(src)
+    return rec
+
+
 # ------------------------------------------------------------------------------------------------
 # prefill
 # ------------------------------------------------------------------------------------------------
@@ -321,8 +382,63 @@ def _cpu_baseline(wl, seconds, O, to_f64):
 
 
 # ------------------------------------------------------------------------------------------------
+def growth_curve(args):
+    """Multi-page decode (B=8, m=5155, n=128, T=20000): per-step latency vs t for R-SWA (flat) and
+    for the full-causal mode (cache m + t, growing), same inputs and launch path."""
+    import types
+    wl = decode_workload("multipage")
+    out = {}
+    for mode in ("rswa", "full"):
+        a = types.SimpleNamespace(chunk=args.chunk, grid=args.grid, unfused=args.unfused)
+        r = run_decode(a, wl, mode == "full", wl.T - 1, 1, False)
+        lat = r["lat"]
+        ts = np.array([t for t, _ in lat], dtype=np.float64)
+        us = np.array([u for _, u in lat])
+        byt = np.array([decode_bytes(wl, int(t), mode == "full", 2) + append_bytes(wl, int(t))
+                        for t in ts])
+        keep = np.linspace(0, len(lat) - 1, 40).round().astype(int)
+        rec = dict(us_per_step_vs_t=[[int(ts[i]), round(float(us[i]), 2)] for i in keep],
+                   gbs_vs_t=[[int(ts[i]), round(float(byt[i] / (us[i] * 1e-6) / 1e9))]
+                             for i in keep],
+                   median_us=float(np.median(us)), tok_s=r["tokens"] / (r["elapsed_ms"] * 1e-3))
+        if mode == "full":
+            rows = 5155 + ts
+            slope = np.polyfit(rows, us, 1)[0] * 1000.0
+            rec["slope_us_per_1k_rows"] = float(slope)
+        else:
+            rec["flatness"] = flatness(lat, 128, int(wl.T))
+        jumps = [[int(ts[i]), round(float(us[i] / us[i - 1]), 3)] for i in range(1, len(us))
+                 if abs(us[i] / us[i - 1] - 1) > 0.10]
+        rec["jumps_over_10pct"] = jumps
+        out[mode] = rec
+        log(f"[bench] growth {mode}: median {rec['median_us']:.1f} us/step")
+    out["workload"] = wl.name
+    return out
+
+
+def ragged_decode(args, steps=3000):
+    import types
+    wl = decode_workload("ragged")
+    a = types.SimpleNamespace(chunk=args.chunk, grid=args.grid, unfused=args.unfused)
+    warm = 300
+    r = run_decode(a, wl, False, steps, warm, True)
+    kms = float(r["kern_ms"].mean())
+    ach = float(r["launch_bytes"].mean()) / (kms * 1e-3) / 1e9
+    return dict(workload=wl.name, steps=steps, timed_t=[warm + 1, warm + steps],
+                tok_s=r["tokens"] / (r["elapsed_ms"] * 1e-3),
+                us_per_step=r["elapsed_ms"] * 1e3 / steps, launch_gbs=ach,
+                frac=ach / PEAK_HBM_GBS)
+
+
 def main():
     args = parse()
+    if args.pmc_summary:
+        rec = pmc_summary(*args.pmc_summary)
+        path = os.path.join(ROOT, "profiles", f"{args.pmc_summary[2]}_traffic.json")
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has no "
               f"multi-GPU path", file=sys.stderr)
@@ -365,6 +481,15 @@ def main():
                                    bytes_per_launch=float(r["launch_bytes"].mean()))
         res["latency_vs_t"] = [[int(t), round(u, 3)] for t, u in r["lat"]]
         res["flatness"] = flatness(r["lat"], int(wl.window[0]), warmup + steps)
+    if args.copy_calibration:
+        res["copy_calibration"] = copy_calibration()
+        log(f"[bench] 1 GiB copy: {res['copy_calibration']['gbs']:.0f} GB/s")
+    if not args.no_decode and not args.no_growth:
+        res["growth"] = growth_curve(args)
+    if not args.no_decode and not args.no_ragged:
+        res["ragged"] = ragged_decode(args)
+        log(f"[bench] ragged: {res['ragged']['us_per_step']:.1f} us/step, "
+            f"{res['ragged']['launch_gbs']:.0f} GB/s")
     if not args.no_prefill:
         p = run_prefill(args)
         if p is not None:

@@ -324,9 +324,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   }
 }
 
-// One workgroup per (b, h): combine the partials of a range split over several pieces.
+// One workgroup per (b, h): combine the partials of a range split over several pieces. The
+// partials' (max, sum) pairs are loaded in parallel and reduced in LDS, then every thread (one
+// output dim) accumulates the weighted numerators with independent loads, so the merge costs a
+// few memory round trips rather than one per partial.
+constexpr int kMergeChunk = kHeadDim;
+
 template <typename OUT>
 __global__ __launch_bounds__(kHeadDim) void decode_merge_kernel(DecodeArgs a) {
+  __shared__ float s_w[kMergeChunk], s_l[kMergeChunk];
+  __shared__ float s_red[kHeadDim / kWave];
   const int s = blockIdx.x;
   const int b = s / a.heads, h = s - (s / a.heads) * a.heads;
   const int64_t c0 = a.ws_cum[b], c1 = a.ws_cum[b + 1];
@@ -336,15 +343,43 @@ __global__ __launch_bounds__(kHeadDim) void decode_merge_kernel(DecodeArgs a) {
   const int64_t A = c0 + h * L;
   const int64_t f = A / W, l = (A + L - 1) / W;
   if (f == l) return;  // written directly by the decode kernel
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int np = (int)(l - f + 1);
+  const float2* ml = a.ws_ml + f + s;
+  const float* acc = a.ws_acc + (f + s) * kHeadDim + tid;
+
+  // global max of the partial maxima
   float M = kNegBig;
-  for (int64_t i = f; i <= l; ++i) M = fmaxf(M, a.ws_ml[i + s].x);
+  for (int i = tid; i < np; i += kHeadDim) M = fmaxf(M, ml[i].x);
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) s_red[wave] = M;
+  __syncthreads();
+  M = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kHeadDim / kWave; ++w) M = fmaxf(M, s_red[w]);
+
   float lsum = 0.f, num = 0.f;
-  for (int64_t i = f; i <= l; ++i) {
-    const float2 ml = a.ws_ml[i + s];
-    const float w = fast_exp2(ml.x - M);
-    lsum = fmaf(ml.y, w, lsum);
-    num = fmaf(a.ws_acc[(i + s) * kHeadDim + tid], w, num);
+  for (int c = 0; c < np; c += kMergeChunk) {
+    const int n = min(kMergeChunk, np - c);
+    __syncthreads();
+    if (tid < n) {
+      const float2 p = ml[c + tid];
+      s_w[tid] = fast_exp2(p.x - M);
+      s_l[tid] = p.y;
+    }
+    __syncthreads();
+    int i = 0;
+    for (; i + 4 <= n; i += 4) {
+      const float x0 = acc[(int64_t)(c + i) * kHeadDim], x1 = acc[(int64_t)(c + i + 1) * kHeadDim];
+      const float x2 = acc[(int64_t)(c + i + 2) * kHeadDim], x3 = acc[(int64_t)(c + i + 3) * kHeadDim];
+      num = fmaf(x0, s_w[i], num);
+      num = fmaf(x1, s_w[i + 1], num);
+      num = fmaf(x2, s_w[i + 2], num);
+      num = fmaf(x3, s_w[i + 3], num);
+    }
+    for (; i < n; ++i) num = fmaf(acc[(int64_t)(c + i) * kHeadDim], s_w[i], num);
+    for (int j = 0; j < n; ++j) lsum = fmaf(s_l[j], s_w[j], lsum);
   }
   store_out(reinterpret_cast<OUT*>(a.out) + (int64_t)s * kHeadDim + tid, num / lsum);
 }
