@@ -167,6 +167,12 @@ rswa_status rswa_cache_info(const rswa_cache* cache, void** storage_dev,
  * depend on these only through float32 summation order. Host only. */
 rswa_status rswa_cache_set_decode_split(rswa_cache* cache, int32_t chunk_rows, int32_t grid_blocks);
 
+/* What the next decode launch on this cache does when no active mask is given (appending = 1 for
+ * rswa_decode_step, 0 for rswa_decode_attn): the workgroups of the decode kernel and the number of
+ * kernel launches (1, or 2 when split ranges need the merge kernel). Host only. */
+rswa_status rswa_cache_decode_plan(const rswa_cache* cache, int32_t appending,
+                                   int32_t* grid_blocks, int32_t* launches);
+
 /* Release the cache: synchronizes the stream it was created on, frees library-owned memory.
  * NULL is accepted. Caller-owned storage is left as is. */
 rswa_status rswa_cache_destroy(rswa_cache* cache);

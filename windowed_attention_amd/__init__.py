@@ -25,7 +25,8 @@ STATUS = {0: "RSWA_OK", -1: "RSWA_E_INVALID", -2: "RSWA_E_UNSUPPORTED", -3: "RSW
 # Every symbol include/rswa.h declares.
 EXPORTS = ("rswa_cache_plan", "rswa_cache_bytes", "rswa_cache_create", "rswa_append_kv",
            "rswa_decode_attn", "rswa_decode_step", "rswa_prefill_attn", "rswa_cache_steps", "rswa_cache_info",
-           "rswa_cache_set_decode_split", "rswa_cache_destroy", "rswa_status_str",
+           "rswa_cache_set_decode_split", "rswa_cache_decode_plan", "rswa_cache_destroy",
+           "rswa_status_str",
            "rswa_last_error")
 
 
@@ -65,6 +66,7 @@ def _load():
         "rswa_cache_steps": (i32, [vp, pi32, vp]),
         "rswa_cache_info": (i32, [vp, ctypes.POINTER(vp), pi64, pi32]),
         "rswa_cache_set_decode_split": (i32, [vp, i32, i32]),
+        "rswa_cache_decode_plan": (i32, [vp, i32, pi32, pi32]),
         "rswa_cache_destroy": (i32, [vp]),
         "rswa_status_str": (ctypes.c_char_p, [i32]),
         "rswa_last_error": (ctypes.c_char_p, []),
@@ -244,6 +246,13 @@ class RswaCache:
     def set_decode_split(self, chunk_rows: int = 0, grid_blocks: int = 0) -> None:
         _check(_lib.rswa_cache_set_decode_split(self.handle, chunk_rows, grid_blocks),
                "rswa_cache_set_decode_split")
+
+    def decode_plan(self, appending: bool = True):
+        """(workgroups, launches) of the next decode launch without an active mask."""
+        g, n = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(_lib.rswa_cache_decode_plan(self.handle, int(appending), ctypes.byref(g),
+                                           ctypes.byref(n)), "rswa_cache_decode_plan")
+        return g.value, n.value
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None:

@@ -167,6 +167,63 @@ __device__ __forceinline__ void unpack_v<float>(const u32x4& v, float* f) {
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Combine the np partials of range s stored at workspace slots f + s .. f + s + np - 1 and write
+// the output; threads [0, 128) hold one output dim each. (Merging inside the decode kernel, by the
+// last workgroup to publish a partial, needs agent-scope release/acquire fences in every
+// workgroup; measured on MI355X that costs about 5x the whole step, so the merge is its own
+// launch.)
+// The (max, sum) pairs are loaded in parallel and reduced in LDS; the numerators are accumulated
+// with independent loads, so the merge costs a few memory round trips, not one per partial.
+constexpr int kMergeChunk = kHeadDim;
+
+template <typename OUT>
+__device__ __forceinline__ void merge_range(const DecodeArgs& a, int64_t s, int64_t f, int np,
+                                            float* s_w, float* s_l, float* s_red) {
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  constexpr int NW = kHeadDim / kWave;
+  const bool worker = tid < kHeadDim;
+  const float2* ml = a.ws_ml + f + s;
+  const float* acc = a.ws_acc + (f + s) * kHeadDim + (worker ? tid : 0);
+  float M = kNegBig;
+  if (worker)
+    for (int i = tid; i < np; i += kHeadDim) M = fmaxf(M, ml[i].x);
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0 && wave < NW) s_red[wave] = M;
+  __syncthreads();
+  M = s_red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, s_red[w]);
+  float lsum = 0.f, num = 0.f;
+  for (int c = 0; c < np; c += kMergeChunk) {
+    const int n = min(kMergeChunk, np - c);
+    __syncthreads();
+    if (tid < n) {
+      const float2 p = ml[c + tid];
+      s_w[tid] = fast_exp2(p.x - M);
+      s_l[tid] = p.y;
+    }
+    __syncthreads();
+    if (worker) {
+      int i = 0;
+      for (; i + 4 <= n; i += 4) {
+        const float x0 = acc[(int64_t)(c + i) * kHeadDim];
+        const float x1 = acc[(int64_t)(c + i + 1) * kHeadDim];
+        const float x2 = acc[(int64_t)(c + i + 2) * kHeadDim];
+        const float x3 = acc[(int64_t)(c + i + 3) * kHeadDim];
+        num = fmaf(x0, s_w[i], num);
+        num = fmaf(x1, s_w[i + 1], num);
+        num = fmaf(x2, s_w[i + 2], num);
+        num = fmaf(x3, s_w[i + 3], num);
+      }
+      for (; i < n; ++i) num = fmaf(acc[(int64_t)(c + i) * kHeadDim], s_w[i], num);
+      for (int j = 0; j < n; ++j) lsum = fmaf(s_l[j], s_w[j], lsum);
+    }
+  }
+  if (worker) store_out(reinterpret_cast<OUT*>(a.out) + s * kHeadDim + tid, num / lsum);
+  __syncthreads();
+}
+
 // Stream rows [r0, r1) of range (b, h); finish with the group merge through LDS, then either the
 // output (the range is not split) or a partial in workspace slot `slot`.
 template <typename KV, typename OUT, int U>
@@ -324,12 +381,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   }
 }
 
-// One workgroup per (b, h): combine the partials of a range split over several pieces. The
-// partials' (max, sum) pairs are loaded in parallel and reduced in LDS, then every thread (one
-// output dim) accumulates the weighted numerators with independent loads, so the merge costs a
-// few memory round trips rather than one per partial.
-constexpr int kMergeChunk = kHeadDim;
-
+// One workgroup per (b, h): combine the partials of a range split over several pieces.
 template <typename OUT>
 __global__ __launch_bounds__(kHeadDim) void decode_merge_kernel(DecodeArgs a) {
   __shared__ float s_w[kMergeChunk], s_l[kMergeChunk];
@@ -343,45 +395,7 @@ __global__ __launch_bounds__(kHeadDim) void decode_merge_kernel(DecodeArgs a) {
   const int64_t A = c0 + h * L;
   const int64_t f = A / W, l = (A + L - 1) / W;
   if (f == l) return;  // written directly by the decode kernel
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int np = (int)(l - f + 1);
-  const float2* ml = a.ws_ml + f + s;
-  const float* acc = a.ws_acc + (f + s) * kHeadDim + tid;
-
-  // global max of the partial maxima
-  float M = kNegBig;
-  for (int i = tid; i < np; i += kHeadDim) M = fmaxf(M, ml[i].x);
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (lane == 0) s_red[wave] = M;
-  __syncthreads();
-  M = s_red[0];
-#pragma unroll
-  for (int w = 1; w < kHeadDim / kWave; ++w) M = fmaxf(M, s_red[w]);
-
-  float lsum = 0.f, num = 0.f;
-  for (int c = 0; c < np; c += kMergeChunk) {
-    const int n = min(kMergeChunk, np - c);
-    __syncthreads();
-    if (tid < n) {
-      const float2 p = ml[c + tid];
-      s_w[tid] = fast_exp2(p.x - M);
-      s_l[tid] = p.y;
-    }
-    __syncthreads();
-    int i = 0;
-    for (; i + 4 <= n; i += 4) {
-      const float x0 = acc[(int64_t)(c + i) * kHeadDim], x1 = acc[(int64_t)(c + i + 1) * kHeadDim];
-      const float x2 = acc[(int64_t)(c + i + 2) * kHeadDim], x3 = acc[(int64_t)(c + i + 3) * kHeadDim];
-      num = fmaf(x0, s_w[i], num);
-      num = fmaf(x1, s_w[i + 1], num);
-      num = fmaf(x2, s_w[i + 2], num);
-      num = fmaf(x3, s_w[i + 3], num);
-    }
-    for (; i < n; ++i) num = fmaf(acc[(int64_t)(c + i) * kHeadDim], s_w[i], num);
-    for (int j = 0; j < n; ++j) lsum = fmaf(s_l[j], s_w[j], lsum);
-  }
-  store_out(reinterpret_cast<OUT*>(a.out) + (int64_t)s * kHeadDim + tid, num / lsum);
+  merge_range<OUT>(a, s, f, (int)(l - f + 1), s_w, s_l, s_red);
 }
 
 #ifndef RSWA_DECODE_ROWS

@@ -33,12 +33,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: s
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
-constexpr int BM = 128;                 // queries per workgroup
 constexpr int BN = 64;                  // keys per tile
 constexpr int KSTR = kHeadDim + 8;      // K tile row stride (bf16): 272 B rows
 constexpr int VSTR = BN + 4;            // V^T tile row stride (bf16): 136 B rows
 constexpr int K_TILE = BN * KSTR;       // bf16 elements per K buffer
 constexpr int V_TILE = kHeadDim * VSTR; // bf16 elements per V^T buffer
+constexpr float kLazy = 8.f;            // log2-domain slack before the reference max moves
 
 __device__ __forceinline__ floatx16 mfma32(const u32x4& a, const u32x4& b, const floatx16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -109,17 +109,32 @@ __device__ __forceinline__ void store_out4<uint16_t>(uint16_t* p, float a, float
                                        f32_to_bf16_bits(c) | (f32_to_bf16_bits(d) << 16)};
 }
 
-template <typename OUT>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
+// max over the two lane halves holding the same query (lanes l and l ^ 32)
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// QB query blocks of 32 per wave: every K / V^T fragment read from LDS feeds QB MFMAs.
+template <typename OUT, int QB>
+__global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_kernel(PrefillArgs a) {
+  constexpr int BMQ = 4 * 32 * QB;  // queries per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t sK[2 * K_TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sVt[2 * V_TILE];
 
   const int s = blockIdx.z, h = blockIdx.y;
   const int cu0 = a.cu_seqlens[s];
   const int S = a.cu_seqlens[s + 1] - cu0;
-  const int q0 = blockIdx.x * BM;
+  const int q0 = blockIdx.x * BMQ;
   if (q0 >= S) return;
-  const int q1 = min(q0 + BM, S);
+  const int q1 = min(q0 + BMQ, S);
   const int m = a.prefix_len[s];
   const int n = a.window[s];
   const bool pc = a.prefix_causal != 0;
@@ -131,13 +146,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const uint16_t* kbase = a.k + ((int64_t)cu0 * a.heads + h) * kHeadDim;
   const uint16_t* vbase = a.v + ((int64_t)cu0 * a.heads + h) * kHeadDim;
 
-  // this lane's query and its Q^T operand (8 d-steps of 16)
-  const int p = q0 + wave * 32 + lq;
-  const int pq = min(p, S - 1);
-  u32x4 qf[8];
+  // this lane's queries (one per query block) and their Q^T operands (8 d-steps of 16)
+  int p[QB];
+  u32x4 qf[QB][8];
 #pragma unroll
-  for (int st = 0; st < 8; ++st)
-    qf[st] = *reinterpret_cast<const u32x4*>(qbase + pq * rs + st * 16 + half * 8);
+  for (int qb = 0; qb < QB; ++qb) {
+    p[qb] = q0 + (wave * QB + qb) * 32 + lq;
+    const int pq = min(p[qb], S - 1);
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+      qf[qb][st] = *reinterpret_cast<const u32x4*>(qbase + pq * rs + st * 16 + half * 8);
+  }
 
   // key tiles: the prefix segment, then the output window segment
   TileSched ts;
@@ -151,13 +170,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   }
   ts.ntiles = ts.n_pre + n_win;
 
+  // visible key interval of each query in each segment: prefix [0, pre_hi], window [win_lo, p]
+  int pre_hi[QB], win_lo[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    pre_hi[qb] = (pc && p[qb] < m) ? min(p[qb], m - 1) : m - 1;
+    win_lo[qb] = p[qb] >= m ? max(m, p[qb] - n + 1) : p[qb] + 1;  // empty for prefix queries
+  }
+
   const float c = a.scale_log2;
-  float m_run = kNegBig, l_run = 0.f;
-  floatx16 o[4];
+  float m_run[QB], l_run[QB];
+  floatx16 o[QB][4];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = kNegBig;
+    l_run[qb] = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.f;
+  }
 
   u32x4 rk[4], rv[4];
   load_tile(rk, rv, kbase, vbase, rs, ts.start(0), S - 1);
@@ -173,70 +205,86 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     const int k0 = ts.start(j);
     const bool is_pre = j < ts.n_pre;
 
-    // S^T = K Q^T for two 32-key blocks
-    floatx16 sacc[2];
+    // S^T = K Q^T for two 32-key blocks; each K fragment feeds QB MFMAs
+    floatx16 sacc[QB][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         const u32x4 ka =
             *reinterpret_cast<const u32x4*>(sk + (kb * 32 + lq) * KSTR + st * 16 + half * 8);
-        sacc[kb] = mfma32(ka, qf[st], sacc[kb]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = mfma32(ka, qf[qb][st], sacc[qb][kb]);
       }
-    }
 
-    // element mask where the tile is not fully visible
+    // element mask (branch-free interval test) where the tile is not fully visible
     const bool need_mask = is_pre ? (k0 + BN > m || (pc && q0 < m && k0 + BN - 1 > q0)) : true;
     if (need_mask) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int qb = 0; qb < QB; ++qb) {
+        const int lo = is_pre ? 0 : win_lo[qb];
+        const int hi = is_pre ? pre_hi[qb] : p[qb];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int k = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          bool vis;
-          if (is_pre)
-            vis = k < m && (!pc || p >= m || k <= p);
-          else
-            vis = k >= m && k <= p && p - k < n;
-          if (!vis) sacc[kb][r] = -INFINITY;
-        }
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int k = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            sacc[qb][kb][r] = (k >= lo && k <= hi) ? sacc[qb][kb][r] : -INFINITY;
+          }
+      }
     }
 
-    // online softmax (log2 domain), one query per lane, keys split across lane and lane ^ 32
-    float mx = -INFINITY;
+    // online softmax (log2 domain), one query per lane, keys split across lane and lane ^ 32.
+    // The reference max moves only when a tile exceeds it by more than kLazy (P <= 2^kLazy,
+    // harmless in float32 and bf16); O / l is exact for any reference max, so the accumulator
+    // rescale is rare.
+    u32x4 pb[QB][2][2];
+    bool rescale = false;
+    float alpha[QB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * c);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f;
-    u32x4 pb[2][2];
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float pr[16];
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][kb][r]);
+      mx = xhalf_max(mx) * c;
+      const bool up = mx > m_run[qb] + kLazy;
+      const float m_new = up ? mx : m_run[qb];
+      alpha[qb] = up ? fast_exp2(m_run[qb] - m_new) : 1.f;
+      rescale = rescale || (up && m_run[qb] != kNegBig);  // O is still zero before any key
+      m_run[qb] = m_new;
+      float psum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        pr[r] = fast_exp2(fmaf(sacc[kb][r], c, -m_new));
-        psum += pr[r];
+      for (int kb = 0; kb < 2; ++kb) {
+        float pr[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          pr[r] = fast_exp2(fmaf(sacc[qb][kb][r], c, -m_new));
+          psum += pr[r];
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+          pb[qb][kb][st] = u32x4{pack_bf16(pr[8 * st + 0], pr[8 * st + 1]),
+                                 pack_bf16(pr[8 * st + 2], pr[8 * st + 3]),
+                                 pack_bf16(pr[8 * st + 4], pr[8 * st + 5]),
+                                 pack_bf16(pr[8 * st + 6], pr[8 * st + 7])};
       }
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-        pb[kb][st] = u32x4{pack_bf16(pr[8 * st + 0], pr[8 * st + 1]),
-                           pack_bf16(pr[8 * st + 2], pr[8 * st + 3]),
-                           pack_bf16(pr[8 * st + 4], pr[8 * st + 5]),
-                           pack_bf16(pr[8 * st + 6], pr[8 * st + 7])};
+      l_run[qb] = fmaf(l_run[qb], alpha[qb], psum);
     }
-    l_run = fmaf(l_run, alpha, psum);
-    if (__any(alpha != 1.f)) {
+    if (__any(rescale)) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha[qb];
     }
 
     // O^T += V^T P^T: for d block db, key step (kb, st) the A operand holds
@@ -250,7 +298,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         for (int st = 0; st < 2; ++st) {
           const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kb * 32 + 16 * st);
           const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + kb * 32 + 16 * st + 8);
-          o[db] = mfma32(u32x4{lo.x, lo.y, hi.x, hi.y}, pb[kb][st], o[db]);
+          const u32x4 va = u32x4{lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(va, pb[qb][kb][st], o[qb][db]);
         }
     }
 
@@ -259,27 +309,36 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   }
 
   // normalise and write: lane holds query p, dims db*32 + 8 g + 4 half + (0..3)
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (p < q1) {
-    const float inv = 1.f / l_tot;
-    OUT* orow = reinterpret_cast<OUT*>(a.out) + ((int64_t)(cu0 + p) * a.heads + h) * kHeadDim;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = xhalf_sum(l_run[qb]);
+    if (p[qb] < q1) {
+      const float inv = 1.f / l_tot;
+      OUT* orow = reinterpret_cast<OUT*>(a.out) + ((int64_t)(cu0 + p[qb]) * a.heads + h) * kHeadDim;
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        store_out4<OUT>(orow + db * 32 + 8 * g + 4 * half, o[db][4 * g] * inv,
-                        o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          store_out4<OUT>(orow + db * 32 + 8 * g + 4 * half, o[qb][db][4 * g] * inv,
+                          o[qb][db][4 * g + 1] * inv, o[qb][db][4 * g + 2] * inv,
+                          o[qb][db][4 * g + 3] * inv);
+    }
   }
 }
 
 }  // namespace
 
+#ifndef RSWA_PREFILL_QB
+#define RSWA_PREFILL_QB 1  // 32-query blocks per wave
+#endif
+
 hipError_t launch_prefill(const PrefillArgs& a, int out_f32, hipStream_t s) {
-  const dim3 grid((a.max_seqlen + BM - 1) / BM, a.heads, a.nseq);
+  constexpr int QB = RSWA_PREFILL_QB;
+  const dim3 grid((a.max_seqlen + 128 * QB - 1) / (128 * QB), a.heads, a.nseq);
   if (out_f32)
-    hipLaunchKernelGGL(prefill_kernel<float>, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((prefill_kernel<float, QB>), grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(prefill_kernel<uint16_t>, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((prefill_kernel<uint16_t, QB>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

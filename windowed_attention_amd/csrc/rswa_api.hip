@@ -231,7 +231,8 @@ rswa_status rswa_cache_create(const rswa_cache_desc* desc, const void* prefix_k_
     const size_t ws_acc_bytes = align_up(ws_slots * rswa::kPlanHeadDim * sizeof(float), 256);
     const size_t ws_ml_bytes = align_up(ws_slots * sizeof(float2), 256);
     const size_t ws_cum_bytes = align_up(((size_t)B + 2) * sizeof(int64_t), 256);
-    e = hipMalloc(&c->ws_dev, ws_acc_bytes + ws_ml_bytes + ws_cum_bytes);
+    const size_t ws_bytes = ws_acc_bytes + ws_ml_bytes + ws_cum_bytes;
+    e = hipMalloc(&c->ws_dev, ws_bytes);
     if (e != hipSuccess) {
       c->ws_dev = nullptr;
       release(c);
@@ -415,6 +416,22 @@ rswa_status rswa_cache_info(const rswa_cache* c, void** storage_dev, int64_t* se
     if (rows_host) rows_host[b] = c->plan.rows[b];
   }
   return RSWA_OK;
+}
+
+rswa_status rswa_cache_decode_plan(const rswa_cache* c, int32_t appending, int32_t* grid_blocks,
+                                  int32_t* launches) {
+  if (!c) return fail(RSWA_E_INVALID, "cache is NULL");
+  try {
+    const std::vector<int64_t> L = c->live_upper(appending ? 1 : 0);
+    const rswa::DecodePlan plan =
+        rswa::plan_decode(L, c->H, (int64_t)c->num_cus * c->blocks_per_cu, c->grid_max,
+                          c->min_rows, c->grid_user, false);
+    if (grid_blocks) *grid_blocks = (int32_t)plan.grid;
+    if (launches) *launches = (plan.grid > 0 ? 1 : 0) + (plan.need_merge ? 1 : 0);
+    return RSWA_OK;
+  } catch (...) {
+    return fail(RSWA_E_INTERNAL, "exception in rswa_cache_decode_plan");
+  }
 }
 
 rswa_status rswa_cache_set_decode_split(rswa_cache* c, int32_t chunk_rows, int32_t grid_blocks) {
