@@ -16,8 +16,9 @@
 // max/sum over keys is in-lane plus one exchange with lane ^ 32. The output is also formed
 // transposed, O^T = V^T P^T: the score accumulator registers, rounded to bf16, are already the B
 // operand of the second MFMA (the key order inside a 16-key step is a permutation that the V^T
-// operand follows), so P never leaves registers. K tiles (64 keys x 128) and V^T tiles
-// (128 x 64 keys) are double-buffered in LDS; Q stays in registers for the whole key loop.
+// operand follows), so P never leaves registers. K and V tiles (64 keys x 128) are
+// double-buffered in LDS, both row-major; the V^T operand comes out of gfx950's transposing LDS
+// read, so V needs no transpose on the way in. Q stays in registers for the whole key loop.
 // Softmax runs in the log2 domain in float32; P is rounded to bf16 for the PV product and the
 // output is normalised by the float32 row sum.
 #include "device.h"
@@ -34,10 +35,16 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int BN = 64;                  // keys per tile
-constexpr int KSTR = kHeadDim + 8;      // K tile row stride (bf16): 272 B rows
-constexpr int VSTR = BN + 4;            // V^T tile row stride (bf16): 136 B rows
-constexpr int K_TILE = BN * KSTR;       // bf16 elements per K buffer
-constexpr int V_TILE = kHeadDim * VSTR; // bf16 elements per V^T buffer
+#ifndef RSWA_PF_KPAD
+#define RSWA_PF_KPAD 8   // bf16 pad per K row (bank spread of the 16-byte operand reads)
+#endif
+#ifndef RSWA_PF_VPAD
+#define RSWA_PF_VPAD 32  // bf16 pad per V row (bank spread of the transposing reads)
+#endif
+constexpr int KSTR = kHeadDim + RSWA_PF_KPAD;  // K tile row stride (bf16)
+constexpr int VSTR = kHeadDim + RSWA_PF_VPAD;  // V tile row stride (bf16)
+constexpr int K_TILE = BN * KSTR;              // bf16 elements per K buffer
+constexpr int V_TILE = BN * VSTR;              // bf16 elements per V buffer
 constexpr float kLazy = 8.f;            // log2-domain slack before the reference max moves
 
 __device__ __forceinline__ floatx16 mfma32(const u32x4& a, const u32x4& b, const floatx16& c) {
@@ -74,27 +81,28 @@ __device__ __forceinline__ void load_tile(u32x4 (&rk)[4], u32x4 (&rv)[4], const 
   }
 }
 
-__device__ __forceinline__ uint32_t word(const u32x4& v, int w) {
-  return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
-}
-
+// Registers -> LDS: K and V tiles both row-major (key rows of 128 dims), 16-byte stores.
 __device__ __forceinline__ void store_tile(const u32x4 (&rk)[4], const u32x4 (&rv)[4], uint16_t* sk,
-                                           uint16_t* svt) {
+                                           uint16_t* sv) {
   const int t = threadIdx.x;
   const int c = t & 15, kg = t >> 4;
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < 4; ++u) {
     *reinterpret_cast<u32x4*>(sk + (kg * 4 + u) * KSTR + c * 8) = rk[u];
-  // transpose 4 keys x 8 dims -> 8 dims x 4 keys
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t x0 = word(rv[0], w), x1 = word(rv[1], w);
-    const uint32_t x2 = word(rv[2], w), x3 = word(rv[3], w);
-    const u32x2 lo = u32x2{(x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16)};
-    const u32x2 hi = u32x2{(x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u)};
-    *reinterpret_cast<u32x2*>(svt + (c * 8 + 2 * w) * VSTR + kg * 4) = lo;
-    *reinterpret_cast<u32x2*>(svt + (c * 8 + 2 * w + 1) * VSTR + kg * 4) = hi;
+    *reinterpret_cast<u32x4*>(sv + (kg * 4 + u) * VSTR + c * 8) = rv[u];
   }
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each group of 16 lanes, output lane i
+// gets element i % 4 of the 8-byte chunks that lanes 4j + i / 4 (j = 0..3) point at. With lane
+// 4j + q pointing at V[k0 + j][d0 + 4q .. +3], lane i receives V[k0 .. k0 + 3][d0 + i]: four
+// consecutive keys of its own dim, i.e. half of a V^T MFMA operand.
+__device__ __forceinline__ u32x2 ld_tr(const uint16_t* p) {
+  const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (v4i16_t __attribute__((address_space(3)))*)(p));
+  return __builtin_bit_cast(u32x2, r);
 }
 
 template <typename OUT>
@@ -127,7 +135,7 @@ template <typename OUT, int QB>
 __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_kernel(PrefillArgs a) {
   constexpr int BMQ = 4 * 32 * QB;  // queries per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t sK[2 * K_TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[2 * V_TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2 * V_TILE];
 
   const int s = blockIdx.z, h = blockIdx.y;
   const int cu0 = a.cu_seqlens[s];
@@ -193,7 +201,7 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_kernel(Pref
 
   u32x4 rk[4], rv[4];
   load_tile(rk, rv, kbase, vbase, rs, ts.start(0), S - 1);
-  store_tile(rk, rv, sK, sVt);
+  store_tile(rk, rv, sK, sV);
   __syncthreads();
 
   for (int j = 0; j < ts.ntiles; ++j) {
@@ -201,7 +209,7 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_kernel(Pref
     const bool more = j + 1 < ts.ntiles;
     if (more) load_tile(rk, rv, kbase, vbase, rs, ts.start(j + 1), S - 1);
     const uint16_t* sk = sK + buf * K_TILE;
-    const uint16_t* svt = sVt + buf * V_TILE;
+    const uint16_t* sv = sV + buf * V_TILE;
     const int k0 = ts.start(j);
     const bool is_pre = j < ts.n_pre;
 
@@ -288,23 +296,27 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_kernel(Pref
     }
 
     // O^T += V^T P^T: for d block db, key step (kb, st) the A operand holds
-    // V[key = kb*32 + 16 st + 8 (e / 4) + 4 half + e % 4][d = db*32 + lq], e = 0..7
+    // V[key = kb*32 + 16 st + 8 (e / 4) + 4 half + e % 4][d = db*32 + lq], e = 0..7, fetched with
+    // two transposing reads: this lane points at V[key0 + j][d0 + 4 q], j = (lane % 16) / 4,
+    // q = lane % 4, where d0 = db*32 + 16 ((lane / 16) % 2) is its 16-lane group's first dim.
+    const uint16_t* vsrc = sv + (((lane & 15) >> 2) + 4 * half) * VSTR + 16 * ((lane >> 4) & 1) +
+                           4 * (lane & 3);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const uint16_t* vrow = svt + (db * 32 + lq) * VSTR + half * 4;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kb * 32 + 16 * st);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + kb * 32 + 16 * st + 8);
+          const uint16_t* pv = vsrc + (kb * 32 + 16 * st) * VSTR + db * 32;
+          const u32x2 lo = ld_tr(pv);
+          const u32x2 hi = ld_tr(pv + 8 * VSTR);
           const u32x4 va = u32x4{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(va, pb[qb][kb][st], o[qb][db]);
         }
     }
 
-    if (more) store_tile(rk, rv, sK + (buf ^ 1) * K_TILE, sVt + (buf ^ 1) * V_TILE);
+    if (more) store_tile(rk, rv, sK + (buf ^ 1) * K_TILE, sV + (buf ^ 1) * V_TILE);
     __syncthreads();
   }
 
