@@ -33,7 +33,12 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in VGPRs
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
+#ifndef RSWA_PF_WAVES
+#define RSWA_PF_WAVES 8  // waves per workgroup (each owns QB x 32 queries)
+#endif
+constexpr int kWavesPF = RSWA_PF_WAVES;
+constexpr int kThreads = 64 * kWavesPF;
+constexpr int kKeysPerThread = 64 * 16 / kThreads;  // a 64-key tile is 64 x 16 pieces of 16 B
 constexpr int BN = 64;                  // keys per tile
 #ifndef RSWA_PF_KPAD
 #define RSWA_PF_KPAD 8   // bf16 pad per K row (bank spread of the 16-byte operand reads)
@@ -67,29 +72,30 @@ struct TileSched {
   __device__ __forceinline__ int start(int j) const { return j < n_pre ? j * BN : ws + (j - n_pre) * BN; }
 };
 
-// Global -> registers: thread t loads 4 consecutive keys x 8 dims of K and of V.
-__device__ __forceinline__ void load_tile(u32x4 (&rk)[4], u32x4 (&rv)[4], const uint16_t* kbase,
-                                          const uint16_t* vbase, int64_t row_stride, int k0,
-                                          int kmax) {
+// Global -> registers: thread t loads kKeysPerThread consecutive keys x 8 dims of K and of V.
+__device__ __forceinline__ void load_tile(u32x4 (&rk)[kKeysPerThread], u32x4 (&rv)[kKeysPerThread],
+                                          const uint16_t* kbase, const uint16_t* vbase,
+                                          int64_t row_stride, int k0, int kmax) {
   const int t = threadIdx.x;
   const int c = t & 15, kg = t >> 4;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int key = min(k0 + kg * 4 + u, kmax);
+  for (int u = 0; u < kKeysPerThread; ++u) {
+    const int key = min(k0 + kg * kKeysPerThread + u, kmax);
     rk[u] = *reinterpret_cast<const u32x4*>(kbase + key * row_stride + c * 8);
     rv[u] = *reinterpret_cast<const u32x4*>(vbase + key * row_stride + c * 8);
   }
 }
 
 // Registers -> LDS: K and V tiles both row-major (key rows of 128 dims), 16-byte stores.
-__device__ __forceinline__ void store_tile(const u32x4 (&rk)[4], const u32x4 (&rv)[4], uint16_t* sk,
+__device__ __forceinline__ void store_tile(const u32x4 (&rk)[kKeysPerThread],
+                                           const u32x4 (&rv)[kKeysPerThread], uint16_t* sk,
                                            uint16_t* sv) {
   const int t = threadIdx.x;
   const int c = t & 15, kg = t >> 4;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    *reinterpret_cast<u32x4*>(sk + (kg * 4 + u) * KSTR + c * 8) = rk[u];
-    *reinterpret_cast<u32x4*>(sv + (kg * 4 + u) * VSTR + c * 8) = rv[u];
+  for (int u = 0; u < kKeysPerThread; ++u) {
+    *reinterpret_cast<u32x4*>(sk + (kg * kKeysPerThread + u) * KSTR + c * 8) = rk[u];
+    *reinterpret_cast<u32x4*>(sv + (kg * kKeysPerThread + u) * VSTR + c * 8) = rv[u];
   }
 }
 
@@ -132,8 +138,9 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 
 // QB query blocks of 32 per wave: every K / V^T fragment read from LDS feeds QB MFMAs.
 template <typename OUT, int QB>
-__global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_kernel(PrefillArgs a) {
-  constexpr int BMQ = 4 * 32 * QB;  // queries per workgroup
+__global__ __launch_bounds__(kThreads, (QB == 1 ? 8 : 4) / kWavesPF) void prefill_kernel(
+    PrefillArgs a) {
+  constexpr int BMQ = kWavesPF * 32 * QB;  // queries per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t sK[2 * K_TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2 * V_TILE];
 
@@ -199,15 +206,16 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_kernel(Pref
       for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.f;
   }
 
-  u32x4 rk[4], rv[4];
-  load_tile(rk, rv, kbase, vbase, rs, ts.start(0), S - 1);
-  store_tile(rk, rv, sK, sV);
+  // Global -> register loads run two tiles ahead (register sets A and B alternate), so a tile's
+  // loads have two tiles of compute to arrive; LDS holds two tiles (being read / being written).
+  u32x4 ka_[kKeysPerThread], va_[kKeysPerThread], kb_[kKeysPerThread], vb_[kKeysPerThread];
+  load_tile(ka_, va_, kbase, vbase, rs, ts.start(0), S - 1);
+  store_tile(ka_, va_, sK, sV);
+  if (ts.ntiles > 1) load_tile(ka_, va_, kbase, vbase, rs, ts.start(1), S - 1);
   __syncthreads();
 
-  for (int j = 0; j < ts.ntiles; ++j) {
-    const int buf = j & 1;
-    const bool more = j + 1 < ts.ntiles;
-    if (more) load_tile(rk, rv, kbase, vbase, rs, ts.start(j + 1), S - 1);
+  // one tile: S^T, mask, softmax and PV from LDS buffer `buf`
+  auto tile = [&](int j, int buf) {
     const uint16_t* sk = sK + buf * K_TILE;
     const uint16_t* sv = sV + buf * V_TILE;
     const int k0 = ts.start(j);
@@ -248,29 +256,30 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_kernel(Pref
       }
     }
 
-    // online softmax (log2 domain), one query per lane, keys split across lane and lane ^ 32.
-    // The reference max moves only when a tile exceeds it by more than kLazy (P <= 2^kLazy,
-    // harmless in float32 and bf16); O / l is exact for any reference max, so the accumulator
-    // rescale is rare.
-    u32x4 pb[QB][2][2];
-    bool rescale = false;
-    float alpha[QB];
+    // Online softmax (log2 domain), one query per lane, keys split across lane and lane ^ 32,
+    // then O^T += V^T P^T, one 32-key block at a time so that one block's softmax (vector ALU)
+    // can overlap the other block's MFMAs. The reference max moves only when a block exceeds it
+    // by more than kLazy (P <= 2^kLazy, harmless in float32 and bf16); O / l is exact for any
+    // reference max, so the accumulator rescale is rare.
+    const uint16_t* vsrc = sv + (((lane & 15) >> 2) + 4 * half) * VSTR + 16 * ((lane >> 4) & 1) +
+                           4 * (lane & 3);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
+    for (int kb = 0; kb < 2; ++kb) {
+      u32x4 pb[QB][2];
+      bool rescale = false;
+      float alpha[QB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][kb][r]);
-      mx = xhalf_max(mx) * c;
-      const bool up = mx > m_run[qb] + kLazy;
-      const float m_new = up ? mx : m_run[qb];
-      alpha[qb] = up ? fast_exp2(m_run[qb] - m_new) : 1.f;
-      rescale = rescale || (up && m_run[qb] != kNegBig);  // O is still zero before any key
-      m_run[qb] = m_new;
-      float psum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+        mx = xhalf_max(mx) * c;
+        const bool up = mx > m_run[qb] + kLazy;
+        const float m_new = up ? mx : m_run[qb];
+        alpha[qb] = up ? fast_exp2(m_run[qb] - m_new) : 1.f;
+        rescale = rescale || (up && m_run[qb] != kNegBig);  // O is still zero before any key
+        m_run[qb] = m_new;
+        float psum = 0.f;
         float pr[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -279,32 +288,27 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_kernel(Pref
         }
 #pragma unroll
         for (int st = 0; st < 2; ++st)
-          pb[qb][kb][st] = u32x4{pack_bf16(pr[8 * st + 0], pr[8 * st + 1]),
-                                 pack_bf16(pr[8 * st + 2], pr[8 * st + 3]),
-                                 pack_bf16(pr[8 * st + 4], pr[8 * st + 5]),
-                                 pack_bf16(pr[8 * st + 6], pr[8 * st + 7])};
+          pb[qb][st] = u32x4{pack_bf16(pr[8 * st + 0], pr[8 * st + 1]),
+                             pack_bf16(pr[8 * st + 2], pr[8 * st + 3]),
+                             pack_bf16(pr[8 * st + 4], pr[8 * st + 5]),
+                             pack_bf16(pr[8 * st + 6], pr[8 * st + 7])};
+        l_run[qb] = fmaf(l_run[qb], alpha[qb], psum);
       }
-      l_run[qb] = fmaf(l_run[qb], alpha[qb], psum);
-    }
-    if (__any(rescale)) {
+      if (__any(rescale)) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+          for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha[qb];
-    }
-
-    // O^T += V^T P^T: for d block db, key step (kb, st) the A operand holds
-    // V[key = kb*32 + 16 st + 8 (e / 4) + 4 half + e % 4][d = db*32 + lq], e = 0..7, fetched with
-    // two transposing reads: this lane points at V[key0 + j][d0 + 4 q], j = (lane % 16) / 4,
-    // q = lane % 4, where d0 = db*32 + 16 ((lane / 16) % 2) is its 16-lane group's first dim.
-    const uint16_t* vsrc = sv + (((lane & 15) >> 2) + 4 * half) * VSTR + 16 * ((lane >> 4) & 1) +
-                           4 * (lane & 3);
+            for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha[qb];
+      }
+      // For d block db and key step st the A operand holds
+      // V[key = kb*32 + 16 st + 8 (e / 4) + 4 half + e % 4][d = db*32 + lq], e = 0..7, fetched
+      // with two transposing reads: this lane points at V[key0 + j][d0 + 4 q], j = (lane % 16)
+      // / 4, q = lane % 4, where d0 = db*32 + 16 ((lane / 16) % 2) is its 16-lane group's first
+      // dim.
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           const uint16_t* pv = vsrc + (kb * 32 + 16 * st) * VSTR + db * 32;
@@ -312,11 +316,21 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_kernel(Pref
           const u32x2 hi = ld_tr(pv + 8 * VSTR);
           const u32x4 va = u32x4{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(va, pb[qb][kb][st], o[qb][db]);
+          for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(va, pb[qb][st], o[qb][db]);
         }
     }
 
-    if (more) store_tile(rk, rv, sK + (buf ^ 1) * K_TILE, sV + (buf ^ 1) * V_TILE);
+  };
+
+  for (int j = 0; j < ts.ntiles; j += 2) {
+    if (j + 2 < ts.ntiles) load_tile(kb_, vb_, kbase, vbase, rs, ts.start(j + 2), S - 1);
+    tile(j, 0);
+    if (j + 1 < ts.ntiles) store_tile(ka_, va_, sK + K_TILE, sV + V_TILE);
+    __syncthreads();
+    if (j + 1 >= ts.ntiles) break;
+    if (j + 3 < ts.ntiles) load_tile(ka_, va_, kbase, vbase, rs, ts.start(j + 3), S - 1);
+    tile(j + 1, 1);
+    if (j + 2 < ts.ntiles) store_tile(kb_, vb_, sK, sV);
     __syncthreads();
   }
 
@@ -346,7 +360,8 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_kernel(Pref
 
 hipError_t launch_prefill(const PrefillArgs& a, int out_f32, hipStream_t s) {
   constexpr int QB = RSWA_PREFILL_QB;
-  const dim3 grid((a.max_seqlen + 128 * QB - 1) / (128 * QB), a.heads, a.nseq);
+  constexpr int BMQ = kWavesPF * 32 * QB;
+  const dim3 grid((a.max_seqlen + BMQ - 1) / BMQ, a.heads, a.nseq);
   if (out_f32)
     hipLaunchKernelGGL((prefill_kernel<float, QB>), grid, dim3(kThreads), 0, s, a);
   else
