@@ -71,9 +71,10 @@ def parse():
     ap.add_argument("--no-ragged", action="store_true", help="skip the ragged-batch decode")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also time a plain 1 GiB device copy (bandwidth reference, PMC scale)")
-    ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL"),
-                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs into "
-                         "profiles/<KERNEL>_traffic.json and exit (no GPU use)")
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "KIND"),
+                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs of the decode or "
+                         "prefill kernel (KIND) into profiles/<KIND>_traffic.json and exit "
+                         "(no GPU use)")
     ap.add_argument("--prefill-runs", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     return ap.parse_args()
@@ -260,7 +261,7 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
     return dict(bytes_moved=2 * nbytes, ms=ms, gbs=2 * nbytes / (ms * 1e-3) / 1e9)
 
 
-def pmc_summary(fetch_csv: str, write_csv: str, kernel: str):
+def pmc_summary(fetch_csv: str, write_csv: str, kind: str):
     """Scale the decode/prefill kernels' FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the same
     counters read for the 1 GiB calibration copy (1 GiB read, 1 GiB written)."""
     import csv
@@ -274,12 +275,14 @@ def pmc_summary(fetch_csv: str, write_csv: str, kernel: str):
         return out
     fetch = per_kernel(fetch_csv, "FETCH_SIZE")
     write = per_kernel(write_csv, "WRITE_SIZE")
-    copy_k = [k for k in fetch if "copy" in k.lower() and "elementwise" in k.lower()] or \
-             [k for k in fetch if "copy" in k.lower()]
-    big = lambda vals: max(vals)
-    cf = (1 << 30) / (big(fetch[copy_k[0]]) * 1024.0)
-    cw = (1 << 30) / (big(write[copy_k[0]]) * 1024.0)
-    names = [k for k in fetch if kernel in k]
+    # torch's copy_ of the calibration buffers dispatches the runtime's blit kernel; its largest
+    # dispatch is the 1 GiB copy (1 GiB read, 1 GiB written)
+    copy_k = [k for k in fetch if k.startswith("__amd_rocclr_copyBuffer")]
+    if not copy_k:
+        raise SystemExit("no calibration copy dispatch in the counter CSV (run with --copy-calibration)")
+    cf = (1 << 30) / (max(fetch[copy_k[0]]) * 1024.0)
+    cw = (1 << 30) / (max(write[copy_k[0]]) * 1024.0)
+    names = [k for k in fetch if f"{kind}_kernel" in k]
     rec = dict(kernel_names=names, copy_kernel=copy_k[0], fetch_scale=cf, write_scale=cw)
     for k in names:
         f = np.array(fetch[k]) * 1024.0 * cf
@@ -288,7 +291,7 @@ def pmc_summary(fetch_csv: str, write_csv: str, kernel: str):
                       write_bytes_median=float(np.median(w)))
     main = max(names, key=lambda k: rec[k]["fetch_bytes_median"])
     rec["bytes_per_launch"] = rec[main]["fetch_bytes_median"] + rec[main]["write_bytes_median"]
-    src = DECODE_SOURCES if kernel.startswith("decode") else PREFILL_SOURCES
+    src = DECODE_SOURCES if kind == "decode" else PREFILL_SOURCES
     rec["source_hash"] = source_hash(src)
     return rec
 
