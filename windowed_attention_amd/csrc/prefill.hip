@@ -33,6 +33,9 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in VGPRs
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+#ifndef RSWA_PF_SCHED
+#define RSWA_PF_SCHED 4  // > 0: K-fragment LDS reads kept ahead of the score MFMAs
+#endif
 #ifndef RSWA_PF_WAVES
 #define RSWA_PF_WAVES 8  // waves per workgroup (each owns QB x 32 queries)
 #endif
@@ -238,6 +241,16 @@ __global__ __launch_bounds__(kThreads, (QB == 1 ? 8 : 4) / kWavesPF) void prefil
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = mfma32(ka, qf[qb][st], sacc[qb][kb]);
       }
+#if RSWA_PF_SCHED
+    // keep RSWA_PF_SCHED K-fragment reads in flight ahead of the score MFMA chain
+    __builtin_amdgcn_sched_group_barrier(0x100, RSWA_PF_SCHED, 0);
+#pragma unroll
+    for (int i = 0; i < 16 - RSWA_PF_SCHED; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, QB * RSWA_PF_SCHED, 0);
+#endif
 
     // element mask (branch-free interval test) where the tile is not fully visible
     const bool need_mask = is_pre ? (k0 + BN > m || (pc && q0 < m && k0 + BN - 1 > q0)) : true;
