@@ -278,3 +278,89 @@ def brute_prefill(Q, K, V, m: int, n: int, prefix_causal: bool = False,
             for c in range(d):
                 O[p][h][c] = sum(w * float(V[k][h][c]) for w, k in zip(ws, keys)) / tot
     return O
+
+
+# ------------------------------------------------------------------------------------------
+# teacher-forced training pass: log-sum-exp and gradients of the masked prefill
+# ------------------------------------------------------------------------------------------
+# The pages train the R-SWA decoder on packed 32K sequences with the encoder frozen [GeekNews,
+# training section; deep dive, training setup table]. They print no backward formula; what
+# follows is the chain rule applied to the masked softmax attention above, in float64:
+#   Z = scale * Q K^T (invisible pairs -inf),  P = softmax_rows(Z),  O = P V,  L = sum(dO * O)
+#   dV = P^T dO,  dP = dO V^T,  dZ = softmax_grad(P, dP),  dQ = scale dZ K,  dK = scale dZ^T Q.
+def softmax_grad(P: np.ndarray, dP: np.ndarray) -> np.ndarray:
+    """Back-propagate dP through P = softmax(Z) taken along the last axis: the Jacobian
+    diag(P) - P P^T applied to dP, i.e. P * (dP - sum_j P_j dP_j)."""
+    return P * (dP - (P * dP).sum(axis=-1, keepdims=True))
+
+
+def prefill_lse(Q, K, m: int, n: int, prefix_causal: bool = False, scale: float | None = None,
+                rows=None, block: int = 512) -> np.ndarray:
+    """Natural-log log-sum-exp of each selected query's visible scaled scores, [rows, H] float64:
+    lse_p = log sum_{k visible} exp(scale q_p . k_k) (max-shifted before the exp)."""
+    Q = np.asarray(Q)
+    S, H, d = Q.shape
+    scale = default_scale(d) if scale is None else scale
+    rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+    Kf = np.asarray(K, dtype=np.float64)
+    keys = np.arange(S)
+    out = np.empty((rows.size, H), dtype=np.float64)
+    for s in range(0, rows.size, block):
+        p = rows[s:s + block]
+        vis = prefill_visible(p[:, None], keys[None, :], m, n, prefix_causal)
+        kmax = int(np.nonzero(vis.any(axis=0))[0].max()) + 1
+        vis = vis[:, :kmax]
+        Qb = np.asarray(Q[p], dtype=np.float64)
+        for h in range(H):
+            z = np.where(vis, scale * (Qb[:, h, :] @ Kf[:kmax, h, :].T), -np.inf)
+            zmax = z.max(axis=1)
+            out[s:s + p.size, h] = zmax + np.log(np.exp(z - zmax[:, None]).sum(axis=1))
+    return out
+
+
+def prefill_backward(Q, K, V, dO, m: int, n: int, prefix_causal: bool = False,
+                     scale: float | None = None, heads=None, q_rows=None, k_rows=None,
+                     block: int = 512):
+    """Gradients of L = sum(dO * prefill(Q, K, V)) for one packed sequence (float64).
+
+    Q, K, V, dO: [S, H, d]. Returns (dQ [q_rows, heads, d], dK [k_rows, heads, d],
+    dV [k_rows, heads, d]) for the selected heads / query rows / key rows (default: all).
+    Every query contributes to the key gradients; the sums over queries run in query blocks of
+    `block` rows (an order of summation only), each block forming its scores, probabilities and
+    probability gradients in full before the chain-rule products.
+    """
+    Q = np.asarray(Q)
+    S, H, d = Q.shape
+    scale = default_scale(d) if scale is None else scale
+    heads = list(range(H)) if heads is None else list(heads)
+    q_rows = np.arange(S) if q_rows is None else np.asarray(q_rows, dtype=np.int64)
+    k_rows = np.arange(S) if k_rows is None else np.asarray(k_rows, dtype=np.int64)
+    q_pos = {int(p): i for i, p in enumerate(q_rows)}
+    Kf = np.asarray(K, dtype=np.float64)
+    Vf = np.asarray(V, dtype=np.float64)
+    dQ = np.zeros((q_rows.size, len(heads), d))
+    dK = np.zeros((k_rows.size, len(heads), d))
+    dV = np.zeros((k_rows.size, len(heads), d))
+    keys = np.arange(S)
+    for s in range(0, S, block):
+        p = np.arange(s, min(S, s + block))
+        vis = prefill_visible(p[:, None], keys[None, :], m, n, prefix_causal)
+        kmax = int(np.nonzero(vis.any(axis=0))[0].max()) + 1
+        vis = vis[:, :kmax]
+        kin = k_rows[k_rows < kmax]
+        kidx = np.nonzero(k_rows < kmax)[0]
+        sel = [i for i, pp in enumerate(p) if int(pp) in q_pos]
+        Qb = np.asarray(Q[p], dtype=np.float64)
+        dOb = np.asarray(dO[p], dtype=np.float64)
+        for hi, h in enumerate(heads):
+            z = np.where(vis, scale * (Qb[:, h, :] @ Kf[:kmax, h, :].T), -np.inf)
+            w = np.exp(z - z.max(axis=1, keepdims=True))
+            P = w / w.sum(axis=1, keepdims=True)
+            dP = dOb[:, h, :] @ Vf[:kmax, h, :].T
+            dZ = softmax_grad(P, dP)
+            if sel:
+                rows_out = [q_pos[int(p[i])] for i in sel]
+                dQ[rows_out, hi, :] = scale * (dZ[sel] @ Kf[:kmax, h, :])
+            dK[kidx, hi, :] += scale * (dZ[:, kin].T @ Qb[:, h, :])
+            dV[kidx, hi, :] += P[:, kin].T @ dOb[:, h, :]
+    return dQ, dK, dV
