@@ -307,3 +307,30 @@ def test_cfg_ragged_sampled(wa):
     worst = check_steps(wl, 0, got, seqs_per_step=3)
     print(f"ragged decode: worst max-abs error {worst:.3e}")
     tr.cache.close()
+
+
+# ---------------------------------------------------------------------------------------------
+# the comparison modes of the pages: vanilla sliding window and sink tokens
+# ---------------------------------------------------------------------------------------------
+def test_vanilla_sliding_window_decode(wa):
+    """Vanilla SWA (the pages' "progressive blurring" contrast case): no reference prefix; the
+    visual tokens are appended through the ring like outputs and slide out of the window."""
+    n, P, T = 48, 100, 150  # window, streamed "visual" tokens, outputs
+    wl = W.make_decode("vswa", 86, "bf16", [0, 0], [n, n], [P + T, P + T], seed=26, outlier_p=0.01)
+    tr = Trajectory(wa, wl, wa.MODE_RSWA)
+    got = tr.run(range(P + 1, P + T + 1), fused=True)  # every query after the visual tokens
+    check_steps(wl, 0, got)
+    # the first visual token is still visible at step n and gone from step n + 1 on: with a
+    # reference prefix (R-SWA) it never leaves
+    assert O.decode_visible(0, n, n)[0] and not O.decode_visible(0, n, n + 1)[0]
+    tr.cache.close()
+
+
+def test_sink_tokens_decode(wa):
+    """Attention sinks: the first s tokens stay visible, the rest slide — R-SWA with m = s."""
+    s, n, T = 4, 32, 200
+    wl = W.make_decode("sink", 87, "bf16", [s, s, s], [n, n, n], [T, T, T], seed=27)
+    tr = Trajectory(wa, wl, wa.MODE_RSWA)
+    got = tr.run(range(1, T + 1), fused=True)
+    check_steps(wl, 0, got)
+    tr.cache.close()
