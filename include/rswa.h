@@ -149,6 +149,42 @@ rswa_status rswa_prefill_attn(const void* q_dev, const void* k_dev, const void* 
                               int32_t nseq, int32_t num_heads, int32_t head_dim, int32_t max_seqlen,
                               int32_t prefix_causal, float softmax_scale, void* stream);
 
+/* K3 forward for training: rswa_prefill_attn plus the per-row log-sum-exp that the backward
+ * needs. lse_dev: device float32 [total][H], written lse[p][h] = ln sum_{k visible} exp(scale q.k)
+ * over the same visible set. Other arguments and errors as rswa_prefill_attn; lse_dev NULL is
+ * RSWA_E_INVALID. */
+rswa_status rswa_prefill_fwd(const void* q_dev, const void* k_dev, const void* v_dev,
+                             void* out_dev, int32_t out_dtype, float* lse_dev,
+                             const int32_t* cu_seqlens_dev, const int32_t* prefix_len_dev,
+                             const int32_t* window_dev, int32_t nseq, int32_t num_heads,
+                             int32_t head_dim, int32_t max_seqlen, int32_t prefix_causal,
+                             float softmax_scale, void* stream);
+
+/* Backward of the teacher-forced pass (the pages train the R-SWA decoder on packed 32K-token
+ * sequences: GeekNews "Unlimited OCR", training section; deep dive "Unlimited-OCR", training
+ * setup). With P the masked softmax of rswa_prefill_attn, O = P V and the output gradient dO:
+ *   delta_p = sum_d dO[p][d] O[p][d],  dS = P * (dO V^T - delta),
+ *   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
+ * Packed documents: each cu_seqlens segment is one prefix + output document with its own m and n;
+ * no query sees a key of another segment.
+ * q/k/v_dev, dout_dev: [total][H][D] bf16; out_dev: the forward output [total][H][D] of out_dtype;
+ * lse_dev: float32 [total][H] from rswa_prefill_fwd with the same arguments.
+ * delta_dev: caller-owned float32 [total][H] work array, overwritten with delta.
+ * dq/dk/dv_dev: [total][H][D] of grad_dtype, overwritten on every row of every segment (rows
+ * beyond cu_seqlens[nseq] are not touched). total_tokens (host) = rows of these arrays, at least
+ * cu_seqlens[nseq]; delta is written for all of them.
+ * The library allocates nothing; all work is enqueued on `stream`.
+ * Errors: as rswa_prefill_attn, plus RSWA_E_INVALID for NULL dout/lse/delta/dq/dk/dv, a bad
+ * grad_dtype or total_tokens < 0. Device-side metadata is trusted. */
+rswa_status rswa_prefill_bwd(const void* q_dev, const void* k_dev, const void* v_dev,
+                             const void* out_dev, int32_t out_dtype, const void* dout_dev,
+                             const float* lse_dev, float* delta_dev, void* dq_dev, void* dk_dev,
+                             void* dv_dev, int32_t grad_dtype, const int32_t* cu_seqlens_dev,
+                             const int32_t* prefix_len_dev, const int32_t* window_dev,
+                             int32_t nseq, int32_t total_tokens, int32_t num_heads,
+                             int32_t head_dim, int32_t max_seqlen, int32_t prefix_causal,
+                             float softmax_scale, void* stream);
+
 /* Copy the per-sequence step counters t_b to steps_host [B]. BLOCKS until `stream` has passed
  * all prior work. Returns RSWA_E_CAPACITY if a FULL_CAUSAL append past max_steps was skipped on
  * the device since creation (the counters are still copied). */

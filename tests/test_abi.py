@@ -110,3 +110,30 @@ def test_null_arguments_are_rejected_before_any_device_work(wa):
                                  null) == -1
     assert lib.rswa_prefill_attn(one, one, one, one, 1, one, one, one, 0, 16, 128, 8, 0, 0.0,
                                  null) == -1
+
+
+def test_training_entry_points_reject_bad_arguments_before_any_device_work(wa):
+    lib = wa._lib
+    null, one = ctypes.c_void_p(None), ctypes.c_void_p(16)
+    # forward with log-sum-exp: NULL lse, bad head_dim
+    assert lib.rswa_prefill_fwd(one, one, one, one, 1, null, one, one, one, 1, 16, 128, 8, 0,
+                                0.0, null) == -1
+    assert lib.rswa_prefill_fwd(one, one, one, one, 1, one, one, one, one, 1, 16, 64, 8, 0,
+                                0.0, null) == -2
+    # backward: each gradient-side pointer NULL in turn, then a bad grad dtype and token count
+    args = [one, one, one, one, 1, one, one, one, one, one, one, 1, one, one, one,
+            1, 8, 16, 128, 8, 0, 0.0, null]
+    for i in (5, 6, 7, 8, 9, 10):
+        bad = list(args)
+        bad[i] = null
+        assert lib.rswa_prefill_bwd(*bad) == -1, i
+    bad = list(args)
+    bad[11] = 7
+    assert lib.rswa_prefill_bwd(*bad) == -1
+    bad = list(args)
+    bad[16] = -1
+    assert lib.rswa_prefill_bwd(*bad) == -1
+    bad = list(args)
+    bad[18] = 96
+    assert lib.rswa_prefill_bwd(*bad) == -2
+    assert b"head_dim" in lib.rswa_last_error()

@@ -24,7 +24,8 @@ STATUS = {0: "RSWA_OK", -1: "RSWA_E_INVALID", -2: "RSWA_E_UNSUPPORTED", -3: "RSW
 
 # Every symbol include/rswa.h declares.
 EXPORTS = ("rswa_cache_plan", "rswa_cache_bytes", "rswa_cache_create", "rswa_append_kv",
-           "rswa_decode_attn", "rswa_decode_step", "rswa_prefill_attn", "rswa_cache_steps", "rswa_cache_info",
+           "rswa_decode_attn", "rswa_decode_step", "rswa_prefill_attn", "rswa_prefill_fwd",
+           "rswa_prefill_bwd", "rswa_cache_steps", "rswa_cache_info",
            "rswa_cache_set_decode_split", "rswa_cache_decode_plan", "rswa_cache_destroy",
            "rswa_status_str",
            "rswa_last_error")
@@ -63,6 +64,10 @@ def _load():
         "rswa_decode_step": (i32, [vp, vp, vp, vp, vp, i32, f32, vp, vp]),
         "rswa_prefill_attn": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                                     vp]),
+        "rswa_prefill_fwd": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                   f32, vp]),
+        "rswa_prefill_bwd": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                                   i32, i32, i32, i32, i32, i32, f32, vp]),
         "rswa_cache_steps": (i32, [vp, pi32, vp]),
         "rswa_cache_info": (i32, [vp, ctypes.POINTER(vp), pi64, pi32]),
         "rswa_cache_set_decode_split": (i32, [vp, i32, i32]),
@@ -336,6 +341,69 @@ def rswa_prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seql
         _dev(window, "window", torch.int32, (nseq,)), nseq, H, D, int(max_seqlen),
         int(bool(prefix_causal)), ctypes.c_float(scale), _stream(stream)), "rswa_prefill_attn")
     return out
+
+
+def _max_seqlen(cu_seqlens: torch.Tensor, max_seqlen: int | None) -> int:
+    if max_seqlen is not None:
+        return int(max_seqlen)
+    cs = cu_seqlens.cpu().numpy()
+    return int(np.diff(cs).max()) if cs.size > 1 else 0
+
+
+def rswa_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                     prefix_len: torch.Tensor, window: torch.Tensor, *, out=None, lse=None,
+                     out_dtype: torch.dtype = torch.bfloat16, prefix_causal: bool = False,
+                     scale: float = 0.0, max_seqlen: int | None = None, stream=None):
+    """Training forward: rswa_prefill_attn plus the natural log-sum-exp per (token, head).
+    Returns (out [total][H][D], lse [total][H] float32)."""
+    total, H, D = q.shape
+    nseq = prefix_len.numel()
+    max_seqlen = _max_seqlen(cu_seqlens, max_seqlen)
+    if out is None:
+        out = torch.empty((total, H, D), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((total, H), dtype=torch.float32, device=q.device)
+    shape = (total, H, D)
+    _check(_lib.rswa_prefill_fwd(
+        _dev(q, "q", torch.bfloat16, shape), _dev(k, "k", torch.bfloat16, shape),
+        _dev(v, "v", torch.bfloat16, shape), _dev(out, "out", None, shape),
+        _dtype_code(out.dtype), _dev(lse, "lse", torch.float32, (total, H)),
+        _dev(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,)),
+        _dev(prefix_len, "prefix_len", torch.int32, (nseq,)),
+        _dev(window, "window", torch.int32, (nseq,)), nseq, H, D, max_seqlen,
+        int(bool(prefix_causal)), ctypes.c_float(scale), _stream(stream)), "rswa_prefill_fwd")
+    return out, lse
+
+
+def rswa_prefill_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                     dout: torch.Tensor, lse: torch.Tensor, cu_seqlens: torch.Tensor,
+                     prefix_len: torch.Tensor, window: torch.Tensor, *, dq=None, dk=None, dv=None,
+                     delta=None, grad_dtype: torch.dtype = torch.float32,
+                     prefix_causal: bool = False, scale: float = 0.0,
+                     max_seqlen: int | None = None, stream=None):
+    """Gradients (dq, dk, dv) of the R-SWA-masked prefill; dout bf16 [total][H][D], out and lse
+    from rswa_prefill_fwd. `delta` ([total][H] float32) is a work array, allocated if absent."""
+    total, H, D = q.shape
+    nseq = prefix_len.numel()
+    max_seqlen = _max_seqlen(cu_seqlens, max_seqlen)
+    shape = (total, H, D)
+    mk = lambda t: torch.empty(shape, dtype=grad_dtype, device=q.device) if t is None else t
+    dq, dk, dv = mk(dq), mk(dk), mk(dv)
+    if delta is None:
+        delta = torch.empty((total, H), dtype=torch.float32, device=q.device)
+    if not (dq.dtype == dk.dtype == dv.dtype):
+        raise TypeError("dq, dk and dv must share one dtype")
+    _check(_lib.rswa_prefill_bwd(
+        _dev(q, "q", torch.bfloat16, shape), _dev(k, "k", torch.bfloat16, shape),
+        _dev(v, "v", torch.bfloat16, shape), _dev(out, "out", None, shape),
+        _dtype_code(out.dtype), _dev(dout, "dout", torch.bfloat16, shape),
+        _dev(lse, "lse", torch.float32, (total, H)), _dev(delta, "delta", torch.float32, (total, H)),
+        _dev(dq, "dq", None, shape), _dev(dk, "dk", None, shape), _dev(dv, "dv", None, shape),
+        _dtype_code(dq.dtype), _dev(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,)),
+        _dev(prefix_len, "prefix_len", torch.int32, (nseq,)),
+        _dev(window, "window", torch.int32, (nseq,)), nseq, total, H, D, max_seqlen,
+        int(bool(prefix_causal)), ctypes.c_float(scale), _stream(stream)), "rswa_prefill_bwd")
+    return dq, dk, dv
 
 
 def status_str(code: int) -> str:

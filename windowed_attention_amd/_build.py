@@ -22,7 +22,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-std=c++17", "-O3", "-fPIC", "-I", INCLUDE, "-I", CSRC]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-HIP_SOURCES = ["rswa_api.hip", "append.hip", "decode.hip", "prefill.hip"]
+HIP_SOURCES = ["rswa_api.hip", "append.hip", "decode.hip", "prefill.hip", "prefill_bwd.hip"]
 CXX_SOURCES = ["plan.cpp"]
 
 

@@ -66,6 +66,7 @@ struct PrefillArgs {
   const uint16_t* k;
   const uint16_t* v;
   void* out;                // [total][H][D]
+  float* lse;               // [total][H] natural log-sum-exp of the scaled scores, or nullptr
   const int32_t* cu_seqlens;
   const int32_t* prefix_len;
   const int32_t* window;
@@ -76,12 +77,36 @@ struct PrefillArgs {
   float scale_log2;
 };
 
+struct BwdArgs {
+  const uint16_t* q;        // [total][H][D] bf16
+  const uint16_t* k;
+  const uint16_t* v;
+  const void* out;          // [total][H][D] forward output (bf16 or float32)
+  const uint16_t* dout;     // [total][H][D] bf16 gradient of the output
+  const float* lse;         // [total][H] natural log-sum-exp from the forward
+  float* delta;             // [total][H] written: rowsum(dout * out)
+  void* dq;                 // [total][H][D] gradients (bf16 or float32)
+  void* dk;
+  void* dv;
+  const int32_t* cu_seqlens;
+  const int32_t* prefix_len;
+  const int32_t* window;
+  int32_t nseq;
+  int32_t heads;
+  int32_t max_seqlen;
+  int32_t prefix_causal;
+  float scale;
+  float scale_log2;
+};
+
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_prefix_copy(const PrefixCopyArgs& a, int kv_f32, int max_rows, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, int batch, int kv_f32, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int kv_f32, int out_f32, int grid_blocks,
                          bool need_merge, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int out_f32, hipStream_t s);
+hipError_t launch_prefill_bwd(const BwdArgs& a, int out_f32, int grad_f32, int64_t total,
+                              hipStream_t s);
 // Resident 256-thread decode workgroups per CU (occupancy of the decode kernel for a batch of B).
 int decode_blocks_per_cu(int kv_f32, int out_f32, int batch);
 size_t decode_lds_bytes(int batch);

@@ -21,17 +21,11 @@
 // read, so V needs no transpose on the way in. Q stays in registers for the whole key loop.
 // Softmax runs in the log2 domain in float32; P is rounded to bf16 for the PV product and the
 // output is normalised by the float32 row sum.
-#include "device.h"
 #include "kernels.h"
+#include "mfma.h"
 
 namespace rswa {
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in VGPRs
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #ifndef RSWA_PF_SCHED
 #define RSWA_PF_SCHED 4  // > 0: K-fragment LDS reads kept ahead of the score MFMAs
@@ -54,18 +48,6 @@ constexpr int VSTR = kHeadDim + RSWA_PF_VPAD;  // V tile row stride (bf16)
 constexpr int K_TILE = BN * KSTR;              // bf16 elements per K buffer
 constexpr int V_TILE = BN * VSTR;              // bf16 elements per V buffer
 constexpr float kLazy = 8.f;            // log2-domain slack before the reference max moves
-
-__device__ __forceinline__ floatx16 mfma32(const u32x4& a, const u32x4& b, const floatx16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  bf16x2v_t v;
-  v[0] = (__bf16)lo;
-  v[1] = (__bf16)hi;
-  return __builtin_bit_cast(uint32_t, v);
-}
 
 struct TileSched {
   int n_pre;   // tiles over the prefix segment [0, pre_end)
@@ -100,43 +82,6 @@ __device__ __forceinline__ void store_tile(const u32x4 (&rk)[kKeysPerThread],
     *reinterpret_cast<u32x4*>(sk + (kg * kKeysPerThread + u) * KSTR + c * 8) = rk[u];
     *reinterpret_cast<u32x4*>(sv + (kg * kKeysPerThread + u) * VSTR + c * 8) = rv[u];
   }
-}
-
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-
-// Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each group of 16 lanes, output lane i
-// gets element i % 4 of the 8-byte chunks that lanes 4j + i / 4 (j = 0..3) point at. With lane
-// 4j + q pointing at V[k0 + j][d0 + 4q .. +3], lane i receives V[k0 .. k0 + 3][d0 + i]: four
-// consecutive keys of its own dim, i.e. half of a V^T MFMA operand.
-__device__ __forceinline__ u32x2 ld_tr(const uint16_t* p) {
-  const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (v4i16_t __attribute__((address_space(3)))*)(p));
-  return __builtin_bit_cast(u32x2, r);
-}
-
-template <typename OUT>
-__device__ __forceinline__ void store_out4(OUT* p, float a, float b, float c, float d);
-template <>
-__device__ __forceinline__ void store_out4<float>(float* p, float a, float b, float c, float d) {
-  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
-}
-template <>
-__device__ __forceinline__ void store_out4<uint16_t>(uint16_t* p, float a, float b, float c, float d) {
-  *reinterpret_cast<u32x2*>(p) = u32x2{f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16),
-                                       f32_to_bf16_bits(c) | (f32_to_bf16_bits(d) << 16)};
-}
-
-// max over the two lane halves holding the same query (lanes l and l ^ 32)
-__device__ __forceinline__ float xhalf_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float xhalf_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // QB query blocks of 32 per wave: every K / V^T fragment read from LDS feeds QB MFMAs.
@@ -352,15 +297,11 @@ __global__ __launch_bounds__(kThreads, (QB == 1 ? 8 : 4) / kWavesPF) void prefil
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = xhalf_sum(l_run[qb]);
     if (p[qb] < q1) {
-      const float inv = 1.f / l_tot;
-      OUT* orow = reinterpret_cast<OUT*>(a.out) + ((int64_t)(cu0 + p[qb]) * a.heads + h) * kHeadDim;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          store_out4<OUT>(orow + db * 32 + 8 * g + 4 * half, o[qb][db][4 * g] * inv,
-                          o[qb][db][4 * g + 1] * inv, o[qb][db][4 * g + 2] * inv,
-                          o[qb][db][4 * g + 3] * inv);
+      const int64_t row = (int64_t)(cu0 + p[qb]) * a.heads + h;
+      store_row128<OUT>(reinterpret_cast<OUT*>(a.out) + row * kHeadDim, o[qb], 1.f / l_tot, half);
+      // natural log-sum-exp of the scaled scores: m_run + log2(l) in the log2 domain, times ln 2
+      if (a.lse != nullptr && half == 0)
+        a.lse[row] = (m_run[qb] + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
     }
   }
 }

@@ -452,16 +452,15 @@ rswa_status rswa_cache_destroy(rswa_cache* c) {
   return RSWA_OK;
 }
 
-rswa_status rswa_prefill_attn(const void* q_dev, const void* k_dev, const void* v_dev,
-                              void* out_dev, int32_t out_dtype, const int32_t* cu_seqlens_dev,
-                              const int32_t* prefix_len_dev, const int32_t* window_dev,
-                              int32_t nseq, int32_t num_heads, int32_t head_dim,
-                              int32_t max_seqlen, int32_t prefix_causal, float softmax_scale,
-                              void* stream) {
-  if (!q_dev || !k_dev || !v_dev || !out_dev)
-    return fail(RSWA_E_INVALID, "q/k/v/out pointer is NULL");
-  if (!cu_seqlens_dev || !prefix_len_dev || !window_dev)
-    return fail(RSWA_E_INVALID, "sequence metadata pointer is NULL");
+namespace {
+
+// Host-checkable arguments shared by the prefill entry points.
+rswa_status check_prefill(const void* q, const void* k, const void* v, const void* out,
+                          int32_t out_dtype, const int32_t* cu, const int32_t* pl,
+                          const int32_t* win, int32_t nseq, int32_t num_heads, int32_t head_dim,
+                          int32_t max_seqlen, int32_t prefix_causal, float softmax_scale) {
+  if (!q || !k || !v || !out) return fail(RSWA_E_INVALID, "q/k/v/out pointer is NULL");
+  if (!cu || !pl || !win) return fail(RSWA_E_INVALID, "sequence metadata pointer is NULL");
   if (nseq < 1) return fail(RSWA_E_INVALID, "nseq must be >= 1");
   if (num_heads < 1 || num_heads > rswa::kMaxHeads)
     return fail(RSWA_E_INVALID, "num_heads out of range");
@@ -474,14 +473,32 @@ rswa_status rswa_prefill_attn(const void* q_dev, const void* k_dev, const void* 
     return fail(RSWA_E_INVALID, "prefix_causal must be 0 or 1");
   if (!(softmax_scale <= 0.f) && !std::isfinite(softmax_scale))
     return fail(RSWA_E_INVALID, "softmax_scale must be finite");
+  return RSWA_OK;
+}
+
+float resolve_scale(float softmax_scale, int32_t head_dim) {
+  return softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+}
+
+rswa_status prefill_forward(const void* q_dev, const void* k_dev, const void* v_dev,
+                            void* out_dev, int32_t out_dtype, float* lse_dev,
+                            const int32_t* cu_seqlens_dev, const int32_t* prefix_len_dev,
+                            const int32_t* window_dev, int32_t nseq, int32_t num_heads,
+                            int32_t head_dim, int32_t max_seqlen, int32_t prefix_causal,
+                            float softmax_scale, void* stream, const char* what) {
+  const rswa_status st = check_prefill(q_dev, k_dev, v_dev, out_dev, out_dtype, cu_seqlens_dev,
+                                       prefix_len_dev, window_dev, nseq, num_heads, head_dim,
+                                       max_seqlen, prefix_causal, softmax_scale);
+  if (st != RSWA_OK) return st;
   if (max_seqlen == 0) return RSWA_OK;
   try {
-    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+    const float scale = resolve_scale(softmax_scale, head_dim);
     rswa::PrefillArgs a{};
     a.q = reinterpret_cast<const uint16_t*>(q_dev);
     a.k = reinterpret_cast<const uint16_t*>(k_dev);
     a.v = reinterpret_cast<const uint16_t*>(v_dev);
     a.out = out_dev;
+    a.lse = lse_dev;
     a.cu_seqlens = cu_seqlens_dev;
     a.prefix_len = prefix_len_dev;
     a.window = window_dev;
@@ -492,11 +509,86 @@ rswa_status rswa_prefill_attn(const void* q_dev, const void* k_dev, const void* 
     a.scale_log2 = scale * 1.4426950408889634f;
     const hipError_t e = rswa::launch_prefill(a, out_dtype == RSWA_F32,
                                               reinterpret_cast<hipStream_t>(stream));
-    if (e == hipErrorNotSupported) return fail(RSWA_E_UNSUPPORTED, "prefill kernel not built");
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
     return RSWA_OK;
   } catch (...) {
-    return fail(RSWA_E_INTERNAL, "exception in rswa_prefill_attn");
+    return fail(RSWA_E_INTERNAL, what);
+  }
+}
+
+}  // namespace
+
+rswa_status rswa_prefill_attn(const void* q_dev, const void* k_dev, const void* v_dev,
+                              void* out_dev, int32_t out_dtype, const int32_t* cu_seqlens_dev,
+                              const int32_t* prefix_len_dev, const int32_t* window_dev,
+                              int32_t nseq, int32_t num_heads, int32_t head_dim,
+                              int32_t max_seqlen, int32_t prefix_causal, float softmax_scale,
+                              void* stream) {
+  return prefill_forward(q_dev, k_dev, v_dev, out_dev, out_dtype, nullptr, cu_seqlens_dev,
+                         prefix_len_dev, window_dev, nseq, num_heads, head_dim, max_seqlen,
+                         prefix_causal, softmax_scale, stream, "exception in rswa_prefill_attn");
+}
+
+rswa_status rswa_prefill_fwd(const void* q_dev, const void* k_dev, const void* v_dev,
+                             void* out_dev, int32_t out_dtype, float* lse_dev,
+                             const int32_t* cu_seqlens_dev, const int32_t* prefix_len_dev,
+                             const int32_t* window_dev, int32_t nseq, int32_t num_heads,
+                             int32_t head_dim, int32_t max_seqlen, int32_t prefix_causal,
+                             float softmax_scale, void* stream) {
+  if (!lse_dev) return fail(RSWA_E_INVALID, "lse pointer is NULL");
+  return prefill_forward(q_dev, k_dev, v_dev, out_dev, out_dtype, lse_dev, cu_seqlens_dev,
+                         prefix_len_dev, window_dev, nseq, num_heads, head_dim, max_seqlen,
+                         prefix_causal, softmax_scale, stream, "exception in rswa_prefill_fwd");
+}
+
+rswa_status rswa_prefill_bwd(const void* q_dev, const void* k_dev, const void* v_dev,
+                             const void* out_dev, int32_t out_dtype, const void* dout_dev,
+                             const float* lse_dev, float* delta_dev, void* dq_dev, void* dk_dev,
+                             void* dv_dev, int32_t grad_dtype, const int32_t* cu_seqlens_dev,
+                             const int32_t* prefix_len_dev, const int32_t* window_dev,
+                             int32_t nseq, int32_t total_tokens, int32_t num_heads,
+                             int32_t head_dim, int32_t max_seqlen, int32_t prefix_causal,
+                             float softmax_scale, void* stream) {
+  const rswa_status st = check_prefill(q_dev, k_dev, v_dev, out_dev, out_dtype, cu_seqlens_dev,
+                                       prefix_len_dev, window_dev, nseq, num_heads, head_dim,
+                                       max_seqlen, prefix_causal, softmax_scale);
+  if (st != RSWA_OK) return st;
+  if (!dout_dev || !lse_dev || !delta_dev)
+    return fail(RSWA_E_INVALID, "dout/lse/delta pointer is NULL");
+  if (!dq_dev || !dk_dev || !dv_dev) return fail(RSWA_E_INVALID, "dq/dk/dv pointer is NULL");
+  if (grad_dtype != RSWA_BF16 && grad_dtype != RSWA_F32)
+    return fail(RSWA_E_INVALID, "grad_dtype must be RSWA_BF16 or RSWA_F32");
+  if (total_tokens < 0) return fail(RSWA_E_INVALID, "total_tokens must be >= 0");
+  if (max_seqlen == 0 || total_tokens == 0) return RSWA_OK;
+  try {
+    const float scale = resolve_scale(softmax_scale, head_dim);
+    rswa::BwdArgs a{};
+    a.q = reinterpret_cast<const uint16_t*>(q_dev);
+    a.k = reinterpret_cast<const uint16_t*>(k_dev);
+    a.v = reinterpret_cast<const uint16_t*>(v_dev);
+    a.out = out_dev;
+    a.dout = reinterpret_cast<const uint16_t*>(dout_dev);
+    a.lse = lse_dev;
+    a.delta = delta_dev;
+    a.dq = dq_dev;
+    a.dk = dk_dev;
+    a.dv = dv_dev;
+    a.cu_seqlens = cu_seqlens_dev;
+    a.prefix_len = prefix_len_dev;
+    a.window = window_dev;
+    a.nseq = nseq;
+    a.heads = num_heads;
+    a.max_seqlen = max_seqlen;
+    a.prefix_causal = prefix_causal;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    const hipError_t e = rswa::launch_prefill_bwd(a, out_dtype == RSWA_F32, grad_dtype == RSWA_F32,
+                                                  total_tokens,
+                                                  reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "prefill backward launch");
+    return RSWA_OK;
+  } catch (...) {
+    return fail(RSWA_E_INTERNAL, "exception in rswa_prefill_bwd");
   }
 }
 

@@ -14,11 +14,13 @@ Recipe (per sequence b of workload `cfg`):
   rng = numpy.random.default_rng(SeedSequence([seed, cfg, b]))
   decode:  prefix K (m,H,D), prefix V (m,H,D), output K (T,H,D), output V (T,H,D), output Q (T,H,D)
   prefill: Q (S,H,D), K (S,H,D), V (S,H,D)
+  output gradient of a prefill workload: default_rng(SeedSequence([seed, cfg, 1000 + b])) draws
+    dO (S,H,D) the same way
   each drawn as standard_normal float32, in that order; then, if outliers are on, for each array in
   the same order a Bernoulli(p) set of positions is drawn as geometric gaps and those entries are
   multiplied by 8. Finally bf16 workloads round every value to nearest-even bf16.
-Per-workload metadata (page counts, lengths, windows of the ragged workload) comes from
-  default_rng(SeedSequence([seed, cfg])).
+Per-workload metadata (page counts, lengths, windows of the ragged workload and of the packed
+  training sequence) comes from default_rng(SeedSequence([seed, cfg])).
 """
 from __future__ import annotations
 
@@ -288,3 +290,42 @@ def prefill_config(seed: int = 0, *, S: int | None = None, prefix_len: int | Non
     n = 128 if window is None else window
     name = "R-SWA masked prefill, S=32768, m=10256 (40 pages), n=128, bf16"
     return make_prefill(name, 4, [S], [m], [n], seed=seed, prefix_causal=prefix_causal)
+
+
+def make_output_grad(wl: PrefillWorkload, seed: int = 0, cfg: int = 6) -> np.ndarray:
+    """Seeded bf16 output gradient dO [total][H][D] for a prefill workload (standard normal)."""
+    total = int(wl.cu_seqlens[-1])
+    H, D = NUM_HEADS, HEAD_DIM
+    g = np.empty((total, H, D), dtype=np.uint16)
+
+    def job(b):
+        rng = np.random.default_rng(np.random.SeedSequence([seed, cfg, 1000 + b]))
+        s0, s1 = int(wl.cu_seqlens[b]), int(wl.cu_seqlens[b + 1])
+        g[s0:s1] = bf16_bits(_draw(rng, (s1 - s0, H, D)))
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(job, range(wl.nseq)))
+    return g
+
+
+def packed_training_config(seed: int = 0, *, S: int = 32768, window: int = 128,
+                           out_per_page=(300, 700)) -> PrefillWorkload:
+    """One training row of S tokens packed with prefix + output documents (GeekNews "Unlimited
+    OCR", training section: single-page to multi-page documents 9:1, multi-page ones of 2 to 50
+    pages, packed to 32K). Documents are drawn until S is filled: 1 page with probability 0.9,
+    else a uniform page count in [2, 50]; prefix m = 256 pages + 16 prompt tokens; output length
+    pages x uniform integer in out_per_page (this library's choice: the pages give no per-page
+    output length). The last document is cut to fit S (its prefix too, if need be)."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 7]))
+    lens, ms = [], []
+    left = S
+    while left > 0:
+        pages = 1 if rng.random() < 0.9 else int(rng.integers(2, 51))
+        m = pages * TOKENS_PER_PAGE + PROMPT_TOKENS
+        outs = int(sum(rng.integers(out_per_page[0], out_per_page[1] + 1, size=pages)))
+        L = min(m + outs, left)
+        lens.append(L)
+        ms.append(min(m, L))
+        left -= L
+    name = f"packed training row, S={S}, {len(lens)} documents, n={window}, bf16"
+    return make_prefill(name, 7, lens, ms, [window] * len(lens), seed=seed)
