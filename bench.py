@@ -8,8 +8,9 @@ warmup steps t = 1..W, then K timed steps. Inputs for every step are resident in
 
 Also reported: per-step latency vs t, the decode kernel's algorithmic HBM GB/s against the 8 TB/s
 peak (HIP events around every decode launch on the launch stream), the multi-page growth curve
-(R-SWA vs full causal, --growth), the masked prefill in TFLOP/s against the bf16 MFMA peak, and the
-fp64 oracle timed on a bounded sample on the host cores (cpu_baseline).
+(R-SWA vs full causal, --growth), the masked prefill in TFLOP/s against the bf16 MFMA peak, the
+teacher-forced training pass (forward with log-sum-exp, then dQ / dK / dV) on the same 32K
+sequence, and the fp64 oracle timed on a bounded sample on the host cores (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -60,6 +61,7 @@ def parse():
     ap.add_argument("--grid", type=int, default=0, help="decode workgroups (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--growth", action="store_true", help="multi-page R-SWA vs full-causal curve")
     ap.add_argument("--kernel-events", action="store_true",
@@ -348,6 +350,61 @@ def run_prefill(args):
                                                            source_hash(PREFILL_SOURCES))))
 
 
+def run_backward(args):
+    """Training pass on the 32K prefill workload: forward with log-sum-exp, then the backward
+    (delta, dK/dV, dQ launches). Algorithmic FLOPs: 4 D per visible (query, key) pair and head
+    for the forward, 10 D for the backward (S = Q K^T, dP = dO V^T, dV, dK, dQ)."""
+    import torch
+    import windowed_attention_amd as wa
+    import workloads as W
+    pw = W.prefill_config()
+    g = W.make_output_grad(pw, seed=0)
+    q, k, v = upload(pw.q, "bf16"), upload(pw.k, "bf16"), upload(pw.v, "bf16")
+    dout = upload(g, "bf16")
+    cu = torch.tensor(pw.cu_seqlens, dtype=torch.int32, device="cuda")
+    m = torch.tensor(pw.prefix_len, dtype=torch.int32, device="cuda")
+    n = torch.tensor(pw.window, dtype=torch.int32, device="cuda")
+    S = int(pw.cu_seqlens[-1])
+    out = torch.empty((S, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((S, H), dtype=torch.float32, device="cuda")
+    delta = torch.empty((S, H), dtype=torch.float32, device="cuda")
+    grads = [torch.empty((S, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+
+    def fwd():
+        wa.rswa_prefill_fwd(q, k, v, cu, m, n, out=out, lse=lse, max_seqlen=S)
+
+    def bwd():
+        wa.rswa_prefill_bwd(q, k, v, out, dout, lse, cu, m, n, dq=grads[0], dk=grads[1],
+                            dv=grads[2], delta=delta, max_seqlen=S)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(args.prefill_runs):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        return float(np.median(times))
+
+    fwd()
+    fwd_ms = timed(fwd)
+    bwd_ms = timed(bwd)
+    pairs = visible_pairs(S, int(pw.prefix_len[0]), int(pw.window[0]))
+    bflop = 10.0 * D * H * pairs
+    tflops = bflop / (bwd_ms * 1e-3) / 1e12
+    train = (bflop + 4.0 * D * H * pairs) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12
+    return dict(workload=pw.name + ", forward + backward, bf16 gradients", fwd_ms=fwd_ms,
+                bwd_ms=bwd_ms, bwd_tflops=tflops, train_tflops=train, bwd_flop=bflop,
+                roofline=dict(bound="mfma", achieved=tflops, peak=PEAK_BF16_TFLOPS,
+                              unit="TFLOP/s", frac=tflops / PEAK_BF16_TFLOPS, traffic=None,
+                              kernel="backward call (delta + dK/dV + dQ launches)"))
+
+
 # ------------------------------------------------------------------------------------------------
 # cpu baseline: the fp64 oracle on a bounded sample
 # ------------------------------------------------------------------------------------------------
@@ -511,6 +568,11 @@ def main():
         if p is not None:
             res["prefill"] = p
             log(f"[bench] prefill: {p['ms']:.3f} ms, {p['tflops']:.1f} TFLOP/s")
+    if not args.no_backward:
+        bw = run_backward(args)
+        res["backward"] = bw
+        log(f"[bench] training pass: forward {bw['fwd_ms']:.3f} ms, backward {bw['bwd_ms']:.3f} ms "
+            f"({bw['bwd_tflops']:.1f} TFLOP/s), fwd+bwd {bw['train_tflops']:.1f} TFLOP/s")
     if wl is not None and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(res))

@@ -68,6 +68,81 @@ __device__ __forceinline__ const uint16_t* tr_base(const uint16_t* tile, int str
          4 * (lane & 3);
 }
 
+// 128-wide bf16 tile (rows of 256 bytes, no padding) whose 16-byte chunks are XOR-swizzled per row:
+// chunk c of row r is stored at chunk c ^ swz(r), swz(r) = 4 (r % 4) + (r / 4) % 4. The straight
+// 16-byte operand read (16 consecutive rows, one chunk) and the transposing read (4 consecutive rows
+// x 4 chunks) then both cover 16 distinct 16-byte bank groups of LDS's 256-byte bank row, so a
+// tile that is read both ways has no bank conflicts (a padded row stride serves only one of them).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// element offset of chunk c (8 bf16) of row r
+__device__ __forceinline__ int swz_chunk(int r, int c) { return r * kHeadDim + 8 * (c ^ swz(r)); }
+
+// Per-lane constants of the operand reads from a swizzled tile.
+struct SwzLane {
+  int a_off;  // straight read: row lq
+  int a_f;    // swz(lq % 16)
+  int a_half;
+  int t_off;  // transposing read: row j = (lane % 16) / 4 + 4 half, element 4 (lane % 2)
+  int t_f;    // swz(j)
+  int t_x;    // chunk within a 4-chunk column block: 2 ((lane / 16) % 2) + (lane % 4) / 2
+  __device__ __forceinline__ explicit SwzLane(int lane) {
+    const int lq = lane & 31, half = lane >> 5;
+    const int j = ((lane & 15) >> 2) + 4 * half;
+    a_off = lq * kHeadDim;
+    a_f = swz(lq & 15);
+    a_half = half;
+    t_off = j * kHeadDim + 4 * (lane & 1);
+    t_f = swz(j);
+    t_x = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  }
+};
+
+// Straight A operand (32 rows r0 .. r0 + 31, r0 a multiple of 16; columns 16 st .. 16 st + 15).
+__device__ __forceinline__ u32x4 swz_ld_a(const uint16_t* tile, const SwzLane& L, int r0, int st) {
+  return *reinterpret_cast<const u32x4*>(tile + r0 * kHeadDim + L.a_off +
+                                         8 * ((2 * st + L.a_half) ^ L.a_f));
+}
+
+// Transposed operand of ld_tr_op from a swizzled tile: columns 32 db + lane % 32, rows
+// r0 + 8 (e / 4) + 4 half + e % 4 (r0 a multiple of 16). Rows j + 8 have swz(j + 8) = swz(j) ^ 2.
+__device__ __forceinline__ u32x4 swz_ld_tr(const uint16_t* tile, const SwzLane& L, int r0, int db) {
+  const uint16_t* p = tile + r0 * kHeadDim + L.t_off;
+  const u32x2 lo = ld_tr(p + 8 * ((4 * db + L.t_x) ^ L.t_f));
+  const u32x2 hi = ld_tr(p + 8 * kHeadDim + 8 * ((4 * db + L.t_x) ^ L.t_f ^ 2));
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+
+// gfx950 LDS DMA (global_load_lds_dwordx4 / _dword): each lane copies 16 (4) bytes from its
+// global address straight into LDS, without passing through registers; the wave's pieces land
+// contiguously at `lds` (wave-uniform, placed in M0), lane L at byte 16 L (4 L). Completion is
+// counted by the wave's vector-memory counter and waited for with dma_wait_barrier. The loads are
+// issued from inline assembly so that the compiler, which cannot tell the DMA's LDS target from
+// the buffers being read, does not wait for every DMA in flight before each LDS read.
+__device__ __forceinline__ uint32_t lds_addr(const void* lds) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds);
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved; it is set right here
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr(lds))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_addr(lds))
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N of this wave's vector-memory loads are outstanding (loads complete in
+// issue order), then join the workgroup barrier. Written out because __syncthreads' fence would
+// also wait for the DMA loads issued for later tiles.
+template <int N>
+__device__ __forceinline__ void dma_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 template <typename OUT>
 __device__ __forceinline__ void store_out4(OUT* p, float a, float b, float c, float d);
 template <>

@@ -21,6 +21,8 @@
 //     V tiles of the prefix segment and the window segment through LDS, S^T = K Q^T,
 //     dP^T = V dO^T, dQ^T = K^T dS^T (K^T from the transposing read).
 // P and dS are rounded to bf16 for the MFMA products; every sum runs in float32.
+#include <type_traits>
+
 #include "kernels.h"
 #include "mfma.h"
 
@@ -68,63 +70,48 @@ __global__ __launch_bounds__(256) void delta_kernel(const OT* __restrict__ out,
 // ------------------------------------------------------------------------------------------
 // dK / dV: key-parallel
 // ------------------------------------------------------------------------------------------
+#ifndef RSWA_KV_SPLIT_MASK
+#define RSWA_KV_SPLIT_MASK 0  // 1: separate unmasked code for fully visible tiles
+#endif
 #ifndef RSWA_KV_WAVES
 #define RSWA_KV_WAVES 4  // waves per workgroup, 32 keys each
-#endif
-#ifndef RSWA_KV_QPAD
-#define RSWA_KV_QPAD 8   // bf16 pad per Q / dO tile row
 #endif
 constexpr int kKvWaves = RSWA_KV_WAVES;
 constexpr int kKvThreads = 64 * kKvWaves;
 constexpr int BNK = 32 * kKvWaves;                 // keys per workgroup
 constexpr int BMQ = 64;                            // queries per LDS tile
-constexpr int QSTR = kHeadDim + RSWA_KV_QPAD;      // Q / dO tile row stride (bf16)
-constexpr int Q_TILE = BMQ * QSTR;
-constexpr int kRowsPerThread = BMQ * 16 / kKvThreads;  // 16-byte pieces per thread per tensor
+constexpr int Q_TILE = BMQ * kHeadDim;             // swizzled Q / dO tile (bf16 elements)
 
-struct QTileRegs {
-  u32x4 q[kRowsPerThread];
-  u32x4 g[kRowsPerThread];
-  float aux;  // lse (threads < BMQ) or delta (threads BMQ .. 2 BMQ - 1)
-};
+constexpr int kGroupsPerWave = BMQ / 4 / kKvWaves;   // 4-row (1 KB) groups per wave
+constexpr int kKvPieces = 2 * kGroupsPerWave;         // 16-byte DMA loads per wave per tile
 
-__device__ __forceinline__ void load_qtile(QTileRegs& r, const uint16_t* qbase,
-                                           const uint16_t* gbase, const float* lse,
-                                           const float* delta, int64_t rs, int heads, int p0,
-                                           int pmax) {
-  const int t = threadIdx.x;
-  const int c = t & 15, rg = t >> 4;
+// Tile p0 .. p0 + 63 of Q and dO (rows clamped to pmax) and its lse / delta, copied by LDS DMA
+// into one buffer set. The lse / delta loads go first: with the 16-byte pieces issued after them,
+// "at most kKvPieces outstanding" then means every earlier tile has landed on every wave.
+__device__ __forceinline__ void dma_qtile(uint16_t* sq, uint16_t* sg, float* sl, float* sd,
+                                          const uint16_t* qbase, const uint16_t* gbase,
+                                          const float* lse, const float* dlt, int64_t rs,
+                                          int heads, int p0, int pmax, int wave, int lane) {
+  if (wave == 0) dma4(lse + (int64_t)min(p0 + lane, pmax) * heads, sl);
+  if (wave == 1) dma4(dlt + (int64_t)min(p0 + lane, pmax) * heads, sd);
 #pragma unroll
-  for (int u = 0; u < kRowsPerThread; ++u) {
-    const int p = min(p0 + rg * kRowsPerThread + u, pmax);
-    r.q[u] = *reinterpret_cast<const u32x4*>(qbase + p * rs + c * 8);
-    r.g[u] = *reinterpret_cast<const u32x4*>(gbase + p * rs + c * 8);
+  for (int u = 0; u < kGroupsPerWave; ++u) {
+    const int grp = wave * kGroupsPerWave + u;
+    const int row = 4 * grp + (lane >> 4);
+    const int c = (lane & 15) ^ swz(row);  // this lane's LDS slot holds chunk c of its row
+    const int64_t off = (int64_t)min(p0 + row, pmax) * rs + c * 8;
+    dma16(qbase + off, sq + grp * 4 * kHeadDim);
+    dma16(gbase + off, sg + grp * 4 * kHeadDim);
   }
-  if (t < 2 * BMQ) {
-    const int p = min(p0 + (t & (BMQ - 1)), pmax);
-    r.aux = t < BMQ ? lse[(int64_t)p * heads] * kLog2e : delta[(int64_t)p * heads];
-  }
-}
-
-__device__ __forceinline__ void store_qtile(const QTileRegs& r, uint16_t* sq, uint16_t* sg,
-                                            float* sl, float* sd) {
-  const int t = threadIdx.x;
-  const int c = t & 15, rg = t >> 4;
-#pragma unroll
-  for (int u = 0; u < kRowsPerThread; ++u) {
-    *reinterpret_cast<u32x4*>(sq + (rg * kRowsPerThread + u) * QSTR + c * 8) = r.q[u];
-    *reinterpret_cast<u32x4*>(sg + (rg * kRowsPerThread + u) * QSTR + c * 8) = r.g[u];
-  }
-  if (t < BMQ) sl[t] = r.aux;
-  else if (t < 2 * BMQ) sd[t - BMQ] = r.aux;
 }
 
 template <typename OUT>
 __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2 * Q_TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sG[2 * Q_TILE];
-  __shared__ __attribute__((aligned(16))) float sL[2 * BMQ];
-  __shared__ __attribute__((aligned(16))) float sD[2 * BMQ];
+  // three buffer sets: the DMA for tile j + 2 runs while tile j is computed
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[3 * Q_TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sG[3 * Q_TILE];
+  __shared__ __attribute__((aligned(16))) float sL[3 * BMQ];
+  __shared__ __attribute__((aligned(16))) float sD[3 * BMQ];
 
   // key blocks outermost across heads: the prefix blocks (long query loops) start first
   const int idx = blockIdx.x;
@@ -139,7 +126,11 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
   const int n = a.window[s];
   const bool pc = a.prefix_causal != 0;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform: readfirstlane lets the compiler keep every per-wave decision
+  // (which query blocks the wave's keys see, whether a tile needs the element mask) in scalar
+  // registers and branch on it instead of masking lanes
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, half = lane >> 5;
   const int64_t rs = (int64_t)a.heads * kHeadDim;
   const int64_t hoff = ((int64_t)cu0 * a.heads + h) * kHeadDim;
@@ -159,6 +150,10 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
       kf[st] = *reinterpret_cast<const u32x4*>(a.k + hoff + kc * rs + st * 16 + half * 8);
       vf[st] = *reinterpret_cast<const u32x4*>(a.v + hoff + kc * rs + st * 16 + half * 8);
     }
+    // Materialise the operands here: the compiler then waits for these loads once, before the
+    // loop, instead of inside it, where its wait would also cover the tile DMA in flight.
+#pragma unroll
+    for (int st = 0; st < 8; ++st) asm volatile("" : "+v"(kf[st]), "+v"(vf[st]));
   }
   // queries that see key kw: [plo, phi)
   int plo, phi;
@@ -194,85 +189,123 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
     zero16(dv[db]);
   }
 
-  const uint16_t* qtr = tr_base(sQ, QSTR, lane);
-  const uint16_t* gtr = tr_base(sG, QSTR, lane);
+  const SwzLane sl_(lane);
 
-  QTileRegs regs;
-  load_qtile(regs, qbase, gbase, lse, dlt, rs, a.heads, qlo, S - 1);
-  store_qtile(regs, sQ, sG, sL, sD);
-  if (ntiles > 1) load_qtile(regs, qbase, gbase, lse, dlt, rs, a.heads, qlo + BMQ, S - 1);
-  __syncthreads();
+  auto issue = [&](int j) {
+    const int b = j % 3;
+    dma_qtile(sQ + b * Q_TILE, sG + b * Q_TILE, sL + b * BMQ, sD + b * BMQ, qbase, gbase, lse,
+              dlt, rs, a.heads, qlo + j * BMQ, S - 1, wave, lane);
+  };
+  issue(0);
+  if (ntiles > 1) {
+    issue(1);
+    dma_wait_barrier<kKvPieces>();
+  } else {
+    dma_wait_barrier<0>();
+  }
+
+  // One 32-query block of the tile in LDS buffers (sq, sg, sl, sd): S = Q K^T and dP = dO V^T
+  // (queries in accumulator rows, this lane's key in the column), P and dS in registers, then
+  // dV^T += dO^T P and dK^T += Q^T dS. Every LDS operand is requested ahead of the MFMA that
+  // uses it: the sixteen straight fragments and lse / delta before the score chain, the sixteen
+  // transposed fragments while it runs, so one wave per SIMD runs at LDS throughput rather than
+  // LDS latency. MASKED selects the element mask (a uniform choice per wave and tile).
+  auto qblock = [&](auto masked_c, const uint16_t* sq, const uint16_t* sg, const float* sl,
+                    const float* sd, int qb, int pb0) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    __builtin_amdgcn_sched_barrier(0);  // blocks do not interleave: registers stay bounded
+    u32x4 af[16];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      af[2 * st] = swz_ld_a(sq, sl_, qb * 32, st);
+      af[2 * st + 1] = swz_ld_a(sg, sl_, qb * 32, st);
+    }
+    float4 l4[4], d4[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      l4[g] = *reinterpret_cast<const float4*>(sl + qb * 32 + 8 * g + 4 * half);
+      d4[g] = *reinterpret_cast<const float4*>(sd + qb * 32 + 8 * g + 4 * half);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    floatx16 sacc, dpacc;
+    zero16(sacc);
+    zero16(dpacc);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      sacc = mfma32(af[2 * st], kf[st], sacc);
+      dpacc = mfma32(af[2 * st + 1], vf[st], dpacc);
+    }
+    // the transposed reads go out once the score MFMAs are issued (the straight fragments are
+    // then dead) and arrive while the softmax waits for the scores
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 tg[8], tq[8];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        tg[2 * db + st] = swz_ld_tr(sg, sl_, qb * 32 + 16 * st, db);
+        tq[2 * db + st] = swz_ld_tr(sq, sl_, qb * 32 + 16 * st, db);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    // accumulator register r: query pb0 + 8 (r / 4) + 4 half + r % 4, key kw; visible iff the
+    // query lies in [plo, phi), tested as one unsigned range check
+    const uint32_t p_rel = (uint32_t)(pb0 + 4 * half - plo);
+    const uint32_t p_width = (uint32_t)(phi - plo);
+    float pr[16], ds[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float lv[4] = {l4[g].x, l4[g].y, l4[g].z, l4[g].w};
+      const float dv4[4] = {d4[g].x, d4[g].y, d4[g].z, d4[g].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        float x = fast_exp2(fmaf(sacc[r], c, -lv[i] * kLog2e));
+        if constexpr (MASKED) x = (p_rel + (uint32_t)(8 * g + i) < p_width) ? x : 0.f;
+        pr[r] = x;
+        ds[r] = x * (dpacc[r] - dv4[i]);
+      }
+    }
+    const u32x4 pb[2] = {pack_b(pr, 0), pack_b(pr, 1)};
+    const u32x4 sb[2] = {pack_b(ds, 0), pack_b(ds, 1)};
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        dv[db] = mfma32(tg[2 * db + st], pb[st], dv[db]);
+        dk[db] = mfma32(tq[2 * db + st], sb[st], dk[db]);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
   for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
+    const int buf = j % 3;
     const int qt0 = qlo + j * BMQ;
+    if (j + 2 < ntiles) issue(j + 2);
     const uint16_t* sq = sQ + buf * Q_TILE;
     const uint16_t* sg = sG + buf * Q_TILE;
     const float* sl = sL + buf * BMQ;
     const float* sd = sD + buf * BMQ;
+#if RSWA_KV_SPLIT_MASK
+    // uniform per wave: every pair of the tile visible, or blocks the wave's keys never see
     const bool full = wave_pre && qt0 + BMQ <= S && (!pc || qt0 >= wk0 + 31);
+    if (full) {
+      qblock(std::false_type{}, sq, sg, sl, sd, 0, qt0);
+      qblock(std::false_type{}, sq, sg, sl, sd, 1, qt0 + 32);
+    } else
+#endif
+    {
 #pragma unroll
-    for (int qb = 0; qb < BMQ / 32; ++qb) {
-      const int pb0 = qt0 + qb * 32;
-      if (pb0 >= wq_hi || pb0 + 32 <= wq_lo) continue;  // wave-uniform
-      floatx16 sacc, dpacc;
-      zero16(sacc);
-      zero16(dpacc);
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const u32x4 qa =
-            *reinterpret_cast<const u32x4*>(sq + (qb * 32 + lq) * QSTR + st * 16 + half * 8);
-        sacc = mfma32(qa, kf[st], sacc);
+      for (int qb = 0; qb < BMQ / 32; ++qb) {
+        const int pb0 = qt0 + qb * 32;
+        // uniform per wave: skip blocks that none of the wave's keys can see
+        if (pb0 < wq_hi && pb0 + 32 > wq_lo) qblock(std::true_type{}, sq, sg, sl, sd, qb, pb0);
       }
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const u32x4 ga =
-            *reinterpret_cast<const u32x4*>(sg + (qb * 32 + lq) * QSTR + st * 16 + half * 8);
-        dpacc = mfma32(ga, vf[st], dpacc);
-      }
-      // accumulator register r: query pb0 + 8 (r / 4) + 4 half + r % 4, key kw
-      float pr[16], ds[16];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 l4 = *reinterpret_cast<const float4*>(sl + qb * 32 + 8 * g + 4 * half);
-        const float4 d4 = *reinterpret_cast<const float4*>(sd + qb * 32 + 8 * g + 4 * half);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * g + i;
-          float x = fast_exp2(fmaf(sacc[r], c, -lv[i]));
-          if (!full) {
-            const int p = pb0 + 8 * g + 4 * half + i;
-            x = (p >= plo && p < phi) ? x : 0.f;
-          }
-          pr[r] = x;
-          ds[r] = x * (dpacc[r] - dv4[i]);
-        }
-      }
-      const u32x4 pb[2] = {pack_b(pr, 0), pack_b(pr, 1)};
-      const u32x4 sb[2] = {pack_b(ds, 0), pack_b(ds, 1)};
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const u32x4 ga = ld_tr_op(gtr + buf * Q_TILE, QSTR, qb * 32 + 16 * st, db * 32);
-          dv[db] = mfma32(ga, pb[st], dv[db]);
-        }
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const u32x4 qa = ld_tr_op(qtr + buf * Q_TILE, QSTR, qb * 32 + 16 * st, db * 32);
-          dk[db] = mfma32(qa, sb[st], dk[db]);
-        }
     }
-    if (j + 1 < ntiles)
-      store_qtile(regs, sQ + (buf ^ 1) * Q_TILE, sG + (buf ^ 1) * Q_TILE, sL + (buf ^ 1) * BMQ,
-                  sD + (buf ^ 1) * BMQ);
+    // tile j + 1 must have landed; tile j + 2's pieces may still be in flight
     if (j + 2 < ntiles)
-      load_qtile(regs, qbase, gbase, lse, dlt, rs, a.heads, qlo + (j + 2) * BMQ, S - 1);
-    __syncthreads();
+      dma_wait_barrier<kKvPieces>();
+    else
+      dma_wait_barrier<0>();
   }
 
   if (kw < S) {
@@ -285,51 +318,41 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
 // ------------------------------------------------------------------------------------------
 // dQ: query-parallel (the forward's key schedule)
 // ------------------------------------------------------------------------------------------
+#ifndef RSWA_DQ_SCHED
+#define RSWA_DQ_SCHED 0  // > 0: fragment reads kept this far ahead of the score MFMAs
+#endif
 #ifndef RSWA_DQ_WAVES
 #define RSWA_DQ_WAVES 8  // waves per workgroup, 32 queries each
-#endif
-#ifndef RSWA_DQ_KPAD
-#define RSWA_DQ_KPAD 8   // bf16 pad per K / V tile row
 #endif
 constexpr int kDqWaves = RSWA_DQ_WAVES;
 constexpr int kDqThreads = 64 * kDqWaves;
 constexpr int BNQ = 32 * kDqWaves;                  // queries per workgroup
 constexpr int BN = 64;                              // keys per tile
-constexpr int KSTR = kHeadDim + RSWA_DQ_KPAD;
-constexpr int K_TILE = BN * KSTR;
-constexpr int kKeyPieces = BN * 16 / kDqThreads;    // 16-byte pieces per thread per tensor
+constexpr int K_TILE = BN * kHeadDim;               // swizzled K / V tile (bf16 elements)
 
-struct KTileRegs {
-  u32x4 k[kKeyPieces];
-  u32x4 v[kKeyPieces];
-};
+constexpr int kKeyGroupsPerWave = BN / 4 / kDqWaves;  // 4-row (1 KB) groups per wave
+constexpr int kDqPieces = 2 * kKeyGroupsPerWave;       // 16-byte DMA loads per wave per tile
 
-__device__ __forceinline__ void load_ktile(KTileRegs& r, const uint16_t* kbase,
-                                           const uint16_t* vbase, int64_t rs, int k0, int kmax) {
-  const int t = threadIdx.x;
-  const int c = t & 15, kg = t >> 4;
+// Keys k0 .. k0 + 63 of K and V (rows clamped to kmax) copied by LDS DMA into one buffer pair.
+__device__ __forceinline__ void dma_ktile(uint16_t* sk, uint16_t* sv, const uint16_t* kbase,
+                                          const uint16_t* vbase, int64_t rs, int k0, int kmax,
+                                          int wave, int lane) {
 #pragma unroll
-  for (int u = 0; u < kKeyPieces; ++u) {
-    const int key = min(k0 + kg * kKeyPieces + u, kmax);
-    r.k[u] = *reinterpret_cast<const u32x4*>(kbase + key * rs + c * 8);
-    r.v[u] = *reinterpret_cast<const u32x4*>(vbase + key * rs + c * 8);
-  }
-}
-
-__device__ __forceinline__ void store_ktile(const KTileRegs& r, uint16_t* sk, uint16_t* sv) {
-  const int t = threadIdx.x;
-  const int c = t & 15, kg = t >> 4;
-#pragma unroll
-  for (int u = 0; u < kKeyPieces; ++u) {
-    *reinterpret_cast<u32x4*>(sk + (kg * kKeyPieces + u) * KSTR + c * 8) = r.k[u];
-    *reinterpret_cast<u32x4*>(sv + (kg * kKeyPieces + u) * KSTR + c * 8) = r.v[u];
+  for (int u = 0; u < kKeyGroupsPerWave; ++u) {
+    const int grp = wave * kKeyGroupsPerWave + u;
+    const int row = 4 * grp + (lane >> 4);
+    const int c = (lane & 15) ^ swz(row);
+    const int64_t off = (int64_t)min(k0 + row, kmax) * rs + c * 8;
+    dma16(kbase + off, sk + grp * 4 * kHeadDim);
+    dma16(vbase + off, sv + grp * 4 * kHeadDim);
   }
 }
 
 template <typename OUT>
 __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2 * K_TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2 * K_TILE];
+  // three buffer pairs: the DMA for tile j + 2 runs while tile j is computed
+  __shared__ __attribute__((aligned(16))) uint16_t sK[3 * K_TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[3 * K_TILE];
 
   const int s = blockIdx.z, h = blockIdx.y;
   const int cu0 = a.cu_seqlens[s];
@@ -341,7 +364,8 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
   const int n = a.window[s];
   const bool pc = a.prefix_causal != 0;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, half = lane >> 5;
   const int64_t rs = (int64_t)a.heads * kHeadDim;
   const int64_t hoff = ((int64_t)cu0 * a.heads + h) * kHeadDim;
@@ -358,8 +382,13 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
     gf[st] = *reinterpret_cast<const u32x4*>(a.dout + hoff + pq * rs + st * 16 + half * 8);
   }
   const int64_t prow = (int64_t)(cu0 + pq) * a.heads + h;
-  const float lse2 = a.lse[prow] * kLog2e;
-  const float dlt = a.delta[prow];
+  float lse2 = a.lse[prow] * kLog2e;
+  float dlt = a.delta[prow];
+  // Materialise the operands here: the compiler then waits for these loads once, before the
+  // loop, instead of inside it, where its wait would also cover the tile DMA in flight.
+#pragma unroll
+  for (int st = 0; st < 8; ++st) asm volatile("" : "+v"(qf[st]), "+v"(gf[st]));
+  asm volatile("" : "+v"(lse2), "+v"(dlt));
 
   // key tiles: the prefix segment, then the output window segment (as in the forward)
   const int pre_end = (pc && q1 <= m) ? q1 : m;
@@ -378,63 +407,90 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
   floatx16 dq[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) zero16(dq[db]);
-  const uint16_t* ktr = tr_base(sK, KSTR, lane);
+  const SwzLane sl_(lane);
 
-  KTileRegs regs;
-  load_ktile(regs, kbase, vbase, rs, tstart(0), S - 1);
-  store_ktile(regs, sK, sV);
-  if (ntiles > 1) load_ktile(regs, kbase, vbase, rs, tstart(1), S - 1);
-  __syncthreads();
+  auto issue = [&](int j) {
+    const int b = j % 3;
+    dma_ktile(sK + b * K_TILE, sV + b * K_TILE, kbase, vbase, rs, tstart(j), S - 1, wave, lane);
+  };
+  issue(0);
+  if (ntiles > 1) {
+    issue(1);
+    dma_wait_barrier<kDqPieces>();
+  } else {
+    dma_wait_barrier<0>();
+  }
+
+  // One 32-key block of the tile in LDS buffers (sk, sv): S^T = K Q^T and dP^T = V dO^T (keys in
+  // accumulator rows, this lane's query in the column), dS^T in registers, dQ^T += K^T dS^T.
+  // MASKED selects the element mask, a uniform choice per tile; a key is visible iff it lies in
+  // [lo, hi], tested as one unsigned range check.
+  auto kblock = [&](auto masked_c, const uint16_t* sk, const uint16_t* sv, int kb, int k0, int lo,
+                    int hi) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    __builtin_amdgcn_sched_barrier(0);  // blocks do not interleave: registers stay bounded
+    floatx16 sacc, dpacc;
+    zero16(sacc);
+    zero16(dpacc);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const u32x4 ka = swz_ld_a(sk, sl_, kb * 32, st);
+      sacc = mfma32(ka, qf[st], sacc);
+    }
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const u32x4 va = swz_ld_a(sv, sl_, kb * 32, st);
+      dpacc = mfma32(va, gf[st], dpacc);
+    }
+#if RSWA_DQ_SCHED
+    // keep RSWA_DQ_SCHED fragment reads in flight ahead of the score chains
+    __builtin_amdgcn_sched_group_barrier(0x100, RSWA_DQ_SCHED, 0);
+#pragma unroll
+    for (int i = 0; i < 16 - RSWA_DQ_SCHED; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, RSWA_DQ_SCHED, 0);
+#endif
+    // accumulator register r: key k0 + kb*32 + 8 (r / 4) + 4 half + r % 4, query p
+    const uint32_t k_rel = (uint32_t)(k0 + kb * 32 + 4 * half - lo);
+    const uint32_t k_width = (uint32_t)max(hi - lo + 1, 0);
+    float ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = fast_exp2(fmaf(sacc[r], c, -lse2));
+      if constexpr (MASKED) x = (k_rel + (uint32_t)(8 * (r >> 2) + (r & 3)) < k_width) ? x : 0.f;
+      ds[r] = x * (dpacc[r] - dlt);
+    }
+    const u32x4 sb[2] = {pack_b(ds, 0), pack_b(ds, 1)};
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const u32x4 ka = swz_ld_tr(sk, sl_, kb * 32 + 16 * st, db);
+        dq[db] = mfma32(ka, sb[st], dq[db]);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
   for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
+    const int buf = j % 3;
+    if (j + 2 < ntiles) issue(j + 2);
     const uint16_t* sk = sK + buf * K_TILE;
     const uint16_t* sv = sV + buf * K_TILE;
     const int k0 = tstart(j);
     const bool is_pre = j < n_pre;
-    const bool need_mask = is_pre ? (k0 + BN > m || (pc && q0 < m && k0 + BN - 1 > q0)) : true;
+    // The element mask is applied to every tile (three vector ALU operations per score): a
+    // separate unmasked copy of the block code doubles the live ranges the register allocator
+    // sees and spills.
     const int lo = is_pre ? 0 : win_lo;
     const int hi = is_pre ? pre_hi : p;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      floatx16 sacc, dpacc;
-      zero16(sacc);
-      zero16(dpacc);
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const u32x4 ka =
-            *reinterpret_cast<const u32x4*>(sk + (kb * 32 + lq) * KSTR + st * 16 + half * 8);
-        sacc = mfma32(ka, qf[st], sacc);
-      }
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const u32x4 va =
-            *reinterpret_cast<const u32x4*>(sv + (kb * 32 + lq) * KSTR + st * 16 + half * 8);
-        dpacc = mfma32(va, gf[st], dpacc);
-      }
-      // accumulator register r: key k0 + kb*32 + 8 (r / 4) + 4 half + r % 4, query p
-      float ds[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = fast_exp2(fmaf(sacc[r], c, -lse2));
-        if (need_mask) {
-          const int k = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          x = (k >= lo && k <= hi) ? x : 0.f;
-        }
-        ds[r] = x * (dpacc[r] - dlt);
-      }
-      const u32x4 sb[2] = {pack_b(ds, 0), pack_b(ds, 1)};
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const u32x4 ka = ld_tr_op(ktr + buf * K_TILE, KSTR, kb * 32 + 16 * st, db * 32);
-          dq[db] = mfma32(ka, sb[st], dq[db]);
-        }
-    }
-    if (j + 1 < ntiles) store_ktile(regs, sK + (buf ^ 1) * K_TILE, sV + (buf ^ 1) * K_TILE);
-    if (j + 2 < ntiles) load_ktile(regs, kbase, vbase, rs, tstart(j + 2), S - 1);
-    __syncthreads();
+    kblock(std::true_type{}, sk, sv, 0, k0, lo, hi);
+    kblock(std::true_type{}, sk, sv, 1, k0, lo, hi);
+    if (j + 2 < ntiles)
+      dma_wait_barrier<kDqPieces>();
+    else
+      dma_wait_barrier<0>();
   }
 
   if (p < q1)
