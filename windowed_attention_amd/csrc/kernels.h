@@ -84,7 +84,8 @@ struct BwdArgs {
   const void* out;          // [total][H][D] forward output (bf16 or float32)
   const uint16_t* dout;     // [total][H][D] bf16 gradient of the output
   const float* lse;         // [total][H] natural log-sum-exp from the forward
-  float* delta;             // [total][H] written: rowsum(dout * out)
+  float* work;              // [2][total][H] written: lse * log2(e), then rowsum(dout * out)
+  int64_t rows;             // total * H
   void* dq;                 // [total][H][D] gradients (bf16 or float32)
   void* dk;
   void* dv;
@@ -105,8 +106,7 @@ hipError_t launch_append(const AppendArgs& a, int batch, int kv_f32, hipStream_t
 hipError_t launch_decode(const DecodeArgs& a, int kv_f32, int out_f32, int grid_blocks,
                          bool need_merge, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int out_f32, hipStream_t s);
-hipError_t launch_prefill_bwd(const BwdArgs& a, int out_f32, int grad_f32, int64_t total,
-                              hipStream_t s);
+hipError_t launch_prefill_bwd(const BwdArgs& a, int out_f32, int grad_f32, hipStream_t s);
 // Resident 256-thread decode workgroups per CU (occupancy of the decode kernel for a batch of B).
 int decode_blocks_per_cu(int kv_f32, int out_f32, int batch);
 size_t decode_lds_bytes(int batch);

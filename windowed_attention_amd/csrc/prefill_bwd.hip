@@ -11,7 +11,8 @@
 // log2 e, so no softmax state is kept between the passes.
 //
 // Three kernels, no atomics and no partial sums:
-//   delta: one 16-lane group per (token, head) row, HBM-bound.
+//   delta: one 16-lane group per (token, head) row, HBM-bound; it also stores lse in the log2
+//     domain next to delta in the caller's work array.
 //   dK/dV: key-parallel. A workgroup owns 32 keys per wave; the wave keeps K and V of its keys in
 //     registers (B operands) and its dK^T, dV^T accumulators in registers, and streams the query
 //     tiles that can see its keys (every query for a prefix key, the n queries of the window for
@@ -21,8 +22,6 @@
 //     V tiles of the prefix segment and the window segment through LDS, S^T = K Q^T,
 //     dP^T = V dO^T, dQ^T = K^T dS^T (K^T from the transposing read).
 // P and dS are rounded to bf16 for the MFMA products; every sum runs in float32.
-#include <type_traits>
-
 #include "kernels.h"
 #include "mfma.h"
 
@@ -50,10 +49,13 @@ __device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8]) {
   }
 }
 
+// Also converts the forward's natural-log lse to the log2 domain the other kernels use:
+// work[0][row] = lse * log2(e), work[1][row] = delta.
 template <typename OT>
 __global__ __launch_bounds__(256) void delta_kernel(const OT* __restrict__ out,
                                                     const uint16_t* __restrict__ dout,
-                                                    float* __restrict__ delta, int64_t rows) {
+                                                    const float* __restrict__ lse,
+                                                    float* __restrict__ work, int64_t rows) {
   const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int c = threadIdx.x & 15;
   const int64_t rr = row < rows ? row : rows - 1;
@@ -64,15 +66,15 @@ __global__ __launch_bounds__(256) void delta_kernel(const OT* __restrict__ out,
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc = fmaf(o[i], g[i], acc);
   acc = row16_sum(acc);
-  if (c == 0 && row < rows) delta[row] = acc;
+  if (row < rows) {
+    if (c == 0) work[rows + row] = acc;
+    if (c == 1) work[row] = lse[row] * kLog2e;
+  }
 }
 
 // ------------------------------------------------------------------------------------------
 // dK / dV: key-parallel
 // ------------------------------------------------------------------------------------------
-#ifndef RSWA_KV_SPLIT_MASK
-#define RSWA_KV_SPLIT_MASK 0  // 1: separate unmasked code for fully visible tiles
-#endif
 #ifndef RSWA_KV_WAVES
 #define RSWA_KV_WAVES 4  // waves per workgroup, 32 keys each
 #endif
@@ -136,8 +138,8 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
   const int64_t hoff = ((int64_t)cu0 * a.heads + h) * kHeadDim;
   const uint16_t* qbase = a.q + hoff;
   const uint16_t* gbase = a.dout + hoff;
-  const float* lse = a.lse + (int64_t)cu0 * a.heads + h;
-  const float* dlt = a.delta + (int64_t)cu0 * a.heads + h;
+  const float* lse = a.work + (int64_t)cu0 * a.heads + h;           // lse * log2(e)
+  const float* dlt = a.work + a.rows + (int64_t)cu0 * a.heads + h;  // delta
 
   // this lane's key and its K / V rows as B operands (8 d-steps of 16)
   const int wk0 = k0 + wave * 32;
@@ -177,9 +179,6 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
   const int qlo = k0 < m ? (pc ? k0 : 0) : k0;
   const int qhi = k0 < m ? S : min(S, klast + n);
   const int ntiles = (qhi - qlo + BMQ - 1) / BMQ;
-  // every (query, key) pair of a tile is visible when all the wave's keys are prefix keys and,
-  // with a causal prefix, the tile's first query is at or after the wave's last key
-  const bool wave_pre = wk0 + 32 <= min(m, S);
 
   const float c = a.scale_log2;
   floatx16 dk[4], dv[4];
@@ -209,10 +208,10 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
   // dV^T += dO^T P and dK^T += Q^T dS. Every LDS operand is requested ahead of the MFMA that
   // uses it: the sixteen straight fragments and lse / delta before the score chain, the sixteen
   // transposed fragments while it runs, so one wave per SIMD runs at LDS throughput rather than
-  // LDS latency. MASKED selects the element mask (a uniform choice per wave and tile).
-  auto qblock = [&](auto masked_c, const uint16_t* sq, const uint16_t* sg, const float* sl,
+  // LDS latency. A query is visible to this lane's key iff it lies in [plo, phi), tested as one
+  // unsigned range check.
+  auto qblock = [&](const uint16_t* sq, const uint16_t* sg, const float* sl,
                     const float* sd, int qb, int pb0) {
-    constexpr bool MASKED = decltype(masked_c)::value;
     __builtin_amdgcn_sched_barrier(0);  // blocks do not interleave: registers stay bounded
     u32x4 af[16];
 #pragma unroll
@@ -247,8 +246,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
         tq[2 * db + st] = swz_ld_tr(sq, sl_, qb * 32 + 16 * st, db);
       }
     __builtin_amdgcn_sched_barrier(0);
-    // accumulator register r: query pb0 + 8 (r / 4) + 4 half + r % 4, key kw; visible iff the
-    // query lies in [plo, phi), tested as one unsigned range check
+    // accumulator register r: query pb0 + 8 (r / 4) + 4 half + r % 4, key kw
     const uint32_t p_rel = (uint32_t)(pb0 + 4 * half - plo);
     const uint32_t p_width = (uint32_t)(phi - plo);
     float pr[16], ds[16];
@@ -259,8 +257,8 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * g + i;
-        float x = fast_exp2(fmaf(sacc[r], c, -lv[i] * kLog2e));
-        if constexpr (MASKED) x = (p_rel + (uint32_t)(8 * g + i) < p_width) ? x : 0.f;
+        float x = fast_exp2(fmaf(sacc[r], c, -lv[i]));
+        x = (p_rel + (uint32_t)(8 * g + i) < p_width) ? x : 0.f;
         pr[r] = x;
         ds[r] = x * (dpacc[r] - dv4[i]);
       }
@@ -285,20 +283,14 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
     const uint16_t* sg = sG + buf * Q_TILE;
     const float* sl = sL + buf * BMQ;
     const float* sd = sD + buf * BMQ;
-#if RSWA_KV_SPLIT_MASK
-    // uniform per wave: every pair of the tile visible, or blocks the wave's keys never see
-    const bool full = wave_pre && qt0 + BMQ <= S && (!pc || qt0 >= wk0 + 31);
-    if (full) {
-      qblock(std::false_type{}, sq, sg, sl, sd, 0, qt0);
-      qblock(std::false_type{}, sq, sg, sl, sd, 1, qt0 + 32);
-    } else
-#endif
+    // The element mask is applied to every block (three vector ALU operations per score): a
+    // separate unmasked copy of the block code doubles the live ranges and spills.
     {
 #pragma unroll
       for (int qb = 0; qb < BMQ / 32; ++qb) {
         const int pb0 = qt0 + qb * 32;
         // uniform per wave: skip blocks that none of the wave's keys can see
-        if (pb0 < wq_hi && pb0 + 32 > wq_lo) qblock(std::true_type{}, sq, sg, sl, sd, qb, pb0);
+        if (pb0 < wq_hi && pb0 + 32 > wq_lo) qblock(sq, sg, sl, sd, qb, pb0);
       }
     }
     // tile j + 1 must have landed; tile j + 2's pieces may still be in flight
@@ -382,8 +374,8 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
     gf[st] = *reinterpret_cast<const u32x4*>(a.dout + hoff + pq * rs + st * 16 + half * 8);
   }
   const int64_t prow = (int64_t)(cu0 + pq) * a.heads + h;
-  float lse2 = a.lse[prow] * kLog2e;
-  float dlt = a.delta[prow];
+  float lse2 = a.work[prow];
+  float dlt = a.work[a.rows + prow];
   // Materialise the operands here: the compiler then waits for these loads once, before the
   // loop, instead of inside it, where its wait would also cover the tile DMA in flight.
 #pragma unroll
@@ -423,11 +415,9 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
 
   // One 32-key block of the tile in LDS buffers (sk, sv): S^T = K Q^T and dP^T = V dO^T (keys in
   // accumulator rows, this lane's query in the column), dS^T in registers, dQ^T += K^T dS^T.
-  // MASKED selects the element mask, a uniform choice per tile; a key is visible iff it lies in
-  // [lo, hi], tested as one unsigned range check.
-  auto kblock = [&](auto masked_c, const uint16_t* sk, const uint16_t* sv, int kb, int k0, int lo,
+  // A key is visible iff it lies in [lo, hi], tested as one unsigned range check.
+  auto kblock = [&](const uint16_t* sk, const uint16_t* sv, int kb, int k0, int lo,
                     int hi) {
-    constexpr bool MASKED = decltype(masked_c)::value;
     __builtin_amdgcn_sched_barrier(0);  // blocks do not interleave: registers stay bounded
     floatx16 sacc, dpacc;
     zero16(sacc);
@@ -459,7 +449,7 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float x = fast_exp2(fmaf(sacc[r], c, -lse2));
-      if constexpr (MASKED) x = (k_rel + (uint32_t)(8 * (r >> 2) + (r & 3)) < k_width) ? x : 0.f;
+      x = (k_rel + (uint32_t)(8 * (r >> 2) + (r & 3)) < k_width) ? x : 0.f;
       ds[r] = x * (dpacc[r] - dlt);
     }
     const u32x4 sb[2] = {pack_b(ds, 0), pack_b(ds, 1)};
@@ -485,8 +475,8 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
     // sees and spills.
     const int lo = is_pre ? 0 : win_lo;
     const int hi = is_pre ? pre_hi : p;
-    kblock(std::true_type{}, sk, sv, 0, k0, lo, hi);
-    kblock(std::true_type{}, sk, sv, 1, k0, lo, hi);
+    kblock(sk, sv, 0, k0, lo, hi);
+    kblock(sk, sv, 1, k0, lo, hi);
     if (j + 2 < ntiles)
       dma_wait_barrier<kDqPieces>();
     else
@@ -500,30 +490,30 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
 
 }  // namespace
 
-hipError_t launch_prefill_bwd(const BwdArgs& a, int out_f32, int grad_f32, int64_t total,
-                              hipStream_t s) {
-  const int64_t rows = total * a.heads;
+hipError_t launch_prefill_bwd(const BwdArgs& a, int out_f32, int grad_f32, hipStream_t s) {
+  const int64_t rows = a.rows;
   if (rows > 0) {
     const dim3 g((unsigned)((rows + 15) / 16));
     if (out_f32)
       hipLaunchKernelGGL(delta_kernel<float>, g, dim3(256), 0, s,
-                         reinterpret_cast<const float*>(a.out), a.dout, a.delta, rows);
+                         reinterpret_cast<const float*>(a.out), a.dout, a.lse, a.work, rows);
     else
       hipLaunchKernelGGL(delta_kernel<uint16_t>, g, dim3(256), 0, s,
-                         reinterpret_cast<const uint16_t*>(a.out), a.dout, a.delta, rows);
+                         reinterpret_cast<const uint16_t*>(a.out), a.dout, a.lse, a.work, rows);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  const dim3 gq((a.max_seqlen + BNQ - 1) / BNQ, a.heads, a.nseq);
   const int nkb = (a.max_seqlen + BNK - 1) / BNK;
   const dim3 gkv((unsigned)nkb * a.heads * a.nseq);
-  const dim3 gq((a.max_seqlen + BNQ - 1) / BNQ, a.heads, a.nseq);
-  if (grad_f32) {
+  if (grad_f32)
     hipLaunchKernelGGL(dkdv_kernel<float>, gkv, dim3(kKvThreads), 0, s, a, nkb);
-    hipLaunchKernelGGL(dq_kernel<float>, gq, dim3(kDqThreads), 0, s, a);
-  } else {
+  else
     hipLaunchKernelGGL(dkdv_kernel<uint16_t>, gkv, dim3(kKvThreads), 0, s, a, nkb);
+  if (grad_f32)
+    hipLaunchKernelGGL(dq_kernel<float>, gq, dim3(kDqThreads), 0, s, a);
+  else
     hipLaunchKernelGGL(dq_kernel<uint16_t>, gq, dim3(kDqThreads), 0, s, a);
-  }
   return hipGetLastError();
 }
 

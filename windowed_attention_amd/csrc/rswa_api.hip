@@ -543,7 +543,7 @@ rswa_status rswa_prefill_fwd(const void* q_dev, const void* k_dev, const void* v
 
 rswa_status rswa_prefill_bwd(const void* q_dev, const void* k_dev, const void* v_dev,
                              const void* out_dev, int32_t out_dtype, const void* dout_dev,
-                             const float* lse_dev, float* delta_dev, void* dq_dev, void* dk_dev,
+                             const float* lse_dev, float* work_dev, void* dq_dev, void* dk_dev,
                              void* dv_dev, int32_t grad_dtype, const int32_t* cu_seqlens_dev,
                              const int32_t* prefix_len_dev, const int32_t* window_dev,
                              int32_t nseq, int32_t total_tokens, int32_t num_heads,
@@ -553,8 +553,8 @@ rswa_status rswa_prefill_bwd(const void* q_dev, const void* k_dev, const void* v
                                        prefix_len_dev, window_dev, nseq, num_heads, head_dim,
                                        max_seqlen, prefix_causal, softmax_scale);
   if (st != RSWA_OK) return st;
-  if (!dout_dev || !lse_dev || !delta_dev)
-    return fail(RSWA_E_INVALID, "dout/lse/delta pointer is NULL");
+  if (!dout_dev || !lse_dev || !work_dev)
+    return fail(RSWA_E_INVALID, "dout/lse/work pointer is NULL");
   if (!dq_dev || !dk_dev || !dv_dev) return fail(RSWA_E_INVALID, "dq/dk/dv pointer is NULL");
   if (grad_dtype != RSWA_BF16 && grad_dtype != RSWA_F32)
     return fail(RSWA_E_INVALID, "grad_dtype must be RSWA_BF16 or RSWA_F32");
@@ -569,7 +569,8 @@ rswa_status rswa_prefill_bwd(const void* q_dev, const void* k_dev, const void* v
     a.out = out_dev;
     a.dout = reinterpret_cast<const uint16_t*>(dout_dev);
     a.lse = lse_dev;
-    a.delta = delta_dev;
+    a.work = work_dev;
+    a.rows = (int64_t)total_tokens * num_heads;
     a.dq = dq_dev;
     a.dk = dk_dev;
     a.dv = dv_dev;
@@ -583,7 +584,6 @@ rswa_status rswa_prefill_bwd(const void* q_dev, const void* k_dev, const void* v
     a.scale = scale;
     a.scale_log2 = scale * 1.4426950408889634f;
     const hipError_t e = rswa::launch_prefill_bwd(a, out_dtype == RSWA_F32, grad_dtype == RSWA_F32,
-                                                  total_tokens,
                                                   reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "prefill backward launch");
     return RSWA_OK;
