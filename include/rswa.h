@@ -69,12 +69,17 @@ typedef struct rswa_cache_desc {
   void* storage_dev;          /* caller-owned device storage of at least rswa_cache_bytes()
                                  bytes, or NULL: the library allocates (and frees) it */
   uint64_t storage_bytes;     /* size of storage_dev; ignored when storage_dev is NULL */
+  int32_t prefix_paged;       /* 0: the cache holds a copy of every prefix (rswa_cache_create);
+                                 1: prefixes stay in a caller-owned token pool, looked up through
+                                 a page table (rswa_cache_create_paged); the storage then holds
+                                 only the output rows */
 } rswa_cache_desc;
 
 typedef struct rswa_cache rswa_cache; /* opaque; owned by the library */
 
 /* Storage layout, for callers that inspect or snapshot the cache. Sequence b owns
- * R_b = m_b + cap_b rows per head (cap_b = n_b in RSWA mode, max_steps_b in FULL_CAUSAL mode):
+ * R_b = m_b + cap_b rows per head (cap_b = n_b in RSWA mode, max_steps_b in FULL_CAUSAL mode),
+ * or R_b = cap_b with prefix_paged = 1 (storage row r then holds cache row m_b + r):
  *   K[b][h][r][i] at element seq_offset[b] + (h * R_b + r) * D + i,
  *   V[b][h][r][i] at element seq_offset[b] + H * R_b * D + (h * R_b + r) * D + i,
  * elements of kv_dtype. Rows [0, m_b) hold the prefix; in RSWA mode output index j (0-based) lives
@@ -96,6 +101,23 @@ uint64_t rswa_cache_bytes(const rswa_cache_desc* desc);
  * (storage_bytes too small), RSWA_E_OOM, RSWA_E_HIP. On error *out is NULL. */
 rswa_status rswa_cache_create(const rswa_cache_desc* desc, const void* prefix_k_dev,
                               const void* prefix_v_dev, void* stream, rswa_cache** out);
+
+/* Create a cache whose prefixes live in a shared, token-granular page pool (survey's paged /
+ * shared prefix KV; the pages serve the model with a page size of one token and plan a pool of
+ * prefill KV chunks: GeekNews "Unlimited OCR", serving flags and limitations). desc->prefix_paged
+ * must be 1. pool_k_dev / pool_v_dev: caller-owned device arrays [pool_rows][H][D] of kv_dtype
+ * (token-major: one row per token, 256 B per head in bf16), read during every decode, unchanged
+ * and alive until rswa_cache_destroy. prefix_table_dev: device int32 [sum_b m_b]; prefix token j
+ * of sequence b is pool row table[M_b + j], M_b = sum_{b' < b} m_b'. Several sequences may
+ * point at the same pool rows (one document decoded by many sequences is stored once). Output rows
+ * (the ring, or the full-causal rows) are per sequence in the cache storage as usual. Entries
+ * outside [0, pool_rows) are rejected with RSWA_E_INVALID (checked on the device at creation; the
+ * call blocks until the check is done). Decode results equal those of rswa_cache_create with the
+ * gathered prefixes, bit for bit. */
+rswa_status rswa_cache_create_paged(const rswa_cache_desc* desc, const void* pool_k_dev,
+                                    const void* pool_v_dev, int64_t pool_rows,
+                                    const int32_t* prefix_table_dev, void* stream,
+                                    rswa_cache** out);
 
 /* K1, append / evict. For every sequence b with active_dev[b] != 0 (or every b when active_dev
  * is NULL): write k_dev[b] / v_dev[b] ([B][H][D], kv_dtype) to row m_b + (t_b mod n_b) of every
@@ -169,16 +191,17 @@ rswa_status rswa_prefill_fwd(const void* q_dev, const void* k_dev, const void* v
  * no query sees a key of another segment.
  * q/k/v_dev, dout_dev: [total][H][D] bf16; out_dev: the forward output [total][H][D] of out_dtype;
  * lse_dev: float32 [total][H] from rswa_prefill_fwd with the same arguments.
- * delta_dev: caller-owned float32 [total][H] work array, overwritten with delta.
+ * work_dev: caller-owned float32 work array of 2 * total_tokens * H values, overwritten with
+ * [0][token][h] = lse * log2(e) and [1][token][h] = delta.
  * dq/dk/dv_dev: [total][H][D] of grad_dtype, overwritten on every row of every segment (rows
  * beyond cu_seqlens[nseq] are not touched). total_tokens (host) = rows of these arrays, at least
- * cu_seqlens[nseq]; delta is written for all of them.
+ * cu_seqlens[nseq]; the work array covers all of them.
  * The library allocates nothing; all work is enqueued on `stream`.
- * Errors: as rswa_prefill_attn, plus RSWA_E_INVALID for NULL dout/lse/delta/dq/dk/dv, a bad
+ * Errors: as rswa_prefill_attn, plus RSWA_E_INVALID for NULL dout/lse/work/dq/dk/dv, a bad
  * grad_dtype or total_tokens < 0. Device-side metadata is trusted. */
 rswa_status rswa_prefill_bwd(const void* q_dev, const void* k_dev, const void* v_dev,
                              const void* out_dev, int32_t out_dtype, const void* dout_dev,
-                             const float* lse_dev, float* delta_dev, void* dq_dev, void* dk_dev,
+                             const float* lse_dev, float* work_dev, void* dq_dev, void* dk_dev,
                              void* dv_dev, int32_t grad_dtype, const int32_t* cu_seqlens_dev,
                              const int32_t* prefix_len_dev, const int32_t* window_dev,
                              int32_t nseq, int32_t total_tokens, int32_t num_heads,

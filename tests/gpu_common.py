@@ -43,12 +43,20 @@ def sample_steps(T: int, n: int, m: int, seed: int = 0, extra: int = 16, crossin
 class Trajectory:
     """Device copies of a decode workload and a cache built from it."""
 
-    def __init__(self, wa, wl: DecodeWorkload, mode: int, storage: torch.Tensor | None = None):
+    def __init__(self, wa, wl: DecodeWorkload, mode: int, storage: torch.Tensor | None = None,
+                 paged=None):
+        """`paged` (a workloads.PagedPrefix): build the cache over the shared token pool and its
+        page table instead of copying wl's gathered prefixes."""
         self.wl = wl
         self.wa = wa
         self.mode = mode
-        self.pk = upload(wl.prefix_k, wl.dtype) if wl.prefix_k.shape[0] else None
-        self.pv = upload(wl.prefix_v, wl.dtype) if wl.prefix_v.shape[0] else None
+        if paged is None:
+            self.pk = upload(wl.prefix_k, wl.dtype) if wl.prefix_k.shape[0] else None
+            self.pv = upload(wl.prefix_v, wl.dtype) if wl.prefix_v.shape[0] else None
+        else:
+            self.pk = self.pv = None
+            pool = dict(pool_k=upload(paged.pool_k, wl.dtype), pool_v=upload(paged.pool_v, wl.dtype),
+                        prefix_table=torch.from_numpy(paged.table).cuda())
         self.q = upload(wl.q, wl.dtype)
         self.k = upload(wl.k, wl.dtype)
         self.v = upload(wl.v, wl.dtype)
@@ -59,9 +67,10 @@ class Trajectory:
             self.active = torch.from_numpy(act).cuda()
         max_steps = wl.steps if mode == wa.MODE_FULL_CAUSAL else None
         window = wl.window if mode == wa.MODE_RSWA else None
+        extra = pool if paged is not None else {}
         self.cache = wa.RswaCache(self.pk, self.pv, wl.prefix_len, window, mode=mode,
                                   max_steps=max_steps, kv_dtype=kv_torch_dtype(wl.dtype),
-                                  storage=storage)
+                                  storage=storage, **extra)
 
     def run(self, checkpoints, out_dtype=torch.float32, t_end: int | None = None,
             fused: bool = False, raw: bool = False):

@@ -137,3 +137,37 @@ def test_training_entry_points_reject_bad_arguments_before_any_device_work(wa):
     bad[18] = 96
     assert lib.rswa_prefill_bwd(*bad) == -2
     assert b"head_dim" in lib.rswa_last_error()
+
+
+def test_paged_plan_stores_only_output_rows(wa):
+    m, n = np.array([300, 150, 0, 40]), np.array([32, 16, 8, 64])
+    _, rows_c, bytes_c = wa.rswa_cache_plan(m, n)
+    _, rows_p, bytes_p = wa.rswa_cache_plan(m, n, paged=True)
+    np.testing.assert_array_equal(rows_c, m + n)
+    np.testing.assert_array_equal(rows_p, n)
+    assert bytes_p == 2 * 16 * 128 * 2 * int(n.sum())
+    assert bytes_c - bytes_p == 2 * 16 * 128 * 2 * int(m.sum())
+
+
+def test_paged_create_checks_arguments_before_device_work(wa):
+    lib = wa._lib
+    null, one = ctypes.c_void_p(None), ctypes.c_void_p(16)
+    d, keep = wa._desc(np.array([5, 3]), np.array([4, 4]), None, 16, 128, wa.torch.bfloat16,
+                       wa.MODE_RSWA, paged=True)
+    h = ctypes.c_void_p(None)
+    # NULL pool / table with m > 0
+    assert lib.rswa_cache_create_paged(ctypes.byref(d), null, one, 10, one, null,
+                                       ctypes.byref(h)) == -1
+    assert lib.rswa_cache_create_paged(ctypes.byref(d), one, one, 10, null, null,
+                                       ctypes.byref(h)) == -1
+    assert lib.rswa_cache_create_paged(ctypes.byref(d), one, one, 0, one, null,
+                                       ctypes.byref(h)) == -1
+    # a paged description given to the copying entry point, and the reverse
+    assert lib.rswa_cache_create(ctypes.byref(d), one, one, null, ctypes.byref(h)) == -1
+    assert b"prefix_paged" in lib.rswa_last_error()
+    d.prefix_paged = 0
+    assert lib.rswa_cache_create_paged(ctypes.byref(d), one, one, 10, one, null,
+                                       ctypes.byref(h)) == -1
+    d.prefix_paged = 2
+    assert lib.rswa_cache_create(ctypes.byref(d), one, one, null, ctypes.byref(h)) == -1
+    assert h.value is None

@@ -351,3 +351,34 @@ def test_mutation_transposed_value_is_caught(monkeypatch):
                         lambda q, K, V, s: real(q, K, V[::-1].copy(), s))
     with pytest.raises(AssertionError):
         test_brute_force_decode(2, 3, 4)
+
+
+# ---------------------------------------------------------------------------------------------
+# prefixes in a shared token pool
+# ---------------------------------------------------------------------------------------------
+def test_paged_prefix_identity_and_permuted_pool():
+    m, H, d = 11, 2, 4
+    pre = rnd((m, H, d), 90)
+    np.testing.assert_array_equal(O.paged_prefix(pre, np.arange(m), 0, m), pre)
+    perm = np.random.default_rng(3).permutation(m + 5)
+    pool = rnd((m + 5, H, d), 91)
+    pool[perm[:m]] = pre          # token j stored at slot perm[j]
+    table = np.concatenate([[7, 7, 7], perm[:m]])  # another sequence's entries come first
+    np.testing.assert_array_equal(O.paged_prefix(pool, table, 3, m), pre)
+
+
+def test_shared_pool_rows_give_each_sequence_its_document():
+    """Two sequences over one document stored once: each sees exactly the document's rows."""
+    m, n, H, d, T = 6, 3, 2, 8, 5
+    doc_k, doc_v = rnd((m, H, d), 92), rnd((m, H, d), 93)
+    pool_k = np.concatenate([rnd((4, H, d), 94), doc_k])
+    pool_v = np.concatenate([rnd((4, H, d), 95), doc_v])
+    table = np.concatenate([np.arange(4, 4 + m), np.arange(4, 4 + m)])
+    ok, ov, q = rnd((T, H, d), 96), rnd((T, H, d), 97), rnd((T, H, d), 98)
+    for s in range(2):
+        pk = O.paged_prefix(pool_k, table, s * m, m)
+        pv = O.paged_prefix(pool_v, table, s * m, m)
+        for t in range(1, T + 1):
+            got, _ = O.decode_step(q[t - 1], pk, pv, ok, ov, t, n)
+            ref, _ = O.decode_step(q[t - 1], doc_k, doc_v, ok, ov, t, n)
+            np.testing.assert_array_equal(got, ref)

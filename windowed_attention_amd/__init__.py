@@ -23,7 +23,8 @@ STATUS = {0: "RSWA_OK", -1: "RSWA_E_INVALID", -2: "RSWA_E_UNSUPPORTED", -3: "RSW
           -4: "RSWA_E_OOM", -5: "RSWA_E_HIP", -6: "RSWA_E_INTERNAL"}
 
 # Every symbol include/rswa.h declares.
-EXPORTS = ("rswa_cache_plan", "rswa_cache_bytes", "rswa_cache_create", "rswa_append_kv",
+EXPORTS = ("rswa_cache_plan", "rswa_cache_bytes", "rswa_cache_create", "rswa_cache_create_paged",
+           "rswa_append_kv",
            "rswa_decode_attn", "rswa_decode_step", "rswa_prefill_attn", "rswa_prefill_fwd",
            "rswa_prefill_bwd", "rswa_cache_steps", "rswa_cache_info",
            "rswa_cache_set_decode_split", "rswa_cache_decode_plan", "rswa_cache_destroy",
@@ -43,7 +44,8 @@ class CacheDesc(ctypes.Structure):
                 ("mode", ctypes.c_int32), ("prefix_len", ctypes.POINTER(ctypes.c_int32)),
                 ("window", ctypes.POINTER(ctypes.c_int32)),
                 ("max_steps", ctypes.POINTER(ctypes.c_int32)),
-                ("storage_dev", ctypes.c_void_p), ("storage_bytes", ctypes.c_uint64)]
+                ("storage_dev", ctypes.c_void_p), ("storage_bytes", ctypes.c_uint64),
+                ("prefix_paged", ctypes.c_int32)]
 
 
 def _load():
@@ -59,6 +61,8 @@ def _load():
         "rswa_cache_plan": (i32, [pdesc, pi64, pi32, ctypes.POINTER(u64)]),
         "rswa_cache_bytes": (u64, [pdesc]),
         "rswa_cache_create": (i32, [pdesc, vp, vp, vp, ctypes.POINTER(vp)]),
+        "rswa_cache_create_paged": (i32, [pdesc, vp, vp, ctypes.c_int64, vp, vp,
+                                          ctypes.POINTER(vp)]),
         "rswa_append_kv": (i32, [vp, vp, vp, vp, vp]),
         "rswa_decode_attn": (i32, [vp, vp, vp, i32, f32, vp, vp]),
         "rswa_decode_step": (i32, [vp, vp, vp, vp, vp, i32, f32, vp, vp]),
@@ -130,7 +134,8 @@ def _i32_array(x, n: int, name: str):
     return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
 
-def _desc(prefix_len, window, max_steps, num_heads, head_dim, kv_dtype, mode, storage=None):
+def _desc(prefix_len, window, max_steps, num_heads, head_dim, kv_dtype, mode, storage=None,
+          paged=False):
     m = np.ascontiguousarray(np.asarray(prefix_len, dtype=np.int32).reshape(-1))
     B = m.size
     keep = [m]
@@ -147,13 +152,15 @@ def _desc(prefix_len, window, max_steps, num_heads, head_dim, kv_dtype, mode, st
     if storage is not None:
         d.storage_dev = storage.data_ptr()
         d.storage_bytes = storage.numel() * storage.element_size()
+    d.prefix_paged = int(bool(paged))
     return d, keep
 
 
 def rswa_cache_plan(prefix_len, window=None, max_steps=None, *, num_heads=16, head_dim=128,
-                    kv_dtype=torch.bfloat16, mode=MODE_RSWA):
+                    kv_dtype=torch.bfloat16, mode=MODE_RSWA, paged=False):
     """Host-only layout: (seq_offset elements [B] int64, rows [B] int32, storage bytes)."""
-    d, keep = _desc(prefix_len, window, max_steps, num_heads, head_dim, kv_dtype, mode)
+    d, keep = _desc(prefix_len, window, max_steps, num_heads, head_dim, kv_dtype, mode,
+                    paged=paged)
     B = d.batch
     off = np.zeros(max(B, 1), dtype=np.int64)
     rows = np.zeros(max(B, 1), dtype=np.int32)
@@ -165,36 +172,58 @@ def rswa_cache_plan(prefix_len, window=None, max_steps=None, *, num_heads=16, he
 
 
 def rswa_cache_bytes(prefix_len, window=None, max_steps=None, *, num_heads=16, head_dim=128,
-                     kv_dtype=torch.bfloat16, mode=MODE_RSWA) -> int:
-    d, keep = _desc(prefix_len, window, max_steps, num_heads, head_dim, kv_dtype, mode)
+                     kv_dtype=torch.bfloat16, mode=MODE_RSWA, paged=False) -> int:
+    d, keep = _desc(prefix_len, window, max_steps, num_heads, head_dim, kv_dtype, mode,
+                    paged=paged)
     return int(_lib.rswa_cache_bytes(ctypes.byref(d)))
 
 
 class RswaCache:
     """A batch of B decode sequences: static prefix rows plus an n-slot ring per sequence
-    (mode MODE_RSWA) or a growing cache (MODE_FULL_CAUSAL)."""
+    (mode MODE_RSWA) or a growing cache (MODE_FULL_CAUSAL).
+
+    With `pool_k`, `pool_v` ([pool_rows][H][D]) and `prefix_table` (int32 [sum m_b], device) the
+    prefixes are not copied: sequence b's prefix token j is pool row prefix_table[M_b + j]
+    (rswa_cache_create_paged); prefix_k / prefix_v must then be None. The pools must stay alive
+    and unchanged while the cache is used (the object keeps a reference)."""
 
     def __init__(self, prefix_k: torch.Tensor | None, prefix_v: torch.Tensor | None, prefix_len,
                  window=None, *, mode=MODE_RSWA, max_steps=None, num_heads=16, head_dim=128,
-                 kv_dtype=None, storage: torch.Tensor | None = None, stream=None):
+                 kv_dtype=None, storage: torch.Tensor | None = None, pool_k=None, pool_v=None,
+                 prefix_table=None, stream=None):
         m = np.asarray(prefix_len, dtype=np.int64).reshape(-1)
+        paged = prefix_table is not None
         if kv_dtype is None:
-            if prefix_k is None:
+            src = pool_k if paged else prefix_k
+            if src is None:
                 raise ValueError("kv_dtype is required when there is no prefix tensor")
-            kv_dtype = prefix_k.dtype
+            kv_dtype = src.dtype
         total_m = int(m.sum())
-        shape = (total_m, num_heads, head_dim)
-        pk = _dev(prefix_k, "prefix_k", kv_dtype, shape) if prefix_k is not None else None
-        pv = _dev(prefix_v, "prefix_v", kv_dtype, shape) if prefix_v is not None else None
         if storage is not None:
             _dev(storage, "storage")
-        d, keep = _desc(m, window, max_steps, num_heads, head_dim, kv_dtype, mode, storage)
+        d, keep = _desc(m, window, max_steps, num_heads, head_dim, kv_dtype, mode, storage,
+                        paged=paged)
         h = ctypes.c_void_p(None)
-        _check(_lib.rswa_cache_create(ctypes.byref(d), pk or ctypes.c_void_p(None),
-                                      pv or ctypes.c_void_p(None), _stream(stream),
-                                      ctypes.byref(h)), "rswa_cache_create")
+        if paged:
+            if prefix_k is not None or prefix_v is not None:
+                raise ValueError("a paged cache takes pool_k / pool_v, not prefix_k / prefix_v")
+            rows = int(pool_k.shape[0])
+            pshape = (rows, num_heads, head_dim)
+            _check(_lib.rswa_cache_create_paged(
+                ctypes.byref(d), _dev(pool_k, "pool_k", kv_dtype, pshape),
+                _dev(pool_v, "pool_v", kv_dtype, pshape), rows,
+                _dev(prefix_table, "prefix_table", torch.int32, (total_m,)), _stream(stream),
+                ctypes.byref(h)), "rswa_cache_create_paged")
+        else:
+            shape = (total_m, num_heads, head_dim)
+            pk = _dev(prefix_k, "prefix_k", kv_dtype, shape) if prefix_k is not None else None
+            pv = _dev(prefix_v, "prefix_v", kv_dtype, shape) if prefix_v is not None else None
+            _check(_lib.rswa_cache_create(ctypes.byref(d), pk or ctypes.c_void_p(None),
+                                          pv or ctypes.c_void_p(None), _stream(stream),
+                                          ctypes.byref(h)), "rswa_cache_create")
         self._h = h
         self._storage = storage
+        self._pools = (pool_k, pool_v, prefix_table) if paged else None
         self.batch = int(m.size)
         self.num_heads = num_heads
         self.head_dim = head_dim

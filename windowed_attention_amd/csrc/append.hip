@@ -7,7 +7,8 @@
 // write per head with no data movement, and the live rows are always the contiguous range
 // [0, m + min(n, t)). Full-causal mode writes row m + j (the cache grows, standard attention).
 // The prefix rows [0, m) are written once at creation and never again (GeekNews, DeepEncoder
-// section: visual tokens are encoded once and stay static).
+// section: visual tokens are encoded once and stay static); a paged prefix is not in the cache
+// at all, and the output rows then start at storage row 0.
 #include "device.h"
 #include "kernels.h"
 
@@ -34,8 +35,9 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     }
     return;
   }
-  const int m = a.meta.prefix_len[b];
-  const int64_t row = a.full_causal ? (int64_t)m + t : (int64_t)m + t % cap;
+  // storage row of the new output: after the prefix, or from row 0 when the prefix is paged
+  const int64_t m0 = a.meta.table ? 0 : a.meta.prefix_len[b];
+  const int64_t row = a.full_causal ? m0 + t : m0 + t % cap;
   const int64_t R = a.meta.rows[b];
   constexpr int CH = kHeadDim * ELEM / 16;  // 16-byte pieces per row
   const int H = a.heads;
@@ -81,7 +83,26 @@ __global__ __launch_bounds__(kThreads) void prefix_copy_kernel(PrefixCopyArgs a)
   }
 }
 
+__global__ __launch_bounds__(kThreads) void table_check_kernel(const int32_t* table, int64_t n,
+                                                               int64_t pool_rows, int32_t* bad) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kThreads) {
+    const int32_t r = table[i];
+    if (r < 0 || r >= pool_rows) *bad = 1;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_table_check(const int32_t* table, int64_t n, int64_t pool_rows, int32_t* bad,
+                              hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t gx = (n + kThreads - 1) / kThreads;
+  if (gx > 4096) gx = 4096;
+  hipLaunchKernelGGL(table_check_kernel, dim3((unsigned)gx), dim3(kThreads), 0, s, table, n,
+                     pool_rows, bad);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const AppendArgs& a, int batch, int kv_f32, hipStream_t s) {
   if (kv_f32)

@@ -236,9 +236,20 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int h, 
   const int g = lane / GL, li = lane % GL;
   const int H = a.heads;
   const int64_t R = a.meta.rows[b];
+  const int m = a.meta.prefix_len[b];
+  // Cache row r lives at Kp + r * D; with a paged prefix the storage starts at row m, and rows
+  // r < m are pool rows found through the page table (one 4-byte lookup per row and group).
+  const bool paged = a.meta.table != nullptr;
+  const int64_t shift = paged ? m : 0;
   KV* seq = reinterpret_cast<KV*>(a.storage) + a.meta.seq_off[b];
-  KV* Kp = seq + (int64_t)h * R * kHeadDim + li * VEC;
-  KV* Vp = seq + (int64_t)(H + h) * R * kHeadDim + li * VEC;
+  KV* Kp = seq + ((int64_t)h * R - shift) * kHeadDim + li * VEC;
+  KV* Vp = seq + ((int64_t)(H + h) * R - shift) * kHeadDim + li * VEC;
+  const int32_t* tab = paged ? a.meta.table + a.meta.table_off[b] : nullptr;
+  const KV* PKp = paged ? reinterpret_cast<const KV*>(a.meta.pool_k) + h * kHeadDim + li * VEC
+                        : nullptr;
+  const KV* PVp = paged ? reinterpret_cast<const KV*>(a.meta.pool_v) + h * kHeadDim + li * VEC
+                        : nullptr;
+  const int64_t pool_stride = (int64_t)H * kHeadDim;
   const int64_t bh = (int64_t)b * H + h;
   const u32x4 qv = ld16(reinterpret_cast<const KV*>(a.q) + bh * kHeadDim + li * VEC);
   const KV* kin = a.k_new ? reinterpret_cast<const KV*>(a.k_new) + bh * kHeadDim + li * VEC : nullptr;
@@ -257,8 +268,14 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int h, 
       const int row = base + u * G + g;
       const int rr = min(row, r1 - 1);
       const bool fresh = rr == rnew;
-      kr[u] = ld16(fresh ? kin : Kp + (int64_t)rr * kHeadDim);
-      vr[u] = ld16(fresh ? vin : Vp + (int64_t)rr * kHeadDim);
+      if (paged && rr < m) {
+        const int64_t pr = (int64_t)tab[rr] * pool_stride;
+        kr[u] = ld16(PKp + pr);
+        vr[u] = ld16(PVp + pr);
+      } else {
+        kr[u] = ld16(fresh ? kin : Kp + (int64_t)rr * kHeadDim);
+        vr[u] = ld16(fresh ? vin : Vp + (int64_t)rr * kHeadDim);
+      }
     }
   };
   if (rb < r1) load(rb, kc, vc);

@@ -13,6 +13,12 @@ struct CacheMeta {
   const int32_t* prefix_len; // [B] m_b
   const int32_t* cap;        // [B] n_b (R-SWA ring slots) or max_steps_b (full causal)
   int32_t* err;              // [1] sticky flag: a full-causal append found no free row
+  // Paged prefix (table != nullptr): cache row r < m_b is pool row table[table_off[b] + r] of the
+  // token-major pools [rows][H][D]; storage row r' holds cache row m_b + r'.
+  const int32_t* table;
+  const int64_t* table_off;  // [B]
+  const void* pool_k;
+  const void* pool_v;
 };
 
 // Step counters t_b are double-buffered: a launch that appends reads steps_in and writes
@@ -106,6 +112,9 @@ hipError_t launch_append(const AppendArgs& a, int batch, int kv_f32, hipStream_t
 hipError_t launch_decode(const DecodeArgs& a, int kv_f32, int out_f32, int grid_blocks,
                          bool need_merge, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int out_f32, hipStream_t s);
+// Sets *bad = 1 if any of the n table entries lies outside [0, pool_rows).
+hipError_t launch_table_check(const int32_t* table, int64_t n, int64_t pool_rows, int32_t* bad,
+                              hipStream_t s);
 hipError_t launch_prefill_bwd(const BwdArgs& a, int out_f32, int grad_f32, hipStream_t s);
 // Resident 256-thread decode workgroups per CU (occupancy of the decode kernel for a batch of B).
 int decode_blocks_per_cu(int kv_f32, int out_f32, int batch);

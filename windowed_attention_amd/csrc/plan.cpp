@@ -27,6 +27,9 @@ rswa_status make_plan(const rswa_cache_desc* d, Plan* p, std::string* why) {
   const bool full = d->mode == RSWA_MODE_FULL_CAUSAL;
   if (!full && !d->window) return bad(RSWA_E_INVALID, "window is NULL in R-SWA mode");
   if (full && !d->max_steps) return bad(RSWA_E_INVALID, "max_steps is NULL in full-causal mode");
+  if (d->prefix_paged != 0 && d->prefix_paged != 1)
+    return bad(RSWA_E_INVALID, "prefix_paged must be 0 or 1");
+  const bool paged = d->prefix_paged == 1;
 
   const int B = d->batch;
   const int64_t H = d->num_heads, D = d->head_dim;
@@ -44,7 +47,7 @@ rswa_status make_plan(const rswa_cache_desc* d, Plan* p, std::string* why) {
     const int64_t cap = full ? d->max_steps[b] : d->window[b];
     if (m < 0) return bad(RSWA_E_INVALID, "prefix_len must be >= 0");
     if (cap < 1) return bad(RSWA_E_INVALID, full ? "max_steps must be >= 1" : "window must be >= 1");
-    const int64_t R = m + cap;
+    const int64_t R = paged ? cap : m + cap;  // a paged prefix is not stored in the cache
     if (R > std::numeric_limits<int32_t>::max() / 2)
       return bad(RSWA_E_INVALID, "prefix_len + capacity too large");
     p->seq_off[b] = off;

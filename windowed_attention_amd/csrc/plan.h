@@ -17,10 +17,10 @@ constexpr int32_t kPlanHeadDim = 128;
 
 struct Plan {
   std::vector<int64_t> seq_off;   // element offset of sequence b's K block
-  std::vector<int32_t> rows;      // R_b = m_b + cap_b
+  std::vector<int32_t> rows;      // R_b = m_b + cap_b (cap_b with a paged prefix)
   std::vector<int32_t> prefix;    // m_b
   std::vector<int32_t> cap;       // n_b (R-SWA) or max_steps_b (full causal)
-  std::vector<int64_t> prefix_row0; // first packed prefix row of sequence b
+  std::vector<int64_t> prefix_row0; // first packed prefix row (page-table entry) of sequence b
   int64_t total_prefix_rows = 0;
   int32_t max_prefix = 0;
   uint64_t bytes = 0;

@@ -130,8 +130,22 @@ uint64_t rswa_cache_bytes(const rswa_cache_desc* desc) {
   return bytes;
 }
 
-rswa_status rswa_cache_create(const rswa_cache_desc* desc, const void* prefix_k_dev,
-                              const void* prefix_v_dev, void* stream, rswa_cache** out) {
+}  // extern "C"
+
+namespace {
+
+// Shared by rswa_cache_create (prefix copied into the cache) and rswa_cache_create_paged (prefix
+// looked up in the caller's pool through the page table).
+struct PagedPrefix {
+  const void* pool_k = nullptr;
+  const void* pool_v = nullptr;
+  int64_t pool_rows = 0;
+  const int32_t* table = nullptr;
+};
+
+rswa_status create_cache(const rswa_cache_desc* desc, const void* prefix_k_dev,
+                         const void* prefix_v_dev, const PagedPrefix* pg, void* stream,
+                         rswa_cache** out) {
   if (!out) return fail(RSWA_E_INVALID, "out is NULL");
   *out = nullptr;
   rswa_cache* c = nullptr;
@@ -140,8 +154,21 @@ rswa_status rswa_cache_create(const rswa_cache_desc* desc, const void* prefix_k_
     std::string why;
     rswa_status s = rswa::make_plan(desc, &p, &why);
     if (s != RSWA_OK) return fail(s, why);
-    if (p.total_prefix_rows > 0 && (!prefix_k_dev || !prefix_v_dev))
+    const bool paged = pg != nullptr;
+    if (paged != (desc->prefix_paged == 1))
+      return fail(RSWA_E_INVALID, paged ? "rswa_cache_create_paged needs desc->prefix_paged = 1"
+                                        : "desc->prefix_paged = 1 needs rswa_cache_create_paged");
+    if (paged) {
+      if (p.total_prefix_rows > 0 && (!pg->pool_k || !pg->pool_v || !pg->table))
+        return fail(RSWA_E_INVALID, "pool_k / pool_v / prefix_table is NULL but some m_b > 0");
+      if (p.total_prefix_rows > 0 && pg->pool_rows < 1)
+        return fail(RSWA_E_INVALID, "pool_rows must be >= 1");
+      if ((reinterpret_cast<uintptr_t>(pg->pool_k) % 16) != 0 ||
+          (reinterpret_cast<uintptr_t>(pg->pool_v) % 16) != 0)
+        return fail(RSWA_E_INVALID, "pool_k / pool_v must be 16-byte aligned");
+    } else if (p.total_prefix_rows > 0 && (!prefix_k_dev || !prefix_v_dev)) {
       return fail(RSWA_E_INVALID, "prefix_k_dev / prefix_v_dev are NULL but some m_b > 0");
+    }
     if (desc->storage_dev && desc->storage_bytes < p.bytes)
       return fail(RSWA_E_CAPACITY, "storage_bytes smaller than rswa_cache_bytes()");
     if (desc->storage_dev && (reinterpret_cast<uintptr_t>(desc->storage_dev) % 16) != 0)
@@ -222,6 +249,13 @@ rswa_status rswa_cache_create(const rswa_cache_desc* desc, const void* prefix_k_
     c->steps_dev[0] = reinterpret_cast<int32_t*>(mb + off_steps);
     c->steps_dev[1] = reinterpret_cast<int32_t*>(mb + off_steps2);
     c->meta.err = reinterpret_cast<int32_t*>(mb + off_err);
+    int32_t* table_bad = reinterpret_cast<int32_t*>(mb + off_err + 4);  // zeroed with the rest
+    if (paged) {
+      c->meta.table = pg->table;
+      c->meta.table_off = c->prefix_row0_dev;
+      c->meta.pool_k = pg->pool_k;
+      c->meta.pool_v = pg->pool_v;
+    }
 
     // decode plan: resident workgroups per CU, and a workspace sized for the largest stream-K
     // grid (partial slot = workgroup index + (b, h) index, see decode.hip)
@@ -243,25 +277,46 @@ rswa_status rswa_cache_create(const rswa_cache_desc* desc, const void* prefix_k_
     c->ws_ml = reinterpret_cast<float2*>(wb + ws_acc_bytes);
     c->ws_cum = reinterpret_cast<int64_t*>(wb + ws_acc_bytes + ws_ml_bytes);
 
-    // prefix rows
-    rswa::PrefixCopyArgs pa{};
-    pa.storage = c->storage;
-    pa.meta = c->meta;
-    pa.pk = prefix_k_dev;
-    pa.pv = prefix_v_dev;
-    pa.prefix_row0 = c->prefix_row0_dev;
-    pa.heads = c->H;
-    pa.batch = B;
-    e = rswa::launch_prefix_copy(pa, c->kv_dtype == RSWA_F32, p.max_prefix, st);
-    if (e != hipSuccess) {
-      release(c);
-      return hip_fail(e, "prefix copy launch");
+    if (paged) {
+      // every page-table entry must name a pool row: checked once here, so decode never reads
+      // outside the pool
+      e = rswa::launch_table_check(pg->table, p.total_prefix_rows, pg->pool_rows, table_bad, st);
+      if (e != hipSuccess) {
+        release(c);
+        return hip_fail(e, "page-table check launch");
+      }
+    } else {
+      rswa::PrefixCopyArgs pa{};
+      pa.storage = c->storage;
+      pa.meta = c->meta;
+      pa.pk = prefix_k_dev;
+      pa.pv = prefix_v_dev;
+      pa.prefix_row0 = c->prefix_row0_dev;
+      pa.heads = c->H;
+      pa.batch = B;
+      e = rswa::launch_prefix_copy(pa, c->kv_dtype == RSWA_F32, p.max_prefix, st);
+      if (e != hipSuccess) {
+        release(c);
+        return hip_fail(e, "prefix copy launch");
+      }
     }
     // the host metadata buffer must outlive the async copy
     e = hipStreamSynchronize(st);
     if (e != hipSuccess) {
       release(c);
       return hip_fail(e, "hipStreamSynchronize(create)");
+    }
+    if (paged) {
+      int32_t bad = 0;
+      e = hipMemcpy(&bad, table_bad, sizeof(bad), hipMemcpyDeviceToHost);
+      if (e != hipSuccess) {
+        release(c);
+        return hip_fail(e, "hipMemcpy(page-table check)");
+      }
+      if (bad) {
+        release(c);
+        return fail(RSWA_E_INVALID, "a page-table entry lies outside [0, pool_rows)");
+      }
     }
     *out = c;
     return RSWA_OK;
@@ -272,6 +327,27 @@ rswa_status rswa_cache_create(const rswa_cache_desc* desc, const void* prefix_k_
     release(c);
     return fail(RSWA_E_INTERNAL, "exception in rswa_cache_create");
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+rswa_status rswa_cache_create(const rswa_cache_desc* desc, const void* prefix_k_dev,
+                              const void* prefix_v_dev, void* stream, rswa_cache** out) {
+  return create_cache(desc, prefix_k_dev, prefix_v_dev, nullptr, stream, out);
+}
+
+rswa_status rswa_cache_create_paged(const rswa_cache_desc* desc, const void* pool_k_dev,
+                                    const void* pool_v_dev, int64_t pool_rows,
+                                    const int32_t* prefix_table_dev, void* stream,
+                                    rswa_cache** out) {
+  PagedPrefix pg;
+  pg.pool_k = pool_k_dev;
+  pg.pool_v = pool_v_dev;
+  pg.pool_rows = pool_rows;
+  pg.table = prefix_table_dev;
+  return create_cache(desc, nullptr, nullptr, &pg, stream, out);
 }
 
 rswa_status rswa_append_kv(rswa_cache* c, const void* k_dev, const void* v_dev,

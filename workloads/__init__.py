@@ -329,3 +329,84 @@ def packed_training_config(seed: int = 0, *, S: int = 32768, window: int = 128,
         left -= L
     name = f"packed training row, S={S}, {len(lens)} documents, n={window}, bf16"
     return make_prefill(name, 7, lens, ms, [window] * len(lens), seed=seed)
+
+
+# --------------------------------------------------------------------------------------------
+# shared prefixes in a token pool (paged prefix KV)
+# --------------------------------------------------------------------------------------------
+@dataclass
+class PagedPrefix:
+    """Every document's prefix stored once in a token pool, and each sequence's page table.
+
+    pool_k / pool_v: [pool_rows][H][D] (token-major); table: int32 [sum_b m_b], sequence b's
+    prefix token j at pool row table[M_b + j], M_b = sum of the earlier m_b'; doc_of_seq[b] is the
+    document sequence b decodes over."""
+    pool_k: np.ndarray
+    pool_v: np.ndarray
+    table: np.ndarray
+    doc_of_seq: np.ndarray
+
+
+def make_paged_decode(name: str, cfg: int, dtype: str, doc_prefix_len, seq_doc, window, steps,
+                      seed: int = 0, scatter: bool = True, spare_rows: int = 0):
+    """Decode trajectories of several sequences per document. Document d's prefix K, V are drawn
+    from SeedSequence([seed, cfg, 5000 + d]); sequence b's output K, V, Q from
+    SeedSequence([seed, cfg, b]) as in make_decode (no prefix draws). The pool holds the documents
+    back to back plus `spare_rows` unused rows; with `scatter` every token's pool row is a seeded
+    permutation (SeedSequence([seed, cfg])) of that order, i.e. token-granular pages in no
+    particular order. Returns (DecodeWorkload whose prefix_k / prefix_v are the gathered
+    per-sequence prefixes, PagedPrefix)."""
+    doc_m = np.asarray(doc_prefix_len, dtype=np.int64)
+    seq_doc = np.asarray(seq_doc, dtype=np.int64)
+    window = np.asarray(window, dtype=np.int32)
+    steps = np.asarray(steps, dtype=np.int32)
+    H, D = NUM_HEADS, HEAD_DIM
+    sdt = np.uint16 if dtype == "bf16" else np.float32
+    doc_off = np.zeros(doc_m.size + 1, dtype=np.int64)
+    np.cumsum(doc_m, out=doc_off[1:])
+    rows = int(doc_off[-1]) + spare_rows
+    flat_k = np.empty((rows, H, D), dtype=sdt)
+    flat_v = np.empty((rows, H, D), dtype=sdt)
+
+    def doc_job(d):
+        rng = np.random.default_rng(np.random.SeedSequence([seed, cfg, 5000 + d]))
+        m = int(doc_m[d])
+        flat_k[doc_off[d]:doc_off[d + 1]] = _store(_draw(rng, (m, H, D)), dtype)
+        flat_v[doc_off[d]:doc_off[d + 1]] = _store(_draw(rng, (m, H, D)), dtype)
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(doc_job, range(doc_m.size)))
+    if spare_rows:
+        rng = np.random.default_rng(np.random.SeedSequence([seed, cfg, 4999]))
+        flat_k[doc_off[-1]:] = _store(_draw(rng, (spare_rows, H, D)), dtype)
+        flat_v[doc_off[-1]:] = _store(_draw(rng, (spare_rows, H, D)), dtype)
+    if scatter:
+        slot = np.random.default_rng(np.random.SeedSequence([seed, cfg])).permutation(rows)
+    else:
+        slot = np.arange(rows)
+    pool_k = np.empty_like(flat_k)
+    pool_v = np.empty_like(flat_v)
+    pool_k[slot] = flat_k
+    pool_v[slot] = flat_v
+    prefix_len = doc_m[seq_doc].astype(np.int32)
+    table = np.concatenate([slot[doc_off[d]:doc_off[d + 1]] for d in seq_doc]).astype(np.int32) \
+        if seq_doc.size else np.zeros(0, dtype=np.int32)
+    wl = make_decode(name, cfg, dtype, np.zeros_like(prefix_len), window, steps, seed=seed)
+    wl.prefix_len = prefix_len
+    wl.prefix_k = pool_k[table]
+    wl.prefix_v = pool_v[table]
+    wl.meta["documents"] = int(doc_m.size)
+    return wl, PagedPrefix(pool_k, pool_v, table, seq_doc)
+
+
+def shared_document_config(seed: int = 0, *, docs: int = 4, per_doc: int = 16, pages: int = 20,
+                           T: int = 2048) -> tuple:
+    """Shared-document decode: `docs` documents of `pages` pages (m = 256 pages + pages - 1 + 16),
+    `per_doc` sequences decoding over each (B = docs x per_doc), n = 128, bf16, token-granular
+    pool in scattered order."""
+    m = pages * TOKENS_PER_PAGE + (pages - 1) + PROMPT_TOKENS
+    B = docs * per_doc
+    name = (f"shared-document R-SWA decode, {docs} documents x {per_doc} sequences (B={B}), "
+            f"{pages} pages (m={m}), n=128, T={T}, bf16, token-granular prefix pool")
+    return make_paged_decode(name, 8, "bf16", [m] * docs, np.repeat(np.arange(docs), per_doc),
+                             [128] * B, [T] * B, seed=seed, scatter=True)
