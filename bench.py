@@ -10,7 +10,8 @@ Also reported: per-step latency vs t, the decode kernel's algorithmic HBM GB/s a
 peak (HIP events around every decode launch on the launch stream), the multi-page growth curve
 (R-SWA vs full causal, --growth), the masked prefill in TFLOP/s against the bf16 MFMA peak, the
 teacher-forced training pass (forward with log-sum-exp, then dQ / dK / dV) on the same 32K
-sequence, and the fp64 oracle timed on a bounded sample on the host cores (cpu_baseline).
+sequence, shared-document decode with the prefixes in a token pool vs copied per sequence, and the
+fp64 oracle timed on a bounded sample on the host cores (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -62,6 +63,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-shared", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--growth", action="store_true", help="multi-page R-SWA vs full-causal curve")
     ap.add_argument("--kernel-events", action="store_true",
@@ -115,20 +117,30 @@ def append_bytes(wl, t: int) -> int:
     return int((wl.steps >= t).sum()) * H * D * e * 4  # k, v read; k, v written
 
 
-def run_decode(args, wl, mode_full: bool, steps: int, warmup: int, kernel_events: bool):
+def run_decode(args, wl, mode_full: bool, steps: int, warmup: int, kernel_events: bool,
+               paged=None):
+    """`paged` (workloads.PagedPrefix): the cache reads the prefixes from the shared token pool
+    through the page table instead of holding copies."""
     import torch
     import windowed_attention_amd as wa
     lib = wa._lib
     dev_q, dev_k, dev_v = upload(wl.q, wl.dtype), upload(wl.k, wl.dtype), upload(wl.v, wl.dtype)
-    pk, pv = upload(wl.prefix_k, wl.dtype), upload(wl.prefix_v, wl.dtype)
     kvdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    if paged is None:
+        pk, pv = upload(wl.prefix_k, wl.dtype), upload(wl.prefix_v, wl.dtype)
+        pool = {}
+    else:
+        pk = pv = None
+        pool = dict(pool_k=upload(paged.pool_k, wl.dtype), pool_v=upload(paged.pool_v, wl.dtype),
+                    prefix_table=torch.from_numpy(paged.table).cuda())
     mode = wa.MODE_FULL_CAUSAL if mode_full else wa.MODE_RSWA
     ragged = bool((wl.steps != wl.steps.max()).any())
     total = warmup + steps
     if total > wl.T:
         raise SystemExit(f"warmup + steps = {total} exceeds the workload's T = {wl.T}")
     cache = wa.RswaCache(pk, pv, wl.prefix_len, None if mode_full else wl.window, mode=mode,
-                         max_steps=wl.steps if mode_full else None, kv_dtype=kvdt)
+                         max_steps=wl.steps if mode_full else None, kv_dtype=kvdt, **pool)
+    del pk, pv
     cache.set_decode_split(args.chunk, args.grid)
     out_dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     out = torch.empty((wl.batch, H, D), dtype=out_dt, device="cuda")
@@ -298,6 +310,32 @@ def pmc_summary(fetch_csv: str, write_csv: str, kind: str):
     return rec
 
 
+def shared_documents(args, warmup=128, steps=1024):
+    """Several sequences decoding over the same documents: prefixes held once in a token pool
+    (paged) vs a copy per sequence. Both read the same rows per step; the paged cache's distinct
+    prefix bytes are those of the documents only."""
+    import workloads as W
+    import torch
+    wl, pp = W.shared_document_config(seed=0)
+    res = dict(workload=wl.name)
+    for kind in ("paged", "copied"):
+        r = run_decode(args, wl, False, steps, warmup, False, paged=pp if kind == "paged" else None)
+        torch.cuda.empty_cache()
+        ms = r["elapsed_ms"] / steps
+        res[kind] = dict(us_per_step=ms * 1e3, tok_s=r["tokens"] / (r["elapsed_ms"] * 1e-3),
+                         requested_gbs=float(r["launch_bytes"].mean()) / (ms * 1e-3) / 1e9)
+    e = 2
+    t_mid = warmup + steps // 2
+    live = int(wl.prefix_len[0]) + 128
+    res["rows_per_step"] = int(wl.batch * live)
+    res["requested_bytes_per_step"] = float(wl.batch * live * 2 * H * D * e)
+    res["distinct_prefix_bytes"] = float(pp.pool_k.nbytes + pp.pool_v.nbytes)
+    res["copied_prefix_bytes"] = float(wl.prefix_k.nbytes + wl.prefix_v.nbytes)
+    res["speedup"] = res["copied"]["us_per_step"] / res["paged"]["us_per_step"]
+    res["t_mid"] = t_mid
+    return res
+
+
 # ------------------------------------------------------------------------------------------------
 # prefill
 # ------------------------------------------------------------------------------------------------
@@ -367,7 +405,7 @@ def run_backward(args):
     S = int(pw.cu_seqlens[-1])
     out = torch.empty((S, H, D), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((S, H), dtype=torch.float32, device="cuda")
-    delta = torch.empty((S, H), dtype=torch.float32, device="cuda")
+    work = torch.empty((2, S, H), dtype=torch.float32, device="cuda")
     grads = [torch.empty((S, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
 
     def fwd():
@@ -375,7 +413,7 @@ def run_backward(args):
 
     def bwd():
         wa.rswa_prefill_bwd(q, k, v, out, dout, lse, cu, m, n, dq=grads[0], dk=grads[1],
-                            dv=grads[2], delta=delta, max_seqlen=S)
+                            dv=grads[2], work=work, max_seqlen=S)
 
     def timed(fn):
         for _ in range(3):
@@ -563,6 +601,10 @@ def main():
         res["ragged"] = ragged_decode(args)
         log(f"[bench] ragged: {res['ragged']['us_per_step']:.1f} us/step, "
             f"{res['ragged']['step_gbs']:.0f} GB/s")
+    if not args.no_decode and not args.no_shared:
+        res["shared_documents"] = sd = shared_documents(args)
+        log(f"[bench] shared documents: paged {sd['paged']['us_per_step']:.1f} us/step, "
+            f"copied {sd['copied']['us_per_step']:.1f} us/step ({sd['speedup']:.2f}x)")
     if not args.no_prefill:
         p = run_prefill(args)
         if p is not None:
