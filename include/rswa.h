@@ -208,6 +208,30 @@ rswa_status rswa_prefill_bwd(const void* q_dev, const void* k_dev, const void* v
                              int32_t head_dim, int32_t max_seqlen, int32_t prefix_causal,
                              float softmax_scale, void* stream);
 
+/* Graph-captured step loop (survey's fused append + decode with a HIP-graph step loop). Capture
+ * `steps` consecutive rswa_decode_step launches of `cache` (no active mask) into a HIP graph:
+ * step i of a replay reads q / k / v from slot i of q_slots / k_slots / v_slots (each [steps][B][H]
+ * [D] of kv_dtype, caller-owned) and writes slot i of out_slots ([steps][B][H][D] of out_dtype).
+ * The caller fills the input slots before each replay. steps must be even (the step counters are
+ * double-buffered, so an even count returns them to the same parity) and at most 4096. The work
+ * split of each step is fixed at capture; the kernels still derive every row range from the
+ * device-side step counters, so replays at any later step are correct. Capture uses a private
+ * stream and enqueues nothing; the graph may be launched on any stream of the cache's device.
+ * Errors: RSWA_E_INVALID, RSWA_E_HIP (capture or instantiation), RSWA_E_INTERNAL. */
+typedef struct rswa_step_graph rswa_step_graph; /* opaque; owned by the library */
+rswa_status rswa_step_graph_create(rswa_cache* cache, int32_t steps, const void* q_slots_dev,
+                                   const void* k_slots_dev, const void* v_slots_dev,
+                                   void* out_slots_dev, int32_t out_dtype, float softmax_scale,
+                                   rswa_step_graph** out);
+
+/* Replay the captured steps on `stream` (appends `steps` outputs to every sequence). In
+ * FULL_CAUSAL mode RSWA_E_CAPACITY if a replay would pass max_steps. */
+rswa_status rswa_step_graph_launch(rswa_step_graph* graph, void* stream);
+
+/* Release the graph (does not synchronize; the caller must not destroy it while a replay that
+ * it enqueued may still be pending). NULL is accepted. */
+rswa_status rswa_step_graph_destroy(rswa_step_graph* graph);
+
 /* Copy the per-sequence step counters t_b to steps_host [B]. BLOCKS until `stream` has passed
  * all prior work. Returns RSWA_E_CAPACITY if a FULL_CAUSAL append past max_steps was skipped on
  * the device since creation (the counters are still copied). */

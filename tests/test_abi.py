@@ -171,3 +171,15 @@ def test_paged_create_checks_arguments_before_device_work(wa):
     d.prefix_paged = 2
     assert lib.rswa_cache_create(ctypes.byref(d), one, one, null, ctypes.byref(h)) == -1
     assert h.value is None
+
+
+def test_step_graph_arguments_are_checked_before_device_work(wa):
+    lib = wa._lib
+    null, one = ctypes.c_void_p(None), ctypes.c_void_p(16)
+    h = ctypes.c_void_p(None)
+    f = ctypes.c_float(0.0)
+    assert lib.rswa_step_graph_create(null, 2, one, one, one, one, 1, f, ctypes.byref(h)) == -1
+    assert lib.rswa_step_graph_create(one, 2, one, one, one, one, 1, f, None) == -1
+    assert lib.rswa_step_graph_launch(null, null) == -1
+    assert lib.rswa_step_graph_destroy(null) == 0
+    assert h.value is None

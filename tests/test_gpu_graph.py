@@ -1,0 +1,106 @@
+"""GPU checks of the graph-captured step loop (rswa_step_graph_*): every replay, with eager work
+(input-slot copies) and a synchronization between replays, must give bit for bit what the same
+fused steps give when launched one by one, including when the captured steps carry the stream-K
+split and its merge launch, and the step counters must advance by the captured count.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_common import Trajectory
+from workloads import to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def wa():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import windowed_attention_amd
+    return windowed_attention_amd
+
+
+def eager(wa, wl, T, mode, split=None, out_dtype=torch.float32):
+    tr = Trajectory(wa, wl, mode)
+    if split:
+        tr.cache.set_decode_split(*split)
+    res = tr.run(range(1, T + 1), out_dtype=out_dtype, t_end=T, fused=True, raw=True)
+    tr.cache.close()
+    return res
+
+
+def replayed(wa, wl, T, G, mode, split=None, out_dtype=torch.float32):
+    tr = Trajectory(wa, wl, mode)
+    if split:
+        tr.cache.set_decode_split(*split)
+    g = wa.StepGraph(tr.cache, G, out_dtype=out_dtype)
+    res = {}
+    for r in range(T // G):
+        t0 = r * G
+        g.q.copy_(tr.q[t0:t0 + G])
+        g.k.copy_(tr.k[t0:t0 + G])
+        g.v.copy_(tr.v[t0:t0 + G])
+        g.launch()
+        torch.cuda.synchronize()
+        for i in range(G):
+            res[t0 + i + 1] = g.out[i].clone()
+    steps = tr.cache.steps()
+    g.close()
+    tr.cache.close()
+    return res, steps
+
+
+# The work split of a captured step is the one chosen at capture. With a fixed grid (or the
+# aligned layout, one workgroup per range) it is the split an eager launch chooses at every step,
+# so replays are bit-identical; an automatic stream-K split can differ while the window fills
+# (same result up to float32 summation order).
+@pytest.mark.parametrize("G,B,split", [(8, 4, (0, 64)), (4, 4, (16, 7)), (2, 4, (0, 32)),
+                                       (8, 48, None)])
+def test_replays_equal_eager_steps(wa, G, B, split):
+    wl = W.make_decode("graph", 10, "bf16", [100] * B, [32] * B, [96] * B, seed=11,
+                       outlier_p=0.01)
+    T = 96
+    ref = eager(wa, wl, T, wa.MODE_RSWA, split)
+    got, steps = replayed(wa, wl, T, G, wa.MODE_RSWA, split)
+    np.testing.assert_array_equal(steps, T)
+    for t in range(1, T + 1):
+        assert torch.equal(got[t].view(torch.int32), ref[t].view(torch.int32)), t
+    for t in (1, 33, 96):  # and the oracle, at a few steps
+        b = t % wl.batch
+        pk, pv = wl.prefix(b)
+        o, _ = O.decode_step(to_f64(wl.q[t - 1, b], "bf16"), to_f64(pk, "bf16"),
+                             to_f64(pv, "bf16"), to_f64(wl.k[:t, b], "bf16"),
+                             to_f64(wl.v[:t, b], "bf16"), t, 32)
+        assert float(np.abs(got[t][b].cpu().numpy() - o).max()) <= 1e-2
+
+
+def test_replays_bf16_output_and_full_causal_capacity(wa):
+    wl = W.make_decode("graph-full", 10, "bf16", [40, 40], [8, 8], [20, 20], seed=12)
+    ref = eager(wa, wl, 20, wa.MODE_FULL_CAUSAL, split=(0, 16), out_dtype=torch.bfloat16)
+    tr = Trajectory(wa, wl, wa.MODE_FULL_CAUSAL)
+    tr.cache.set_decode_split(0, 16)  # a fixed grid: the split eager launches choose too
+    g = wa.StepGraph(tr.cache, 2, out_dtype=torch.bfloat16)
+    for r in range(10):
+        g.q.copy_(tr.q[2 * r:2 * r + 2])
+        g.k.copy_(tr.k[2 * r:2 * r + 2])
+        g.v.copy_(tr.v[2 * r:2 * r + 2])
+        g.launch()
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(g.out[i].view(torch.int16), ref[2 * r + i + 1].view(torch.int16))
+    with pytest.raises(wa.RswaError) as e:  # a replay past max_steps is refused on the host
+        g.launch()
+    assert e.value.status == -3
+    g.close()
+    tr.cache.close()
+
+
+def test_odd_step_count_is_rejected(wa):
+    wl = W.make_decode("graph-odd", 10, "bf16", [8], [4], [4], seed=13)
+    tr = Trajectory(wa, wl, wa.MODE_RSWA)
+    with pytest.raises(wa.RswaError) as e:
+        wa.StepGraph(tr.cache, 3)
+    assert e.value.status == -1
+    tr.cache.close()

@@ -28,6 +28,7 @@ EXPORTS = ("rswa_cache_plan", "rswa_cache_bytes", "rswa_cache_create", "rswa_cac
            "rswa_decode_attn", "rswa_decode_step", "rswa_prefill_attn", "rswa_prefill_fwd",
            "rswa_prefill_bwd", "rswa_cache_steps", "rswa_cache_info",
            "rswa_cache_set_decode_split", "rswa_cache_decode_plan", "rswa_cache_destroy",
+           "rswa_step_graph_create", "rswa_step_graph_launch", "rswa_step_graph_destroy",
            "rswa_status_str",
            "rswa_last_error")
 
@@ -77,6 +78,9 @@ def _load():
         "rswa_cache_set_decode_split": (i32, [vp, i32, i32]),
         "rswa_cache_decode_plan": (i32, [vp, i32, pi32, pi32]),
         "rswa_cache_destroy": (i32, [vp]),
+        "rswa_step_graph_create": (i32, [vp, i32, vp, vp, vp, vp, i32, f32, ctypes.POINTER(vp)]),
+        "rswa_step_graph_launch": (i32, [vp, vp]),
+        "rswa_step_graph_destroy": (i32, [vp]),
         "rswa_status_str": (ctypes.c_char_p, [i32]),
         "rswa_last_error": (ctypes.c_char_p, []),
     }
@@ -370,6 +374,44 @@ def rswa_prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seql
         _dev(window, "window", torch.int32, (nseq,)), nseq, H, D, int(max_seqlen),
         int(bool(prefix_causal)), ctypes.c_float(scale), _stream(stream)), "rswa_prefill_attn")
     return out
+
+
+class StepGraph:
+    """`steps` fused decode steps of a cache captured in a HIP graph (rswa_step_graph_create).
+    Before each replay, write step i's q / k / v into slot i of `q`, `k`, `v` ([steps][B][H][D]);
+    the outputs land in slot i of `out`."""
+
+    def __init__(self, cache: "RswaCache", steps: int, out_dtype: torch.dtype = torch.float32,
+                 scale: float = 0.0):
+        shape = (steps, cache.batch, cache.num_heads, cache.head_dim)
+        dev = torch.device("cuda", torch.cuda.current_device())
+        self.q = torch.zeros(shape, dtype=cache.kv_dtype, device=dev)
+        self.k = torch.zeros_like(self.q)
+        self.v = torch.zeros_like(self.q)
+        self.out = torch.zeros(shape, dtype=out_dtype, device=dev)
+        self.cache = cache
+        self.steps = steps
+        h = ctypes.c_void_p(None)
+        _check(_lib.rswa_step_graph_create(cache.handle, steps, _dev(self.q, "q"), _dev(self.k, "k"),
+                                           _dev(self.v, "v"), _dev(self.out, "out"),
+                                           _dtype_code(out_dtype), ctypes.c_float(scale),
+                                           ctypes.byref(h)), "rswa_step_graph_create")
+        self._h = h
+
+    def launch(self, stream=None) -> None:
+        _check(_lib.rswa_step_graph_launch(self._h, _stream(stream)), "rswa_step_graph_launch")
+
+    def close(self) -> None:
+        if self._h is not None:
+            torch.cuda.synchronize()
+            _lib.rswa_step_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def _max_seqlen(cu_seqlens: torch.Tensor, max_seqlen: int | None) -> int:

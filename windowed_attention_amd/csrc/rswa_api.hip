@@ -464,6 +464,124 @@ rswa_status rswa_decode_step(rswa_cache* c, const void* q_dev, const void* k_dev
                        stream, "rswa_decode_step");
 }
 
+struct rswa_step_graph {
+  rswa_cache* c = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  int32_t steps = 0;
+};
+
+namespace {
+
+void release_graph(rswa_step_graph* g) {
+  if (!g) return;
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
+  delete g;
+}
+
+}  // namespace
+
+rswa_status rswa_step_graph_create(rswa_cache* c, int32_t steps, const void* q_slots,
+                                   const void* k_slots, const void* v_slots, void* out_slots,
+                                   int32_t out_dtype, float softmax_scale,
+                                   rswa_step_graph** out) {
+  if (!out) return fail(RSWA_E_INVALID, "out is NULL");
+  *out = nullptr;
+  if (!c) return fail(RSWA_E_INVALID, "cache is NULL");
+  if (steps < 2 || steps > 4096 || (steps & 1))
+    return fail(RSWA_E_INVALID, "steps must be even, in [2, 4096]");
+  if (!q_slots || !k_slots || !v_slots || !out_slots)
+    return fail(RSWA_E_INVALID, "q / k / v / out slot pointer is NULL");
+  if (out_dtype != RSWA_BF16 && out_dtype != RSWA_F32)
+    return fail(RSWA_E_INVALID, "out_dtype must be RSWA_BF16 or RSWA_F32");
+  rswa_step_graph* g = nullptr;
+  hipStream_t cs = nullptr;
+  const std::vector<int64_t> calls = c->calls;
+  const int cur = c->cur;
+  try {
+    DeviceGuard dg(c->device);
+    g = new rswa_step_graph();
+    g->c = c;
+    g->steps = steps;
+    hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+    if (e != hipSuccess) {
+      release_graph(g);
+      return hip_fail(e, "hipStreamCreateWithFlags(capture)");
+    }
+    const size_t elem = c->kv_dtype == RSWA_F32 ? 4 : 2;
+    const size_t slot = (size_t)c->B * c->H * c->D;
+    const size_t oelem = out_dtype == RSWA_F32 ? 4 : 2;
+    e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) {
+      (void)hipStreamDestroy(cs);
+      release_graph(g);
+      return hip_fail(e, "hipStreamBeginCapture");
+    }
+    rswa_status st = RSWA_OK;
+    for (int i = 0; i < steps && st == RSWA_OK; ++i) {
+      const char* q = reinterpret_cast<const char*>(q_slots) + i * slot * elem;
+      const char* k = reinterpret_cast<const char*>(k_slots) + i * slot * elem;
+      const char* v = reinterpret_cast<const char*>(v_slots) + i * slot * elem;
+      char* o = reinterpret_cast<char*>(out_slots) + i * slot * oelem;
+      st = decode_launch(c, q, k, v, o, out_dtype, softmax_scale, nullptr, cs,
+                         "rswa_step_graph_create");
+    }
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(cs, &graph);
+    g->graph = graph;
+    // capture enqueues nothing: the host view of the cache stays where it was
+    c->calls = calls;
+    c->cur = cur;
+    if (st != RSWA_OK || e != hipSuccess) {
+      (void)hipStreamDestroy(cs);
+      release_graph(g);
+      return st != RSWA_OK ? st : hip_fail(e, "hipStreamEndCapture");
+    }
+    e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
+    (void)hipStreamDestroy(cs);
+    if (e != hipSuccess) {
+      g->exec = nullptr;
+      release_graph(g);
+      return hip_fail(e, "hipGraphInstantiate");
+    }
+    *out = g;
+    return RSWA_OK;
+  } catch (...) {
+    c->calls = calls;
+    c->cur = cur;
+    if (cs) (void)hipStreamDestroy(cs);
+    release_graph(g);
+    return fail(RSWA_E_INTERNAL, "exception in rswa_step_graph_create");
+  }
+}
+
+rswa_status rswa_step_graph_launch(rswa_step_graph* g, void* stream) {
+  if (!g) return fail(RSWA_E_INVALID, "graph is NULL");
+  rswa_cache* c = g->c;
+  try {
+    if (c->full()) {
+      for (int b = 0; b < c->B; ++b)
+        if (c->calls[b] + g->steps > c->plan.cap[b])
+          return fail(RSWA_E_CAPACITY, "full-causal append past max_steps");
+    }
+    DeviceGuard dg(c->device);
+    const hipError_t e = hipGraphLaunch(g->exec, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+    for (int b = 0; b < c->B; ++b) c->calls[b] += g->steps;
+    return RSWA_OK;
+  } catch (...) {
+    return fail(RSWA_E_INTERNAL, "exception in rswa_step_graph_launch");
+  }
+}
+
+rswa_status rswa_step_graph_destroy(rswa_step_graph* g) {
+  if (!g) return RSWA_OK;
+  DeviceGuard dg(g->c->device);
+  release_graph(g);
+  return RSWA_OK;
+}
+
 rswa_status rswa_cache_steps(rswa_cache* c, int32_t* steps_host, void* stream) {
   if (!c || !steps_host) return fail(RSWA_E_INVALID, "cache / steps_host is NULL");
   try {
