@@ -64,6 +64,7 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-shared", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--growth", action="store_true", help="multi-page R-SWA vs full-causal curve")
     ap.add_argument("--kernel-events", action="store_true",
@@ -336,6 +337,64 @@ def shared_documents(args, warmup=128, steps=1024):
     return res
 
 
+def graph_loop(args, G=64, replays=6):
+    """Fused decode steps launched one by one vs replayed from a captured HIP graph of G steps
+    (input slots filled once; timing only). Same workloads as the single-page fp32 (B = 1) and
+    the headline batched decode."""
+    import torch
+    import windowed_attention_amd as wa
+    import workloads as W
+    res = {}
+    for name, wl in (("single", W.decode_config(1)), ("batched", W.decode_config(2, T=1200))):
+        kvdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        q, k, v = upload(wl.q, wl.dtype), upload(wl.k, wl.dtype), upload(wl.v, wl.dtype)
+        out = torch.empty((wl.batch, H, D), dtype=torch.float32, device="cuda")
+        times = {}
+        for kind in ("eager", "graph"):
+            pk, pv = upload(wl.prefix_k, wl.dtype), upload(wl.prefix_v, wl.dtype)
+            cache = wa.RswaCache(pk, pv, wl.prefix_len, wl.window, kv_dtype=kvdt)
+            if kind == "graph":
+                g = wa.StepGraph(cache, G)
+                g.q.copy_(q[:G])
+                g.k.copy_(k[:G])
+                g.v.copy_(v[:G])
+                g.launch()  # warmup
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for _ in range(replays):
+                    g.launch()
+                b.record()
+                torch.cuda.synchronize()
+                times[kind] = a.elapsed_time(b) * 1e3 / (G * replays)
+                g.close()
+            else:  # raw C-ABI calls, as in the headline measurement
+                lib, h = wa._lib, cache.handle
+                sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+                sb = wl.batch * H * D * q.element_size()
+                qb, kb, vb, ob = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()
+                zero = ctypes.c_float(0.0)
+
+                def step(t):
+                    o = t * sb
+                    if lib.rswa_decode_step(h, qb + o, kb + o, vb + o, ob, wa.F32, zero, None, sp):
+                        raise RuntimeError(lib.rswa_last_error())
+                for t in range(G):
+                    step(t)
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for t in range(G, G + G * replays):
+                    step(t)
+                b.record()
+                torch.cuda.synchronize()
+                times[kind] = a.elapsed_time(b) * 1e3 / (G * replays)
+            cache.close()
+        res[name] = dict(workload=wl.name, eager_us_per_step=times["eager"],
+                         graph_us_per_step=times["graph"], graph_steps=G)
+    return res
+
+
 # ------------------------------------------------------------------------------------------------
 # prefill
 # ------------------------------------------------------------------------------------------------
@@ -605,6 +664,11 @@ def main():
         res["shared_documents"] = sd = shared_documents(args)
         log(f"[bench] shared documents: paged {sd['paged']['us_per_step']:.1f} us/step, "
             f"copied {sd['copied']['us_per_step']:.1f} us/step ({sd['speedup']:.2f}x)")
+    if not args.no_decode and not args.no_graph:
+        res["graph_loop"] = gl = graph_loop(args)
+        for k2, r2 in gl.items():
+            log(f"[bench] graph loop {k2}: eager {r2['eager_us_per_step']:.2f} us/step, "
+                f"graph {r2['graph_us_per_step']:.2f} us/step")
     if not args.no_prefill:
         p = run_prefill(args)
         if p is not None:
