@@ -34,8 +34,15 @@ PEAK_BF16_TFLOPS = 2500.0
 H, D = 16, 128
 DECODE_SOURCES = ["windowed_attention_amd/csrc/decode.hip", "windowed_attention_amd/csrc/device.h",
                   "windowed_attention_amd/csrc/kernels.h"]
-PREFILL_SOURCES = ["windowed_attention_amd/csrc/prefill.hip",
+PREFILL_SOURCES = ["windowed_attention_amd/csrc/prefill.hip", "windowed_attention_amd/csrc/mfma.h",
                    "windowed_attention_amd/csrc/device.h", "windowed_attention_amd/csrc/kernels.h"]
+BACKWARD_SOURCES = ["windowed_attention_amd/csrc/prefill_bwd.hip",
+                    "windowed_attention_amd/csrc/mfma.h", "windowed_attention_amd/csrc/device.h",
+                    "windowed_attention_amd/csrc/kernels.h"]
+KIND_SOURCES = {"decode": DECODE_SOURCES, "prefill": PREFILL_SOURCES,
+                "backward": BACKWARD_SOURCES}
+KIND_KERNELS = {"decode": ("decode_kernel",), "prefill": ("prefill_kernel",),
+                "backward": ("delta_kernel", "dkdv_kernel", "dq_kernel")}
 
 
 def log(*a):
@@ -297,17 +304,20 @@ def pmc_summary(fetch_csv: str, write_csv: str, kind: str):
         raise SystemExit("no calibration copy dispatch in the counter CSV (run with --copy-calibration)")
     cf = (1 << 30) / (max(fetch[copy_k[0]]) * 1024.0)
     cw = (1 << 30) / (max(write[copy_k[0]]) * 1024.0)
-    names = [k for k in fetch if f"{kind}_kernel" in k]
+    names = [k for k in fetch if any(f"::{n}<" in k for n in KIND_KERNELS[kind])]
     rec = dict(kernel_names=names, copy_kernel=copy_k[0], fetch_scale=cf, write_scale=cw)
     for k in names:
         f = np.array(fetch[k]) * 1024.0 * cf
         w = np.array(write.get(k, [0.0])) * 1024.0 * cw
         rec[k] = dict(dispatches=int(f.size), fetch_bytes_median=float(np.median(f)),
                       write_bytes_median=float(np.median(w)))
-    main = max(names, key=lambda k: rec[k]["fetch_bytes_median"])
-    rec["bytes_per_launch"] = rec[main]["fetch_bytes_median"] + rec[main]["write_bytes_median"]
-    src = DECODE_SOURCES if kind == "decode" else PREFILL_SOURCES
-    rec["source_hash"] = source_hash(src)
+    if kind == "backward":  # the backward call: its three launches together
+        rec["bytes_per_launch"] = sum(rec[k]["fetch_bytes_median"] + rec[k]["write_bytes_median"]
+                                      for k in names)
+    else:
+        main = max(names, key=lambda k: rec[k]["fetch_bytes_median"])
+        rec["bytes_per_launch"] = rec[main]["fetch_bytes_median"] + rec[main]["write_bytes_median"]
+    rec["source_hash"] = source_hash(KIND_SOURCES[kind])
     return rec
 
 
@@ -498,7 +508,9 @@ def run_backward(args):
     return dict(workload=pw.name + ", forward + backward, bf16 gradients", fwd_ms=fwd_ms,
                 bwd_ms=bwd_ms, bwd_tflops=tflops, train_tflops=train, bwd_flop=bflop,
                 roofline=dict(bound="mfma", achieved=tflops, peak=PEAK_BF16_TFLOPS,
-                              unit="TFLOP/s", frac=tflops / PEAK_BF16_TFLOPS, traffic=None,
+                              unit="TFLOP/s", frac=tflops / PEAK_BF16_TFLOPS,
+                              traffic=traffic_from_profile("backward",
+                                                           source_hash(BACKWARD_SOURCES)),
                               kernel="backward call (delta + dK/dV + dQ launches)"))
 
 
