@@ -334,3 +334,23 @@ def test_sink_tokens_decode(wa):
     got = tr.run(range(1, T + 1), fused=True)
     check_steps(wl, 0, got)
     tr.cache.close()
+
+
+def test_maximum_batch(wa):
+    """The largest batch a cache accepts (2048 sequences), ragged prefixes and windows, through
+    the fused step; sampled sequences at every step against the oracle."""
+    B = 2048
+    rng = np.random.default_rng(31)
+    m = rng.integers(0, 40, size=B)
+    n = rng.integers(1, 24, size=B)
+    m[0] = 0  # a sequence with no prefix
+    wl = W.make_decode("maxbatch", 88, "bf16", m, n, [20] * B, seed=31)
+    tr = Trajectory(wa, wl, wa.MODE_RSWA)
+    got = tr.run(range(1, 21), fused=True)
+    check_steps(wl, 0, got, seqs_per_step=24, seed=3)
+    for t in (1, 20):
+        o, _ = oracle_out(wl, t, 0, 0)
+        assert float(np.abs(got[t][0] - o).max()) <= TOL["bf16"]
+    tr.cache.close()
+    with pytest.raises(wa.RswaError):
+        wa.rswa_cache_plan([4] * (B + 1), [4] * (B + 1))
