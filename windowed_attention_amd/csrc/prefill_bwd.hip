@@ -75,6 +75,9 @@ __global__ __launch_bounds__(256) void delta_kernel(const OT* __restrict__ out,
 // ------------------------------------------------------------------------------------------
 // dK / dV: key-parallel
 // ------------------------------------------------------------------------------------------
+#ifndef RSWA_BWD_LEAN
+#define RSWA_BWD_LEAN 1  // dP accumulated on -delta; element masks only where needed
+#endif
 #ifndef RSWA_KV_WAVES
 #define RSWA_KV_WAVES 4  // waves per workgroup, 32 keys each
 #endif
@@ -179,6 +182,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
   const int qlo = k0 < m ? (pc ? k0 : 0) : k0;
   const int qhi = k0 < m ? S : min(S, klast + n);
   const int ntiles = (qhi - qlo + BMQ - 1) / BMQ;
+  const bool wave_pre = wk0 + 32 <= min(m, S);  // all of the wave's keys are prefix keys
 
   const float c = a.scale_log2;
   floatx16 dk[4], dv[4];
@@ -211,7 +215,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
   // LDS latency. A query is visible to this lane's key iff it lies in [plo, phi), tested as one
   // unsigned range check.
   auto qblock = [&](const uint16_t* sq, const uint16_t* sg, const float* sl,
-                    const float* sd, int qb, int pb0) {
+                    const float* sd, int qb, int pb0, bool masked) {
     __builtin_amdgcn_sched_barrier(0);  // blocks do not interleave: registers stay bounded
     u32x4 af[16];
 #pragma unroll
@@ -228,7 +232,18 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
     __builtin_amdgcn_sched_barrier(0);
     floatx16 sacc, dpacc;
     zero16(sacc);
+#if RSWA_BWD_LEAN
+    // dP accumulates on top of -delta, so the chain yields dP - delta directly
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      dpacc[4 * g + 0] = -d4[g].x;
+      dpacc[4 * g + 1] = -d4[g].y;
+      dpacc[4 * g + 2] = -d4[g].z;
+      dpacc[4 * g + 3] = -d4[g].w;
+    }
+#else
     zero16(dpacc);
+#endif
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       sacc = mfma32(af[2 * st], kf[st], sacc);
@@ -250,6 +265,26 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
     const uint32_t p_rel = (uint32_t)(pb0 + 4 * half - plo);
     const uint32_t p_width = (uint32_t)(phi - plo);
     float pr[16], ds[16];
+#if RSWA_BWD_LEAN
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float lv[4] = {l4[g].x, l4[g].y, l4[g].z, l4[g].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        pr[r] = fast_exp2(fmaf(sacc[r], c, -lv[i]));
+        ds[r] = pr[r] * dpacc[r];
+      }
+    }
+    if (masked) {  // uniform: only blocks that straddle a visibility boundary
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool vis = p_rel + (uint32_t)(8 * (r >> 2) + (r & 3)) < p_width;
+        pr[r] = vis ? pr[r] : 0.f;
+        ds[r] = vis ? ds[r] : 0.f;
+      }
+    }
+#else
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const float lv[4] = {l4[g].x, l4[g].y, l4[g].z, l4[g].w};
@@ -263,6 +298,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
         ds[r] = x * (dpacc[r] - dv4[i]);
       }
     }
+#endif
     const u32x4 pb[2] = {pack_b(pr, 0), pack_b(pr, 1)};
     const u32x4 sb[2] = {pack_b(ds, 0), pack_b(ds, 1)};
 #pragma unroll
@@ -290,7 +326,11 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
       for (int qb = 0; qb < BMQ / 32; ++qb) {
         const int pb0 = qt0 + qb * 32;
         // uniform per wave: skip blocks that none of the wave's keys can see
-        if (pb0 < wq_hi && pb0 + 32 > wq_lo) qblock(sq, sg, sl, sd, qb, pb0);
+        // every (query, key) pair of the block is visible when the wave's keys are all prefix
+        // keys, the block's queries all exist and (causal prefix) follow the wave's last key
+        const bool masked =
+            !(wave_pre && pb0 + 32 <= S && (!pc || pb0 >= wk0 + 31));
+        if (pb0 < wq_hi && pb0 + 32 > wq_lo) qblock(sq, sg, sl, sd, qb, pb0, masked);
       }
     }
     // tile j + 1 must have landed; tile j + 2's pieces may still be in flight
@@ -417,11 +457,16 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
   // accumulator rows, this lane's query in the column), dS^T in registers, dQ^T += K^T dS^T.
   // A key is visible iff it lies in [lo, hi], tested as one unsigned range check.
   auto kblock = [&](const uint16_t* sk, const uint16_t* sv, int kb, int k0, int lo,
-                    int hi) {
+                    int hi, bool masked) {
     __builtin_amdgcn_sched_barrier(0);  // blocks do not interleave: registers stay bounded
     floatx16 sacc, dpacc;
     zero16(sacc);
+#if RSWA_BWD_LEAN
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dpacc[r] = -dlt;  // the chain yields dP - delta
+#else
     zero16(dpacc);
+#endif
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       const u32x4 ka = swz_ld_a(sk, sl_, kb * 32, st);
@@ -446,12 +491,22 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
     const uint32_t k_rel = (uint32_t)(k0 + kb * 32 + 4 * half - lo);
     const uint32_t k_width = (uint32_t)max(hi - lo + 1, 0);
     float ds[16];
+#if RSWA_BWD_LEAN
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(fmaf(sacc[r], c, -lse2)) * dpacc[r];
+    if (masked) {  // uniform: only tiles that are not wholly visible
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        ds[r] = (k_rel + (uint32_t)(8 * (r >> 2) + (r & 3)) < k_width) ? ds[r] : 0.f;
+    }
+#else
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float x = fast_exp2(fmaf(sacc[r], c, -lse2));
       x = (k_rel + (uint32_t)(8 * (r >> 2) + (r & 3)) < k_width) ? x : 0.f;
       ds[r] = x * (dpacc[r] - dlt);
     }
+#endif
     const u32x4 sb[2] = {pack_b(ds, 0), pack_b(ds, 1)};
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -475,8 +530,10 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
     // sees and spills.
     const int lo = is_pre ? 0 : win_lo;
     const int hi = is_pre ? pre_hi : p;
-    kblock(sk, sv, 0, k0, lo, hi);
-    kblock(sk, sv, 1, k0, lo, hi);
+    // uniform per tile: prefix tiles that every query of the workgroup sees whole need no mask
+    const bool masked = is_pre ? (k0 + BN > m || (pc && q0 < m && k0 + BN - 1 > q0)) : true;
+    kblock(sk, sv, 0, k0, lo, hi, masked);
+    kblock(sk, sv, 1, k0, lo, hi, masked);
     if (j + 2 < ntiles)
       dma_wait_barrier<kDqPieces>();
     else
