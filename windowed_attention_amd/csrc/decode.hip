@@ -18,8 +18,10 @@
 //      o = sum_s 2^(M_s - M) A_s / sum_s 2^(M_s - M) l_s,   M = max_s M_s.
 //
 // Inside a piece. A row of K or V is 256 B (bf16) or 512 B (fp32): 16 or 32 lanes each load 16 B of
-// it, so a wave streams 4 (bf16) or 2 (fp32) rows per load instruction, 1 KiB contiguous, and the
-// next tile's rows are loaded while the current one is reduced. Each lane group keeps its own
+// it, so a wave streams 4 (bf16) or 2 (fp32) rows per load instruction, 1 KiB contiguous. Load
+// latency is covered by the other resident waves of the CU (loading the next tile into registers
+// ahead of the current one's reduction, RSWA_DECODE_PREFETCH=1, measured no faster and costs
+// registers, so it is off). Each lane group keeps its own
 // float32 online-softmax state (running max in the log2 domain, running sum, 8 or 4 output dims);
 // q.k partial dot products are summed across the group with DPP row operations. At the end of a
 // range the group states are merged through LDS.

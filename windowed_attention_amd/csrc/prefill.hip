@@ -10,17 +10,20 @@
 // masks are applied only on tiles that need them (the prefix's ragged last tile, the causal-prefix
 // diagonal, and the window tiles).
 //
-// Tiling. A 256-thread workgroup owns 128 queries of one (sequence, head); each wave owns 32.
+// Tiling. A workgroup of RSWA_PF_WAVES waves (8: 512 threads, two waves per SIMD) owns 32 queries
+// per wave of one (sequence, head).
 // Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: the accumulator puts one
 // query per lane (lane % 32) and 16 of the block's 32 keys in that lane's registers, so the softmax
 // max/sum over keys is in-lane plus one exchange with lane ^ 32. The output is also formed
 // transposed, O^T = V^T P^T: the score accumulator registers, rounded to bf16, are already the B
 // operand of the second MFMA (the key order inside a 16-key step is a permutation that the V^T
 // operand follows), so P never leaves registers. K and V tiles (64 keys x 128) are
-// double-buffered in LDS, both row-major; the V^T operand comes out of gfx950's transposing LDS
-// read, so V needs no transpose on the way in. Q stays in registers for the whole key loop.
-// Softmax runs in the log2 domain in float32; P is rounded to bf16 for the PV product and the
-// output is normalised by the float32 row sum.
+// double-buffered in LDS, both row-major (rows padded against bank conflicts), and loaded two
+// tiles ahead; the V^T operand comes out of gfx950's transposing LDS read, so V needs no transpose
+// on the way in. Q stays in registers for the whole key loop. Softmax runs in the log2 domain in
+// float32 with a lazily moved reference max; P is rounded to bf16 for the PV product and the
+// output is normalised by the float32 row sum. With a non-null lse the natural log-sum-exp of
+// each query's scaled scores is written too (the training pass needs it).
 #include "kernels.h"
 #include "mfma.h"
 
