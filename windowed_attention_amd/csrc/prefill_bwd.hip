@@ -17,7 +17,9 @@
 //     registers (B operands) and its dK^T, dV^T accumulators in registers, and streams the query
 //     tiles that can see its keys (every query for a prefix key, the n queries of the window for
 //     an output key) through LDS: Q and dO tiles row-major, read both straight (S = Q K^T,
-//     dP = dO V^T) and through the transposing LDS read (dV^T = dO^T P, dK^T = Q^T dS).
+//     dP = dO V^T) and through the transposing LDS read (dV^T = dO^T P, dK^T = Q^T dS). The
+//     loop over 32-query blocks is software-pipelined: S and dP of the next block are issued
+//     while P and dS of the current block are formed.
 //   dQ: query-parallel, the forward's tiling: Q and dO of 32 queries per wave in registers, K and
 //     V tiles of the prefix segment and the window segment through LDS, S^T = K Q^T,
 //     dP^T = V dO^T, dQ^T = K^T dS^T (K^T from the transposing read).
@@ -29,6 +31,9 @@ namespace rswa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Scheduling fence: the interleave of MFMAs, LDS reads and vector-ALU work stays as written.
+#define FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // ------------------------------------------------------------------------------------------
 // delta_p = rowsum(dO * O) per (token, head) row: 16 lanes x 8 dims per row
@@ -75,9 +80,6 @@ __global__ __launch_bounds__(256) void delta_kernel(const OT* __restrict__ out,
 // ------------------------------------------------------------------------------------------
 // dK / dV: key-parallel
 // ------------------------------------------------------------------------------------------
-#ifndef RSWA_BWD_LEAN
-#define RSWA_BWD_LEAN 1  // dP accumulated on -delta; element masks only where needed
-#endif
 #ifndef RSWA_KV_WAVES
 #define RSWA_KV_WAVES 4  // waves per workgroup, 32 keys each
 #endif
@@ -110,13 +112,18 @@ __device__ __forceinline__ void dma_qtile(uint16_t* sq, uint16_t* sg, float* sl,
   }
 }
 
+
+// Each wave walks every 32-query block of the workgroup's query range (blocks its keys cannot see
+// are masked out); step b issues S and dP of block b + 1 in between the vector-ALU work of block b
+// (P, dS and their bf16 packing), then dV^T and dK^T of block b, so a wave's matrix cores are fed
+// while its P / dS are formed. Four buffer sets: the copy of tile j + 3 goes out at the middle of
+// tile j, after the barrier that retires tile j - 1's buffers.
 template <typename OUT>
 __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
-  // three buffer sets: the DMA for tile j + 2 runs while tile j is computed
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[3 * Q_TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sG[3 * Q_TILE];
-  __shared__ __attribute__((aligned(16))) float sL[3 * BMQ];
-  __shared__ __attribute__((aligned(16))) float sD[3 * BMQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[4 * Q_TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sG[4 * Q_TILE];
+  __shared__ __attribute__((aligned(16))) float sL[4 * BMQ];
+  __shared__ __attribute__((aligned(16))) float sD[4 * BMQ];
 
   // key blocks outermost across heads: the prefix blocks (long query loops) start first
   const int idx = blockIdx.x;
@@ -131,12 +138,9 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
   const int n = a.window[s];
   const bool pc = a.prefix_causal != 0;
 
-  // the wave index is uniform: readfirstlane lets the compiler keep every per-wave decision
-  // (which query blocks the wave's keys see, whether a tile needs the element mask) in scalar
-  // registers and branch on it instead of masking lanes
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lq = lane & 31, half = lane >> 5;
+  const int half = lane >> 5;
   const int64_t rs = (int64_t)a.heads * kHeadDim;
   const int64_t hoff = ((int64_t)cu0 * a.heads + h) * kHeadDim;
   const uint16_t* qbase = a.q + hoff;
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
 
   // this lane's key and its K / V rows as B operands (8 d-steps of 16)
   const int wk0 = k0 + wave * 32;
-  const int kw = wk0 + lq;
+  const int kw = wk0 + (lane & 31);
   u32x4 kf[8], vf[8];
   {
     const int kc = min(kw, S - 1);
@@ -171,13 +175,6 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
     plo = kw;
     phi = min(S, kw + n);
   }
-  // ... and the union over this wave's keys, and over the workgroup's
-  int wq_lo = 0, wq_hi = 0;
-  if (wk0 < S) {
-    const int wlast = min(wk0 + 31, S - 1);
-    wq_lo = wk0 < m ? (pc ? wk0 : 0) : wk0;
-    wq_hi = wk0 < m ? S : min(S, wlast + n);
-  }
   const int klast = min(k0 + BNK, S) - 1;
   const int qlo = k0 < m ? (pc ? k0 : 0) : k0;
   const int qhi = k0 < m ? S : min(S, klast + n);
@@ -191,153 +188,146 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
     zero16(dk[db]);
     zero16(dv[db]);
   }
-
   const SwzLane sl_(lane);
 
   auto issue = [&](int j) {
-    const int b = j % 3;
+    const int b = j & 3;
     dma_qtile(sQ + b * Q_TILE, sG + b * Q_TILE, sL + b * BMQ, sD + b * BMQ, qbase, gbase, lse,
               dlt, rs, a.heads, qlo + j * BMQ, S - 1, wave, lane);
   };
-  issue(0);
-  if (ntiles > 1) {
-    issue(1);
-    dma_wait_barrier<kKvPieces>();
-  } else {
-    dma_wait_barrier<0>();
-  }
 
-  // One 32-query block of the tile in LDS buffers (sq, sg, sl, sd): S = Q K^T and dP = dO V^T
-  // (queries in accumulator rows, this lane's key in the column), P and dS in registers, then
-  // dV^T += dO^T P and dK^T += Q^T dS. Every LDS operand is requested ahead of the MFMA that
-  // uses it: the sixteen straight fragments and lse / delta before the score chain, the sixteen
-  // transposed fragments while it runs, so one wave per SIMD runs at LDS throughput rather than
-  // LDS latency. A query is visible to this lane's key iff it lies in [plo, phi), tested as one
-  // unsigned range check.
-  auto qblock = [&](const uint16_t* sq, const uint16_t* sg, const float* sl,
-                    const float* sd, int qb, int pb0, bool masked) {
-    __builtin_amdgcn_sched_barrier(0);  // blocks do not interleave: registers stay bounded
-    u32x4 af[16];
+  // Scores of block b (queries qlo + 32 b + ...) that this lane's key cannot see set to -inf,
+  // where the block is not fully visible (uniform per wave); P and dS are then exactly zero.
+  // Accumulator register r holds query pb0 + 8 (r / 4) + 4 half + r % 4.
+  auto mask_block = [&](floatx16& sc, int b) {
+    const int pb0 = qlo + 32 * b;
+    const bool masked = !(wave_pre && pb0 + 32 <= S && (!pc || pb0 >= wk0 + 31));
+    if (masked) {
+      const uint32_t p_rel = (uint32_t)(pb0 + 4 * half - plo);
+      const uint32_t p_width = (uint32_t)(phi - plo);
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      af[2 * st] = swz_ld_a(sq, sl_, qb * 32, st);
-      af[2 * st + 1] = swz_ld_a(sg, sl_, qb * 32, st);
+      for (int r = 0; r < 16; ++r)
+        sc[r] = p_rel + (uint32_t)(8 * (r >> 2) + (r & 3)) < p_width ? sc[r] : -INFINITY;
     }
+  };
+
+  // One step: S and dP - delta of the next block (rows rn of tile buffers qn / gn / dn_) into
+  // sn / dn under P, dS of the current block (scores sc, dc; rows rc of qc / gc / lc), then
+  // dV^T += dO^T P and dK^T += Q^T dS for the current block.
+  auto step = [&](floatx16& sc, floatx16& dc, floatx16& sn, floatx16& dn, const uint16_t* qn,
+                  const uint16_t* gn, const float* dn_, int rn, const uint16_t* qc,
+                  const uint16_t* gc, const float* lc, int rc) {
     float4 l4[4], d4[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      l4[g] = *reinterpret_cast<const float4*>(sl + qb * 32 + 8 * g + 4 * half);
-      d4[g] = *reinterpret_cast<const float4*>(sd + qb * 32 + 8 * g + 4 * half);
+      l4[g] = *reinterpret_cast<const float4*>(lc + rc + 8 * g + 4 * half);
+      d4[g] = *reinterpret_cast<const float4*>(dn_ + rn + 8 * g + 4 * half);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    floatx16 sacc, dpacc;
-    zero16(sacc);
-#if RSWA_BWD_LEAN
-    // dP accumulates on top of -delta, so the chain yields dP - delta directly
+    u32x4 fq[3], fg[3];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      dpacc[4 * g + 0] = -d4[g].x;
-      dpacc[4 * g + 1] = -d4[g].y;
-      dpacc[4 * g + 2] = -d4[g].z;
-      dpacc[4 * g + 3] = -d4[g].w;
+    for (int i = 0; i < 3; ++i) {
+      fq[i] = swz_ld_a(qn, sl_, rn, i);
+      fg[i] = swz_ld_a(gn, sl_, rn, i);
     }
-#else
-    zero16(dpacc);
-#endif
+    FENCE();
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      sacc = mfma32(af[2 * st], kf[st], sacc);
-      dpacc = mfma32(af[2 * st + 1], vf[st], dpacc);
+    for (int g = 0; g < 4; ++g) {  // dP accumulates on top of -delta: the chain yields dP - delta
+      dn[4 * g + 0] = -d4[g].x;
+      dn[4 * g + 1] = -d4[g].y;
+      dn[4 * g + 2] = -d4[g].z;
+      dn[4 * g + 3] = -d4[g].w;
     }
-    // the transposed reads go out once the score MFMAs are issued (the straight fragments are
-    // then dead) and arrive while the softmax waits for the scores
-    __builtin_amdgcn_sched_barrier(0);
-    u32x4 tg[8], tq[8];
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        tg[2 * db + st] = swz_ld_tr(sg, sl_, qb * 32 + 16 * st, db);
-        tq[2 * db + st] = swz_ld_tr(sq, sl_, qb * 32 + 16 * st, db);
-      }
-    __builtin_amdgcn_sched_barrier(0);
-    // accumulator register r: query pb0 + 8 (r / 4) + 4 half + r % 4, key kw
-    const uint32_t p_rel = (uint32_t)(pb0 + 4 * half - plo);
-    const uint32_t p_width = (uint32_t)(phi - plo);
     float pr[16], ds[16];
-#if RSWA_BWD_LEAN
+    u32x4 pb[2], sb[2], tg[2], tq[2];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float lv[4] = {l4[g].x, l4[g].y, l4[g].z, l4[g].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g + i;
-        pr[r] = fast_exp2(fmaf(sacc[r], c, -lv[i]));
-        ds[r] = pr[r] * dpacc[r];
+    for (int i = 0; i < 8; ++i) {
+      sn = mfma32(fq[i % 3], kf[i], i == 0 ? floatx16{} : sn);
+      dn = mfma32(fg[i % 3], vf[i], dn);
+      if (i + 3 < 8) {
+        fq[i % 3] = swz_ld_a(qn, sl_, rn, i + 3);
+        fg[i % 3] = swz_ld_a(gn, sl_, rn, i + 3);
       }
+#pragma unroll
+      for (int e = 2 * i; e < 2 * i + 2; ++e) {
+        const float lv = (e & 3) == 0 ? l4[e >> 2].x : (e & 3) == 1 ? l4[e >> 2].y
+                                                      : (e & 3) == 2 ? l4[e >> 2].z : l4[e >> 2].w;
+        pr[e] = fast_exp2(fmaf(sc[e], c, -lv));
+        ds[e] = pr[e] * dc[e];
+      }
+      if (i == 4) {
+        pb[0] = pack_b(pr, 0);
+        sb[0] = pack_b(ds, 0);
+      }
+      if (i >= 8 - 2) {  // transposed operands of the first products of the second half
+        const int k = i - (8 - 2);  // pair k: d block k / 2, key step k % 2
+        tg[k] = swz_ld_tr(gc, sl_, rc + 16 * (k & 1), k >> 1);
+        tq[k] = swz_ld_tr(qc, sl_, rc + 16 * (k & 1), k >> 1);
+      }
+      FENCE();
     }
-    if (masked) {  // uniform: only blocks that straddle a visibility boundary
+    pb[1] = pack_b(pr, 1);
+    sb[1] = pack_b(ds, 1);
+    FENCE();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool vis = p_rel + (uint32_t)(8 * (r >> 2) + (r & 3)) < p_width;
-        pr[r] = vis ? pr[r] : 0.f;
-        ds[r] = vis ? ds[r] : 0.f;
+    for (int k = 0; k < 8; ++k) {
+      const int db = k >> 1, st = k & 1;
+      dv[db] = mfma32(tg[k % 2], pb[st], dv[db]);
+      dk[db] = mfma32(tq[k % 2], sb[st], dk[db]);
+      if (k + 2 < 8) {
+        const int kk = k + 2;
+        tg[k % 2] = swz_ld_tr(gc, sl_, rc + 16 * (kk & 1), kk >> 1);
+        tq[k % 2] = swz_ld_tr(qc, sl_, rc + 16 * (kk & 1), kk >> 1);
       }
+      FENCE();
     }
-#else
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float lv[4] = {l4[g].x, l4[g].y, l4[g].z, l4[g].w};
-      const float dv4[4] = {d4[g].x, d4[g].y, d4[g].z, d4[g].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g + i;
-        float x = fast_exp2(fmaf(sacc[r], c, -lv[i]));
-        x = (p_rel + (uint32_t)(8 * g + i) < p_width) ? x : 0.f;
-        pr[r] = x;
-        ds[r] = x * (dpacc[r] - dv4[i]);
-      }
-    }
-#endif
-    const u32x4 pb[2] = {pack_b(pr, 0), pack_b(pr, 1)};
-    const u32x4 sb[2] = {pack_b(ds, 0), pack_b(ds, 1)};
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        dv[db] = mfma32(tg[2 * db + st], pb[st], dv[db]);
-        dk[db] = mfma32(tq[2 * db + st], sb[st], dk[db]);
-      }
-    __builtin_amdgcn_sched_barrier(0);
   };
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j % 3;
-    const int qt0 = qlo + j * BMQ;
-    if (j + 2 < ntiles) issue(j + 2);
-    const uint16_t* sq = sQ + buf * Q_TILE;
-    const uint16_t* sg = sG + buf * Q_TILE;
-    const float* sl = sL + buf * BMQ;
-    const float* sd = sD + buf * BMQ;
-    // The element mask is applied to every block (three vector ALU operations per score): a
-    // separate unmasked copy of the block code doubles the live ranges and spills.
-    {
+  issue(0);
+  if (ntiles > 1) issue(1);
+  if (ntiles > 2) issue(2);
+  if (ntiles > 2)
+    dma_wait_barrier<2 * kKvPieces>();
+  else if (ntiles > 1)
+    dma_wait_barrier<kKvPieces>();
+  else
+    dma_wait_barrier<0>();
+
+  // block 0's S and dP - delta
+  floatx16 s0, d0, s1, d1;
+  {
+    zero16(s0);
 #pragma unroll
-      for (int qb = 0; qb < BMQ / 32; ++qb) {
-        const int pb0 = qt0 + qb * 32;
-        // uniform per wave: skip blocks that none of the wave's keys can see
-        // every (query, key) pair of the block is visible when the wave's keys are all prefix
-        // keys, the block's queries all exist and (causal prefix) follow the wave's last key
-        const bool masked =
-            !(wave_pre && pb0 + 32 <= S && (!pc || pb0 >= wk0 + 31));
-        if (pb0 < wq_hi && pb0 + 32 > wq_lo) qblock(sq, sg, sl, sd, qb, pb0, masked);
-      }
+    for (int g = 0; g < 4; ++g) {
+      const float4 d = *reinterpret_cast<const float4*>(sD + 8 * g + 4 * half);
+      d0[4 * g + 0] = -d.x;
+      d0[4 * g + 1] = -d.y;
+      d0[4 * g + 2] = -d.z;
+      d0[4 * g + 3] = -d.w;
     }
-    // tile j + 1 must have landed; tile j + 2's pieces may still be in flight
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      s0 = mfma32(swz_ld_a(sQ, sl_, 0, st), kf[st], s0);
+      d0 = mfma32(swz_ld_a(sG, sl_, 0, st), vf[st], d0);
+    }
+    mask_block(s0, 0);
+  }
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int b = j & 3, bn = (j + 1) & 3;
+    const uint16_t* q_j = sQ + b * Q_TILE;
+    const uint16_t* g_j = sG + b * Q_TILE;
+    step(s0, d0, s1, d1, q_j, g_j, sD + b * BMQ, 32, q_j, g_j, sL + b * BMQ, 0);
+    mask_block(s1, 2 * j + 1);
+    // tile j + 1 must have landed (tile j + 2's copy may still be in flight); past this barrier
+    // every wave is done with tile j - 1, whose buffers take tile j + 3
     if (j + 2 < ntiles)
       dma_wait_barrier<kKvPieces>();
     else
       dma_wait_barrier<0>();
+    if (j + 3 < ntiles) issue(j + 3);
+    step(s1, d1, s0, d0, sQ + bn * Q_TILE, sG + bn * Q_TILE, sD + bn * BMQ, 0, q_j, g_j,
+         sL + b * BMQ, 32);
+    if (j + 1 < ntiles) mask_block(s0, 2 * j + 2);
   }
 
   if (kw < S) {
@@ -461,12 +451,8 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);  // blocks do not interleave: registers stay bounded
     floatx16 sacc, dpacc;
     zero16(sacc);
-#if RSWA_BWD_LEAN
 #pragma unroll
     for (int r = 0; r < 16; ++r) dpacc[r] = -dlt;  // the chain yields dP - delta
-#else
-    zero16(dpacc);
-#endif
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       const u32x4 ka = swz_ld_a(sk, sl_, kb * 32, st);
@@ -491,7 +477,6 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
     const uint32_t k_rel = (uint32_t)(k0 + kb * 32 + 4 * half - lo);
     const uint32_t k_width = (uint32_t)max(hi - lo + 1, 0);
     float ds[16];
-#if RSWA_BWD_LEAN
 #pragma unroll
     for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(fmaf(sacc[r], c, -lse2)) * dpacc[r];
     if (masked) {  // uniform: only tiles that are not wholly visible
@@ -499,14 +484,6 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
       for (int r = 0; r < 16; ++r)
         ds[r] = (k_rel + (uint32_t)(8 * (r >> 2) + (r & 3)) < k_width) ? ds[r] : 0.f;
     }
-#else
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = fast_exp2(fmaf(sacc[r], c, -lse2));
-      x = (k_rel + (uint32_t)(8 * (r >> 2) + (r & 3)) < k_width) ? x : 0.f;
-      ds[r] = x * (dpacc[r] - dlt);
-    }
-#endif
     const u32x4 sb[2] = {pack_b(ds, 0), pack_b(ds, 1)};
 #pragma unroll
     for (int db = 0; db < 4; ++db)
