@@ -76,6 +76,27 @@ def test_prefill_bf16_output_is_rne_of_f32(wa):
     np.testing.assert_array_equal(W.bf16_bits(bf), W.bf16_bits(f32))
 
 
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_prefill_wide_row_offsets_match(wa, out_dtype):
+    """A launch whose max_seqlen * heads * 128 reaches 2^31 forms its K / V row offsets in 64 bits
+    instead of with the 24-bit multiply; both must give the same output bit for bit. (max_seqlen
+    only sizes the grid: the workgroups past each sequence's end exit at once.)"""
+    pw = W.make_prefill("wide", 4, [300, 129], [70, 64], [16, 128], seed=21)
+    q, k, v = upload(pw.q, "bf16"), upload(pw.k, "bf16"), upload(pw.v, "bf16")
+    cu = torch.tensor(pw.cu_seqlens, dtype=torch.int32, device="cuda")
+    m = torch.tensor(pw.prefix_len, dtype=torch.int32, device="cuda")
+    n = torch.tensor(pw.window, dtype=torch.int32, device="cuda")
+    H = q.shape[1]
+    wide = (1 << 31) // (H * 128)
+    narrow = wa.rswa_prefill_attn(q, k, v, cu, m, n, out_dtype=out_dtype, max_seqlen=300)
+    widened = wa.rswa_prefill_attn(q, k, v, cu, m, n, out_dtype=out_dtype, max_seqlen=wide)
+    torch.cuda.synchronize()
+    bits = torch.int32 if out_dtype == torch.float32 else torch.int16
+    assert torch.equal(narrow.view(bits), widened.view(bits))
+    ref = oracle_seq(pw, 0)
+    assert float(np.abs(widened[:300].float().cpu().numpy() - ref).max()) <= TOL
+
+
 def test_prefill_rows_match_decode_steps(wa):
     """The teacher-forced row of output t equals decode step t on the same inputs (both K3 and
     K2 against the oracle, and against each other)."""

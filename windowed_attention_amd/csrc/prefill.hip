@@ -53,7 +53,8 @@ constexpr int kDmaPieces = 2 * kDmaGroups;          // 16-byte DMA loads per wav
 // Tile k0 .. k0 + 63 of K and V (rows clamped to kmax) copied by LDS DMA into one buffer pair,
 // swizzled: lane l of a 4-row group fetches the global chunk that belongs in LDS slot l % 16 of
 // its row. With WIDE false the row offset is a 24-bit multiply (full rate; the launcher
-// guarantees key * row_stride < 2^31), instead of the quarter-rate 64-bit one.
+// guarantees key * row_stride < 2^31, and at most 1024 heads keep row_stride below 2^24),
+// instead of the quarter-rate 64-bit one.
 template <bool WIDE>
 __device__ __forceinline__ void dma_kv_tile(uint16_t* sk, uint16_t* sv, const uint16_t* kbase,
                                             const uint16_t* vbase, int row_stride, int k0,
