@@ -102,9 +102,9 @@ uint64_t rswa_cache_bytes(const rswa_cache_desc* desc);
 rswa_status rswa_cache_create(const rswa_cache_desc* desc, const void* prefix_k_dev,
                               const void* prefix_v_dev, void* stream, rswa_cache** out);
 
-/* Create a cache whose prefixes live in a shared, token-granular page pool (survey's paged /
- * shared prefix KV; the pages serve the model with a page size of one token and plan a pool of
- * prefill KV chunks: GeekNews "Unlimited OCR", serving flags and limitations). desc->prefix_paged
+/* Create a cache whose prefixes live in a shared, token-granular page pool (paged / shared prefix
+ * KV; the pages serve the model with a page size of one token and plan a pool of prefill KV
+ * chunks: GeekNews "Unlimited OCR", serving flags and limitations). desc->prefix_paged
  * must be 1. pool_k_dev / pool_v_dev: caller-owned device arrays [pool_rows][H][D] of kv_dtype
  * (token-major: one row per token, 256 B per head in bf16), read during every decode, unchanged
  * and alive until rswa_cache_destroy. prefix_table_dev: device int32 [sum_b m_b]; prefix token j
@@ -208,7 +208,7 @@ rswa_status rswa_prefill_bwd(const void* q_dev, const void* k_dev, const void* v
                              int32_t head_dim, int32_t max_seqlen, int32_t prefix_causal,
                              float softmax_scale, void* stream);
 
-/* Graph-captured step loop (survey's fused append + decode with a HIP-graph step loop). Capture
+/* Graph-captured step loop (fused append + decode steps replayed from a HIP graph). Capture
  * `steps` consecutive rswa_decode_step launches of `cache` (no active mask) into a HIP graph:
  * step i of a replay reads q / k / v from slot i of q_slots / k_slots / v_slots (each [steps][B][H]
  * [D] of kv_dtype, caller-owned) and writes slot i of out_slots ([steps][B][H][D] of out_dtype).
