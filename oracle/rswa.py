@@ -15,7 +15,7 @@ What R-SWA computes, as the pages state it:
     "model architecture" sections]
   * The prefix is encoded once and never changes during decoding. [GeekNews, DeepEncoder section]
 
-Readings taken where the pages are silent or garbled (each also listed in the design doc):
+Readings taken where the pages are silent or garbled:
   R1  the n-token window includes the current output token (self), so the latest query sees
       exactly the L_m + min(n, t) rows the cache holds;
   R2  "evict the (m+1)-th" means the element at 1-based queue position m + 1, i.e. the oldest
