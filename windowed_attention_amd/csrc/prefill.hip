@@ -170,6 +170,9 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
     float pr[16];
     u32x4 va[4];
     FENCE();
+    // While its score MFMAs and softmax interleave, a wave issues ahead of the other wave on its
+    // SIMD (measured: 1.5 % faster than equal priorities; raising it over the PV half gains less).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       nxt = mfma32(kf[i & 3], qf[i], i == 0 ? floatx16{} : nxt);
@@ -194,6 +197,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
     // computed here, under the score MFMAs, not sunk past the rescale branch to its use
     asm volatile("" : "+v"(pb0));
     FENCE();
+    __builtin_amdgcn_s_setprio(0);
     if (__any(rescale)) {
 #pragma unroll
       for (int db = 0; db < 4; ++db)
