@@ -122,8 +122,8 @@ template <typename OUT>
 __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
   __shared__ __attribute__((aligned(16))) uint16_t sQ[4 * Q_TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sG[4 * Q_TILE];
-  __shared__ __attribute__((aligned(16))) float sL[4 * BMQ];
-  __shared__ __attribute__((aligned(16))) float sD[4 * BMQ];
+  __shared__ __attribute__((aligned(16))) float sL[2 * kKvWaves * BMQ];
+  __shared__ __attribute__((aligned(16))) float sD[2 * kKvWaves * BMQ];
 
   // key blocks outermost across heads: the prefix blocks (long query loops) start first
   const int idx = blockIdx.x;
@@ -148,12 +148,12 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
   const float* lse = a.work + (int64_t)cu0 * a.heads + h;           // lse * log2(e)
   const float* dlt = a.work + a.rows + (int64_t)cu0 * a.heads + h;  // delta
 
-  // this lane's key and its K / V rows as B operands (8 d-steps of 16)
-  const int wk0 = k0 + wave * 32;
-  const int kw = wk0 + (lane & 31);
+  const float c = a.scale_log2;
+  const SwzLane sl_(lane);
   u32x4 kf[8], vf[8];
-  {
-    const int kc = min(kw, S - 1);
+  // this lane's key as B operands (8 d-steps of 16 of its K and V rows)
+  auto load_kv = [&](int key) {
+    const int kc = min(key, S - 1);
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       kf[st] = *reinterpret_cast<const u32x4*>(a.k + hoff + kc * rs + st * 16 + half * 8);
@@ -163,32 +163,176 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
     // loop, instead of inside it, where its wait would also cover the tile DMA in flight.
 #pragma unroll
     for (int st = 0; st < 8; ++st) asm volatile("" : "+v"(kf[st]), "+v"(vf[st]));
-  }
-  // queries that see key kw: [plo, phi)
-  int plo, phi;
-  if (kw >= S) {
-    plo = phi = 0;
-  } else if (kw < m) {
-    plo = pc ? kw : 0;
-    phi = S;
-  } else {
-    plo = kw;
-    phi = min(S, kw + n);
-  }
-  const int klast = min(k0 + BNK, S) - 1;
-  const int qlo = k0 < m ? (pc ? k0 : 0) : k0;
-  const int qhi = k0 < m ? S : min(S, klast + n);
-  const int ntiles = (qhi - qlo + BMQ - 1) / BMQ;
-  const bool wave_pre = wk0 + 32 <= min(m, S);  // all of the wave's keys are prefix keys
+  };
+  // queries that see key kw: [lo, hi)
+  auto key_range = [&](int key, int& lo, int& hi) {
+    if (key >= S) {
+      lo = hi = 0;
+    } else if (key < m) {
+      lo = pc ? key : 0;
+      hi = S;
+    } else {
+      lo = key;
+      hi = min(S, key + n);
+    }
+  };
 
-  const float c = a.scale_log2;
+  // The block that straddles the prefix end (m not a multiple of 128): its first hs key sets of
+  // 32 hold the r = m mod 128 prefix keys, which every later query sees, while its other keys see
+  // only their windows. Run as usual, one wave would stream all queries while three wait; instead
+  // the four waves take one such key set at a time and a quarter of its query blocks each, from
+  // private double-buffered 32-query tiles, and add their partial dK, dV through LDS. The main
+  // loop below then handles the block's remaining (window-only) keys.
+  const int r_pre = m % BNK;
+  const bool boundary = r_pre > 0 && kblk == m / BNK;
+  const int hs = boundary ? (r_pre + 31) / 32 : 0;
+  for (int set = 0; set < hs; ++set) {
+    const int ks0 = k0 + 32 * set;
+    const int kws = ks0 + (lane & 31);
+    load_kv(kws);
+    int plo, phi;
+    key_range(kws, plo, phi);
+    const int slo = pc ? ks0 : 0;  // ks0 < m: a prefix key set
+    const int nb = (S - slo + 31) / 32;
+    const int per = (nb + kKvWaves - 1) / kKvWaves;
+    const int b0 = min(nb, wave * per), b1 = min(nb, b0 + per);
+    floatx16 dk[4], dv[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      zero16(dk[db]);
+      zero16(dv[db]);
+    }
+    uint16_t* wq = sQ + wave * Q_TILE;  // this wave's two 32-row Q buffers
+    uint16_t* wg = sG + wave * Q_TILE;
+    float* wl = sL + wave * 2 * BMQ;    // and two 64-float lse / delta buffers
+    float* wd = sD + wave * 2 * BMQ;
+    auto issue_blk = [&](int b, int buf) {
+      const int p0 = slo + 32 * b;
+      dma4(lse + (int64_t)min(p0 + lane, S - 1) * a.heads, wl + buf * BMQ);
+      dma4(dlt + (int64_t)min(p0 + lane, S - 1) * a.heads, wd + buf * BMQ);
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const int row = 4 * g + (lane >> 4);
+        const int64_t off = (int64_t)min(p0 + row, S - 1) * rs + 8 * ((lane & 15) ^ swz(row));
+        dma16(qbase + off, wq + buf * 32 * kHeadDim + g * 4 * kHeadDim);
+        dma16(gbase + off, wg + buf * 32 * kHeadDim + g * 4 * kHeadDim);
+      }
+    };
+    constexpr int kBlkPieces = 18;
+    if (b0 < b1) issue_blk(b0, 0);
+    if (b0 + 1 < b1) issue_blk(b0 + 1, 1);
+    for (int b = b0; b < b1; ++b) {
+      const int buf = (b - b0) & 1;
+      if (b + 1 < b1)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kBlkPieces) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      const uint16_t* q_t = wq + buf * 32 * kHeadDim;
+      const uint16_t* g_t = wg + buf * 32 * kHeadDim;
+      const float* l_t = wl + buf * BMQ;
+      const float* d_t = wd + buf * BMQ;
+      floatx16 sacc, dpacc;
+      zero16(sacc);
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const float4 d4 = *reinterpret_cast<const float4*>(d_t + 8 * gg + 4 * half);
+        dpacc[4 * gg + 0] = -d4.x;  // the chain yields dP - delta
+        dpacc[4 * gg + 1] = -d4.y;
+        dpacc[4 * gg + 2] = -d4.z;
+        dpacc[4 * gg + 3] = -d4.w;
+      }
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        sacc = mfma32(swz_ld_a(q_t, sl_, 0, st), kf[st], sacc);
+        dpacc = mfma32(swz_ld_a(g_t, sl_, 0, st), vf[st], dpacc);
+      }
+      const int pb0 = slo + 32 * b;
+      const uint32_t p_rel = (uint32_t)(pb0 + 4 * half - plo);
+      const uint32_t p_width = (uint32_t)(phi - plo);
+      float pr[16], ds[16];
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const float4 l4 = *reinterpret_cast<const float4*>(l_t + 8 * gg + 4 * half);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = 4 * gg + i;
+          const bool vis = p_rel + (uint32_t)(8 * gg + i) < p_width;
+          pr[rr] = vis ? fast_exp2(fmaf(sacc[rr], c, -lv[i])) : 0.f;
+          ds[rr] = pr[rr] * dpacc[rr];
+        }
+      }
+      const u32x4 pb[2] = {pack_b(pr, 0), pack_b(pr, 1)};
+      const u32x4 sb[2] = {pack_b(ds, 0), pack_b(ds, 1)};
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          dv[db] = mfma32(swz_ld_tr(g_t, sl_, 16 * st, db), pb[st], dv[db]);
+          dk[db] = mfma32(swz_ld_tr(q_t, sl_, 16 * st, db), sb[st], dk[db]);
+        }
+      if (b + 2 < b1) {
+        // every LDS read of this buffer has returned before the copy overwrites it
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue_blk(b + 2, buf);
+      }
+    }
+    // add the four partial dK^T, dV^T (this wave's registers; same lane layout in every wave)
+    __syncthreads();
+    float* pk = reinterpret_cast<float*>(wq);  // 16 KB: 64 registers x 64 lanes
+    float* pv = reinterpret_cast<float*>(wg);
+    if (wave > 0) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          pk[(db * 16 + i) * 64 + lane] = dk[db][i];
+          pv[(db * 16 + i) * 64 + lane] = dv[db][i];
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 1; w < kKvWaves; ++w) {
+        const float* ok = reinterpret_cast<const float*>(sQ + w * Q_TILE);
+        const float* ov = reinterpret_cast<const float*>(sG + w * Q_TILE);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            dk[db][i] += ok[(db * 16 + i) * 64 + lane];
+            dv[db][i] += ov[(db * 16 + i) * 64 + lane];
+          }
+      }
+      if (kws < S) {
+        const int64_t row = ((int64_t)(cu0 + kws) * a.heads + h) * kHeadDim;
+        store_row128<OUT>(reinterpret_cast<OUT*>(a.dk) + row, dk, a.scale, half);
+        store_row128<OUT>(reinterpret_cast<OUT*>(a.dv) + row, dv, 1.f, half);
+      }
+    }
+    __syncthreads();
+  }
+  if (hs == kKvWaves) return;  // the whole block held prefix keys (uniform)
+
+  // this lane's key (none for the waves whose key sets the split above covered)
+  const int wk0 = k0 + wave * 32;
+  const int kw = wave < hs ? S : wk0 + (lane & 31);
+  load_kv(kw);
+  int plo, phi;
+  key_range(kw, plo, phi);
+  const int kfirst = k0 + 32 * hs;  // first key the loop below owns
+  const int klast = min(k0 + BNK, S) - 1;
+  const int qlo = kfirst < m ? (pc ? kfirst : 0) : kfirst;
+  const int qhi = kfirst < m ? S : min(S, klast + n);
+  const int ntiles = (qhi - qlo + BMQ - 1) / BMQ;
+  const bool wave_pre = wave >= hs && wk0 + 32 <= min(m, S);  // all the wave's keys are prefix keys
+
   floatx16 dk[4], dv[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
     zero16(dk[db]);
     zero16(dv[db]);
   }
-  const SwzLane sl_(lane);
 
   auto issue = [&](int j) {
     const int b = j & 3;
