@@ -4,9 +4,10 @@ Each case draws its own sizes from a fixed seed: packed prefill batches (ragged 
 prefix lengths anywhere in [0, S], windows shorter and longer than the outputs, causal and
 bidirectional prefixes) for the forward with log-sum-exp and for the training backward, and
 decode batches (ragged step counts, R-SWA and full-causal caches, bf16 and fp32, the fused step
-and the separate append + decode, forced stream-K splits) checked at random steps. Tolerances are
-the ones of the per-path tests: max-abs 1e-2 (bf16 inputs) / 1e-5 (fp32) on float32 outputs,
-2e-4 on lse, 1e-2 of the largest reference entry on each gradient.
+and the separate append + decode, forced stream-K splits, prefixes shared through a token pool)
+checked at random steps. Tolerances are the ones of the per-path tests: max-abs 1e-2 (bf16
+inputs) / 1e-5 (fp32) on float32 outputs, 2e-4 on lse, 1e-2 of the largest reference entry on
+each gradient.
 """
 import numpy as np
 import pytest
@@ -128,3 +129,42 @@ def test_fuzz_decode(wa, seed):
             err = float(np.abs(got[t][b] - o).max())
             assert err <= TOL[dtype], (f"seed {seed} t={t} b={b} (m={int(m[b])}, n={int(n[b])}, "
                                        f"{dtype}, {'full' if full else 'rswa'}): {err}")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_fuzz_paged_decode(wa, seed):
+    """Prefixes held once in a scattered token pool and shared by several sequences: every random
+    checkpoint bit-identical to a cache holding copies of the same prefixes, and within the decode
+    tolerance of the oracle over `oracle.paged_prefix` of the pool."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 902]))
+    docs = rng.integers(0, 300, size=int(rng.integers(1, 4)))
+    B = int(rng.integers(1, 7))
+    seq_doc = rng.integers(0, docs.size, size=B)
+    dtype = "bf16" if rng.integers(0, 3) else "f32"
+    full = bool(rng.integers(0, 4) == 0)
+    n = rng.choice([1, 16, 64, 128], size=B)
+    steps = rng.integers(1, 130, size=B)
+    wl, pp = W.make_paged_decode(f"fuzzp{seed}", 9, dtype, docs.tolist(), seq_doc.tolist(),
+                                 n.tolist(), steps.tolist(), seed=seed,
+                                 spare_rows=int(rng.integers(0, 40)))
+    mode = wa.MODE_FULL_CAUSAL if full else wa.MODE_RSWA
+    checks = sorted(set(rng.integers(1, wl.T + 1, size=5).tolist()) | {1, wl.T})
+    fused = bool(rng.integers(0, 2))
+    got = Trajectory(wa, wl, mode, paged=pp).run(checks, fused=fused, raw=True)
+    ref = Trajectory(wa, wl, mode).run(checks, fused=fused, raw=True)
+    off = np.concatenate([[0], np.cumsum(wl.prefix_len)])
+    f = lambda x: to_f64(x, dtype)
+    for t in checks:
+        act = torch.from_numpy(wl.active(t).astype(bool)).cuda()
+        assert torch.equal(got[t][act].view(torch.int32), ref[t][act].view(torch.int32)), t
+        out = got[t].cpu().numpy()
+        for b in range(B):
+            if wl.steps[b] < t:
+                continue
+            mb = int(wl.prefix_len[b])
+            pk = O.paged_prefix(pp.pool_k, pp.table, int(off[b]), mb)
+            pv = O.paged_prefix(pp.pool_v, pp.table, int(off[b]), mb)
+            o, _ = O.decode_step(f(wl.q[t - 1, b]), f(pk), f(pv), f(wl.k[:t, b]), f(wl.v[:t, b]),
+                                 t, int(wl.window[b]), O.FULL if full else O.RSWA)
+            err = float(np.abs(out[b] - o).max())
+            assert err <= TOL[dtype], f"seed {seed} t={t} b={b}: {err}"
