@@ -16,9 +16,13 @@ LIB = os.path.join(ROOT, "windowed_attention_amd", "librswa.so")
 
 @pytest.fixture(scope="module")
 def wa():
-    if not os.path.exists(LIB):  # build once if nothing is built yet
-        from windowed_attention_amd import _build
-        _build.build()
+    if not os.path.exists(LIB):  # build once if nothing is built yet (without importing the
+        import importlib.util    # package, which needs the library)
+        spec = importlib.util.spec_from_file_location(
+            "windowed_attention_amd_build", os.path.join(ROOT, "windowed_attention_amd", "_build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
     import windowed_attention_amd
     return windowed_attention_amd
 
