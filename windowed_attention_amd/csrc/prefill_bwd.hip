@@ -639,16 +639,28 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  for (int j = 0; j < ntiles; ++j) {
+  // Leading tiles that need no element mask (inside the prefix, and below the diagonal of a
+  // causal prefix) run a loop without mask tests or end-of-loop cases.
+  int n_plain = min(m / BN, n_pre);
+  if (pc && q0 < m) n_plain = min(n_plain, (q0 + 1) / BN);
+  const int j_plain = min(n_plain, ntiles - 2);
+  int j = 0;
+  for (; j < j_plain; ++j) {
+    const int buf = j % 3;
+    issue(j + 2);
+    const uint16_t* sk = sK + buf * K_TILE;
+    const uint16_t* sv = sV + buf * K_TILE;
+    kblock(sk, sv, 0, 0, 0, 0, false);
+    kblock(sk, sv, 1, 0, 0, 0, false);
+    dma_wait_barrier<kDqPieces>();
+  }
+  for (; j < ntiles; ++j) {
     const int buf = j % 3;
     if (j + 2 < ntiles) issue(j + 2);
     const uint16_t* sk = sK + buf * K_TILE;
     const uint16_t* sv = sV + buf * K_TILE;
     const int k0 = tstart(j);
     const bool is_pre = j < n_pre;
-    // The element mask is applied to every tile (three vector ALU operations per score): a
-    // separate unmasked copy of the block code doubles the live ranges the register allocator
-    // sees and spills.
     const int lo = is_pre ? 0 : win_lo;
     const int hi = is_pre ? pre_hi : p;
     // uniform per tile: prefix tiles that every query of the workgroup sees whole need no mask
