@@ -177,6 +177,7 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 // The (max, sum) pairs are loaded in parallel and reduced in LDS; the numerators are accumulated
 // with independent loads, so the merge costs a few memory round trips, not one per partial.
 constexpr int kMergeChunk = kHeadDim;
+constexpr int kMergeFast = 16;  // pieces per range merged from registers in one memory round trip
 
 template <typename OUT>
 __device__ __forceinline__ void merge_range(const DecodeArgs& a, int64_t s, int64_t f, int np,
@@ -187,6 +188,37 @@ __device__ __forceinline__ void merge_range(const DecodeArgs& a, int64_t s, int6
   const float2* ml = a.ws_ml + f + s;
   const float* acc = a.ws_acc + (f + s) * kHeadDim + (worker ? tid : 0);
   float M = kNegBig;
+  if (np <= kMergeFast) {
+    // Few pieces (the usual case): every partial of the range is requested at once, so the merge
+    // waits for memory once instead of once per dependent step.
+    const float2 p = tid < np ? ml[tid] : make_float2(kNegBig, 0.f);
+    float x[kMergeFast];
+#pragma unroll
+    for (int i = 0; i < kMergeFast; ++i) x[i] = i < np ? acc[(int64_t)i * kHeadDim] : 0.f;
+    M = p.x;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    if (lane == 0 && wave < NW) s_red[wave] = M;
+    __syncthreads();
+    M = s_red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_red[w]);
+    if (tid < np) {
+      s_w[tid] = fast_exp2(p.x - M);
+      s_l[tid] = p.y;
+    }
+    __syncthreads();
+    float lsum = 0.f, num = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMergeFast; ++i)
+      if (i < np) {
+        num = fmaf(x[i], s_w[i], num);
+        lsum = fmaf(s_l[i], s_w[i], lsum);
+      }
+    if (worker) store_out(reinterpret_cast<OUT*>(a.out) + s * kHeadDim + tid, num / lsum);
+    __syncthreads();
+    return;
+  }
   if (worker)
     for (int i = tid; i < np; i += kHeadDim) M = fmaxf(M, ml[i].x);
 #pragma unroll
