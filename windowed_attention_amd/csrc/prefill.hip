@@ -82,10 +82,24 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
   __shared__ __attribute__((aligned(16))) uint16_t sK[4 * T_TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sV[4 * T_TILE];
 
-  const int s = blockIdx.z, h = blockIdx.y;
+  // XCD-aware tile order: workgroups are dispatched round-robin over the 8 XCDs (workgroup i on
+  // XCD i % 8), so giving each XCD a contiguous run of (query tile, head) pairs keeps one head's
+  // query tiles together and its K / V tiles shared in that XCD's L2.
+  int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+  {
+    const int nx = gridDim.x, ny = gridDim.y, nwg = nx * ny * gridDim.z;
+    if (nwg % 8 == 0) {
+      const int i = bx + nx * (by + ny * bz);
+      const int l = (i % 8) * (nwg / 8) + i / 8;
+      bx = l % nx;
+      by = (l / nx) % ny;
+      bz = l / (nx * ny);
+    }
+  }
+  const int s = bz, h = by;
   const int cu0 = a.cu_seqlens[s];
   const int S = a.cu_seqlens[s + 1] - cu0;
-  const int q0 = blockIdx.x * BMQ;
+  const int q0 = bx * BMQ;
   if (q0 >= S) return;
   const int q1 = min(q0 + BMQ, S);
   const int m = a.prefix_len[s];

@@ -520,10 +520,23 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[3 * K_TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sV[3 * K_TILE];
 
-  const int s = blockIdx.z, h = blockIdx.y;
+  // XCD-aware tile order (as in the forward): workgroup i runs on XCD i % 8, so each XCD takes a
+  // contiguous run of (query tile, head) pairs and one head's K / V tiles stay in its L2.
+  int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+  {
+    const int nx = gridDim.x, ny = gridDim.y, nwg = nx * ny * gridDim.z;
+    if (nwg % 8 == 0) {
+      const int i = bx + nx * (by + ny * bz);
+      const int l = (i % 8) * (nwg / 8) + i / 8;
+      bx = l % nx;
+      by = (l / nx) % ny;
+      bz = l / (nx * ny);
+    }
+  }
+  const int s = bz, h = by;
   const int cu0 = a.cu_seqlens[s];
   const int S = a.cu_seqlens[s + 1] - cu0;
-  const int q0 = blockIdx.x * BNQ;
+  const int q0 = bx * BNQ;
   if (q0 >= S) return;
   const int q1 = min(q0 + BNQ, S);
   const int m = a.prefix_len[s];
