@@ -71,12 +71,26 @@ __device__ __forceinline__ void dma_kv_tile(uint16_t* sk, uint16_t* sv, const ui
   }
 }
 
+// A tile whose 64 rows all lie in [0, kmax]: no clamp, so the lanes' byte offsets within the tile
+// (`voff`, computed once per kernel) are fixed and only the tile's wave-uniform base moves.
+__device__ __forceinline__ void dma_kv_tile_u(uint16_t* sk, uint16_t* sv, const uint16_t* kt,
+                                              const uint16_t* vt, const uint32_t (&voff)[kDmaGroups],
+                                              int wave) {
+#pragma unroll
+  for (int u = 0; u < kDmaGroups; ++u) {
+    const int grp = wave * kDmaGroups + u;
+    dma16s(kt, voff[u], sk + grp * 4 * kHeadDim);
+    dma16s(vt, voff[u], sv + grp * 4 * kHeadDim);
+  }
+}
+
 // Scheduling fence: the interleave of MFMAs and vector-ALU work stays as written.
 #define FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // The copy of tile j + 3 is issued at the middle of tile j, after the barrier that retires tile
 // j - 1's buffer, and waited for two tiles later.
-template <typename OUT, bool WIDE>
+// LSE: also keep the float32 sum of the unrounded probabilities and write the log-sum-exp.
+template <typename OUT, bool WIDE, bool LSE>
 __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(PrefillArgs a) {
   constexpr int BMQ = kWavesPF * 32;  // queries per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t sK[4 * T_TILE];
@@ -146,11 +160,14 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
   const int win_lo = p >= m ? max(m, p - n + 1) : p + 1;
 
   const float c = a.scale_log2;
-  float m_run = kNegBig, l_run = 0.f;
+  // running reference max (log2 domain), the threshold past which it moves, the row sum of the
+  // bf16-rounded probabilities (the output's normaliser) and, for the log-sum-exp, of the unrounded
+  float m_run = kNegBig, m_thr = kNegBig, l_run = 0.f, l_exact = 0.f;
   floatx16 o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) zero16(o[db]);
   const SwzLane sl_(lane);
+  const bf16x2v_t ones2 = {(__bf16)1.f, (__bf16)1.f};
 
   // element mask of the 32-key block kb of tile j, where that block is not fully visible
   auto mask_block = [&](floatx16& sc, int j, int kb) {
@@ -168,6 +185,19 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
     }
   };
 
+  // Row sum of the bf16-rounded probabilities that enter the PV product (two per dot2), so the
+  // output's weights sum to one as rounded.
+  auto rowsum8 = [&](const u32x4& pb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // copied out word by word: a bit_cast of the vector element compiles to the wrong register
+      const uint32_t w = pb[i];
+      bf16x2v_t pw;
+      __builtin_memcpy(&pw, &w, sizeof(w));
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(pw, ones2, l_run, false);
+    }
+  };
+
   // One pipeline step: the softmax of block `cur` (scores complete, masked) under the score
   // MFMAs of the next block (rows r_next of tile sk_next) into `nxt`, then O^T += V^T P^T for
   // `cur` (rows r_cur of tile sv_cur) under the rest of the softmax.
@@ -179,8 +209,8 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
     float mx = cur[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, cur[r]);
-    float m_new = 0.f, alpha = 1.f;
-    bool rescale = false;
+    float m_new = 0.f;
+    bool up = false;
     float pr[16];
     u32x4 va[4];
     FENCE();
@@ -193,12 +223,10 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
       if (i < 4) kf[i] = swz_ld_a(sk_next, sl_, r_next, i + 4);
       if (i >= 4) va[i - 4] = swz_ld_tr(sv_cur, sl_, r_cur, i - 4);
       if (i == 0) {
-        mx = xhalf_max(mx) * c;
-        const bool up = mx > m_run + kLazy;
-        m_new = up ? mx : m_run;
-        alpha = up ? fast_exp2(m_run - m_new) : 1.f;
-        rescale = up && m_run != kNegBig;
-        m_run = m_new;
+        // the reference max moves only when the block max passes it by kLazy
+        const float mxs = xhalf_max(mx) * c;
+        up = mxs > m_thr;
+        m_new = up ? mxs : m_run;
       } else {
         const int r = i - 1;  // exponentials 0..6 here, 7 below
         pr[r] = fast_exp2(fmaf(cur[r], c, -m_new));
@@ -212,11 +240,18 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
     asm volatile("" : "+v"(pb0));
     FENCE();
     __builtin_amdgcn_s_setprio(0);
-    if (__any(rescale)) {
+    // Rare: some lane's reference max moved. Its accumulators and row sum are rescaled (lanes whose
+    // max stayed get exp2(0) = 1; the first block of a row scales zeros).
+    if (__any(up)) {
+      const float alpha = fast_exp2(m_run - m_new);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      l_run *= alpha;
+      if (LSE) l_exact *= alpha;
+      m_run = m_new;
+      m_thr = m_new + kLazy;
     }
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -228,23 +263,35 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
     }
     const u32x4 pb1 = u32x4{pack_bf16(pr[8], pr[9]), pack_bf16(pr[10], pr[11]),
                             pack_bf16(pr[12], pr[13]), pack_bf16(pr[14], pr[15])};
-    float psum = 0.f;
+    rowsum8(pb0);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       o[db] = mfma32(va[db], pb1, o[db]);
-      psum += (pr[4 * db] + pr[4 * db + 1]) + (pr[4 * db + 2] + pr[4 * db + 3]);
+      if (db == 0) rowsum8(pb1);
+      if (LSE) l_exact += (pr[4 * db] + pr[4 * db + 1]) + (pr[4 * db + 2] + pr[4 * db + 3]);
       FENCE();
     }
-    l_run = fmaf(l_run, alpha, psum);
-    asm volatile("" : "+v"(l_run));  // the row sum under this step's MFMAs, not deferred
   };
 
   const int rs32 = (int)rs;
-  auto issue = [&](int j) {
-    const int b = j & 3;
-    dma_kv_tile<WIDE>(sK + b * T_TILE, sV + b * T_TILE, kbase, vbase, rs32, ts.start(j), kmax,
-                      wave, lane);
+  // this lane's byte offsets within a tile, for the unclamped copies
+  uint32_t voff[kDmaGroups];
+#pragma unroll
+  for (int u = 0; u < kDmaGroups; ++u) {
+    const int row = 4 * (wave * kDmaGroups + u) + (lane >> 4);
+    voff[u] = 2u * (uint32_t)(row * rs32 + 8 * ((lane & 15) ^ swz(row)));
+  }
+  // copy tile j into buffer b (= j % 4)
+  auto issue_to = [&](int j, int b) {
+    const int k0 = ts.start(j);
+    if (k0 + BN - 1 <= kmax)
+      dma_kv_tile_u(sK + b * T_TILE, sV + b * T_TILE, kbase + (int64_t)k0 * rs,
+                    vbase + (int64_t)k0 * rs, voff, wave);
+    else
+      dma_kv_tile<WIDE>(sK + b * T_TILE, sV + b * T_TILE, kbase, vbase, rs32, k0, kmax, wave,
+                        lane);
   };
+  auto issue = [&](int j) { issue_to(j, j & 3); };
   issue(0);
   if (nt > 1) issue(1);
   if (nt > 2) issue(2);
@@ -267,6 +314,18 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
   if (pc && q0 < m) n_plain = min(n_plain, (q0 + 1) / BN);
   const int j_plain = min(n_plain - 1, nt - 3);
   int j = 0;
+  // four tiles per iteration, so that every LDS buffer offset is a constant
+  for (; j + 4 <= j_plain; j += 4) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint16_t* k_j = sK + b * T_TILE;
+      const uint16_t* v_j = sV + b * T_TILE;
+      step(s0, s1, k_j, 32, v_j, 0);
+      dma_wait_barrier<kDmaPieces>();
+      issue_to(j + b + 3, (b + 3) & 3);
+      step(s1, s0, sK + ((b + 1) & 3) * T_TILE, 0, v_j, 32);
+    }
+  }
   for (; j < j_plain; ++j) {
     const uint16_t* k_j = sK + (j & 3) * T_TILE;
     const uint16_t* v_j = sV + (j & 3) * T_TILE;
@@ -296,8 +355,10 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
   if (p < q1) {
     const int64_t row = (int64_t)(cu0 + p) * a.heads + h;
     store_row128<OUT>(reinterpret_cast<OUT*>(a.out) + row * kHeadDim, o, 1.f / l_tot, half);
-    if (a.lse != nullptr && half == 0)
-      a.lse[row] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+    if (LSE) {
+      const float le = xhalf_sum(l_exact);
+      if (half == 0) a.lse[row] = (m_run + __builtin_amdgcn_logf(le)) * 0.69314718055994531f;
+    }
   }
 }
 
@@ -308,14 +369,21 @@ hipError_t launch_prefill(const PrefillArgs& a, int out_f32, hipStream_t s) {
   const dim3 grid((a.max_seqlen + BMQ - 1) / BMQ, a.heads, a.nseq);
   // 24-bit row offsets hold when (max_seqlen - 1) * heads * 128 < 2^31
   const bool wide = (int64_t)a.max_seqlen * a.heads * kHeadDim >= (int64_t{1} << 31);
-  if (out_f32 && wide)
-    hipLaunchKernelGGL((prefill_kernel<float, true>), grid, dim3(kThreads), 0, s, a);
-  else if (out_f32)
-    hipLaunchKernelGGL((prefill_kernel<float, false>), grid, dim3(kThreads), 0, s, a);
-  else if (wide)
-    hipLaunchKernelGGL((prefill_kernel<uint16_t, true>), grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((prefill_kernel<uint16_t, false>), grid, dim3(kThreads), 0, s, a);
+  const bool lse = a.lse != nullptr;
+#define RSWA_PREFILL_LAUNCH(OUT, W, L) \
+  hipLaunchKernelGGL((prefill_kernel<OUT, W, L>), grid, dim3(kThreads), 0, s, a)
+  if (lse) {
+    if (out_f32 && wide) RSWA_PREFILL_LAUNCH(float, true, true);
+    else if (out_f32) RSWA_PREFILL_LAUNCH(float, false, true);
+    else if (wide) RSWA_PREFILL_LAUNCH(uint16_t, true, true);
+    else RSWA_PREFILL_LAUNCH(uint16_t, false, true);
+  } else {
+    if (out_f32 && wide) RSWA_PREFILL_LAUNCH(float, true, false);
+    else if (out_f32) RSWA_PREFILL_LAUNCH(float, false, false);
+    else if (wide) RSWA_PREFILL_LAUNCH(uint16_t, true, false);
+    else RSWA_PREFILL_LAUNCH(uint16_t, false, false);
+  }
+#undef RSWA_PREFILL_LAUNCH
   return hipGetLastError();
 }
 
