@@ -169,7 +169,16 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
   const SwzLane sl_(lane);
   const bf16x2v_t ones2 = {(__bf16)1.f, (__bf16)1.f};
 
-  // element mask of the 32-key block kb of tile j, where that block is not fully visible
+  // scaled maximum of a score block over its 32 keys (16 in-lane, 16 in lane ^ 32)
+  auto block_max = [&](const floatx16& x) {
+    float mx = x[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+    return xhalf_max(mx) * c;
+  };
+
+  // element mask of the 32-key block kb of tile j, where that block is not fully visible;
+  // returns whether it masked anything
   auto mask_block = [&](floatx16& sc, int j, int kb) {
     const int k0 = ts.start(j) + kb * 32;
     const bool is_pre = j < ts.n_pre;
@@ -183,6 +192,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
         sc[r] = (k >= lo && k <= hi) ? sc[r] : -INFINITY;
       }
     }
+    return need;
   };
 
   // Row sum of the bf16-rounded probabilities that enter the PV product (two per dot2), so the
@@ -198,17 +208,18 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
     }
   };
 
-  // One pipeline step: the softmax of block `cur` (scores complete, masked) under the score
-  // MFMAs of the next block (rows r_next of tile sk_next) into `nxt`, then O^T += V^T P^T for
-  // `cur` (rows r_cur of tile sv_cur) under the rest of the softmax.
-  auto step = [&](floatx16& cur, floatx16& nxt, const uint16_t* sk_next, int r_next,
-                  const uint16_t* sv_cur, int r_cur) {
-    u32x4 kf[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) kf[i] = swz_ld_a(sk_next, sl_, r_next, i);
-    float mx = cur[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, cur[r]);
+  // One pipeline step: the softmax of block `cur` (scores complete, masked; `mxs` its scaled
+  // maximum) under the score MFMAs of the next block (rows r_next of tile sk_next) into `nxt`,
+  // then O^T += V^T P^T for `cur` (rows r_cur of tile sv_cur) under the rest of the softmax. The
+  // maximum of `nxt` (before any mask) is formed under the last PV MFMAs and returned in `mxs`, so
+  // that the next step starts with MFMAs rather than with a chain of vector-ALU maxima.
+  // `kf` arrives holding the first four K fragments of the next block (read by the previous step)
+  // and leaves holding those of the block after it (rows r_after of tile sk_after), read under the
+  // last PV MFMAs into the registers the V operands free. `mid` runs between the two halves: the
+  // tile barrier and the copy of a later tile, when this step has them.
+  auto step = [&](floatx16& cur, floatx16& nxt, u32x4 (&kf)[4], const uint16_t* sk_next,
+                  int r_next, const uint16_t* sv_cur, int r_cur, float& mxs, auto&& mid,
+                  const uint16_t* sk_after, int r_after) {
     float m_new = 0.f;
     bool up = false;
     float pr[16];
@@ -224,7 +235,6 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
       if (i >= 4) va[i - 4] = swz_ld_tr(sv_cur, sl_, r_cur, i - 4);
       if (i == 0) {
         // the reference max moves only when the block max passes it by kLazy
-        const float mxs = xhalf_max(mx) * c;
         up = mxs > m_thr;
         m_new = up ? mxs : m_run;
       } else {
@@ -240,9 +250,10 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
     asm volatile("" : "+v"(pb0));
     FENCE();
     __builtin_amdgcn_s_setprio(0);
+    mid();
     // Rare: some lane's reference max moved. Its accumulators and row sum are rescaled (lanes whose
     // max stayed get exp2(0) = 1; the first block of a row scales zeros).
-    if (__any(up)) {
+    if (__builtin_expect(__any(up), 0)) {
       const float alpha = fast_exp2(m_run - m_new);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
@@ -264,10 +275,22 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
     const u32x4 pb1 = u32x4{pack_bf16(pr[8], pr[9]), pack_bf16(pr[10], pr[11]),
                             pack_bf16(pr[12], pr[13]), pack_bf16(pr[14], pr[15])};
     rowsum8(pb0);
+    float mn = 0.f;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       o[db] = mfma32(va[db], pb1, o[db]);
+      kf[db] = swz_ld_a(sk_after, sl_, r_after, db);
       if (db == 0) rowsum8(pb1);
+      if (db == 1) {
+        mn = fmaxf(nxt[0], nxt[1]);
+#pragma unroll
+        for (int r = 2; r < 8; ++r) mn = fmaxf(mn, nxt[r]);
+      }
+      if (db == 2) {
+#pragma unroll
+        for (int r = 8; r < 16; ++r) mn = fmaxf(mn, nxt[r]);
+      }
+      if (db == 3) mxs = xhalf_max(mn) * c;
       if (LSE) l_exact += (pr[4 * db] + pr[4 * db + 1]) + (pr[4 * db + 2] + pr[4 * db + 3]);
       FENCE();
     }
@@ -284,7 +307,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
   // copy tile j into buffer b (= j % 4)
   auto issue_to = [&](int j, int b) {
     const int k0 = ts.start(j);
-    if (k0 + BN - 1 <= kmax)
+    if (__builtin_expect(k0 + BN - 1 <= kmax, 1))
       dma_kv_tile_u(sK + b * T_TILE, sV + b * T_TILE, kbase + (int64_t)k0 * rs,
                     vbase + (int64_t)k0 * rs, voff, wave);
     else
@@ -307,6 +330,11 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
 #pragma unroll
   for (int st = 0; st < 8; ++st) s0 = mfma32(swz_ld_a(sK, sl_, 0, st), qf[st], s0);
   mask_block(s0, 0, 0);
+  float mxs = block_max(s0);
+  u32x4 kf[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kf[i] = swz_ld_a(sK, sl_, 32, i);
+  auto none = [] {};
 
   // Leading tiles that need no element mask (inside the prefix, and below the diagonal of a
   // causal prefix) run a loop without mask tests or end-of-loop cases.
@@ -320,35 +348,40 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
     for (int b = 0; b < 4; ++b) {
       const uint16_t* k_j = sK + b * T_TILE;
       const uint16_t* v_j = sV + b * T_TILE;
-      step(s0, s1, k_j, 32, v_j, 0);
-      dma_wait_barrier<kDmaPieces>();
-      issue_to(j + b + 3, (b + 3) & 3);
-      step(s1, s0, sK + ((b + 1) & 3) * T_TILE, 0, v_j, 32);
+      const uint16_t* k_n = sK + ((b + 1) & 3) * T_TILE;
+      step(s0, s1, kf, k_j, 32, v_j, 0, mxs, [&] {
+        dma_wait_barrier<kDmaPieces>();
+        issue_to(j + b + 3, (b + 3) & 3);
+      }, k_n, 0);
+      step(s1, s0, kf, k_n, 0, v_j, 32, mxs, none, k_n, 32);
     }
   }
   for (; j < j_plain; ++j) {
     const uint16_t* k_j = sK + (j & 3) * T_TILE;
     const uint16_t* v_j = sV + (j & 3) * T_TILE;
-    step(s0, s1, k_j, 32, v_j, 0);
-    dma_wait_barrier<kDmaPieces>();
-    issue(j + 3);
-    step(s1, s0, sK + ((j + 1) & 3) * T_TILE, 0, v_j, 32);
+    const uint16_t* k_n = sK + ((j + 1) & 3) * T_TILE;
+    step(s0, s1, kf, k_j, 32, v_j, 0, mxs, [&] {
+      dma_wait_barrier<kDmaPieces>();
+      issue(j + 3);
+    }, k_n, 0);
+    step(s1, s0, kf, k_n, 0, v_j, 32, mxs, none, k_n, 32);
   }
   for (; j < nt; ++j) {
     const uint16_t* k_j = sK + (j & 3) * T_TILE;
     const uint16_t* v_j = sV + (j & 3) * T_TILE;
     const uint16_t* k_n = sK + ((j + 1) & 3) * T_TILE;
-    step(s0, s1, k_j, 32, v_j, 0);
-    mask_block(s1, j, 1);
     // tile j + 1 must have landed (tile j + 2's copy may still be in flight); past this barrier
     // every wave is done with tile j - 1, whose buffer takes tile j + 3
-    if (j + 2 < nt)
-      dma_wait_barrier<kDmaPieces>();
-    else
-      dma_wait_barrier<0>();
-    if (j + 3 < nt) issue(j + 3);
-    step(s1, s0, k_n, 0, v_j, 32);
-    if (j + 1 < nt) mask_block(s0, j + 1, 0);
+    step(s0, s1, kf, k_j, 32, v_j, 0, mxs, [&] {
+      if (j + 2 < nt)
+        dma_wait_barrier<kDmaPieces>();
+      else
+        dma_wait_barrier<0>();
+      if (j + 3 < nt) issue(j + 3);
+    }, k_n, 0);
+    if (mask_block(s1, j, 1)) mxs = block_max(s1);
+    step(s1, s0, kf, k_n, 0, v_j, 32, mxs, none, k_n, 32);
+    if (j + 1 < nt && mask_block(s0, j + 1, 0)) mxs = block_max(s0);
   }
 
   const float l_tot = xhalf_sum(l_run);
