@@ -131,9 +131,10 @@ __device__ __forceinline__ void dma16(const void* g, void* lds) {
 }
 // The same copy from a wave-uniform base address (SGPR pair) plus a per-lane 32-bit byte offset:
 // the address arithmetic of a tile then runs on the scalar unit.
-__device__ __forceinline__ void dma16s(const void* base, uint32_t off, void* lds) {
+// `lds` is an LDS byte address (lds_addr of the destination), wave-uniform.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
-               "s"(lds_addr(lds))
+               "s"(lds)
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* g, void* lds) {

@@ -73,14 +73,13 @@ __device__ __forceinline__ void dma_kv_tile(uint16_t* sk, uint16_t* sv, const ui
 
 // A tile whose 64 rows all lie in [0, kmax]: no clamp, so the lanes' byte offsets within the tile
 // (`voff`, computed once per kernel) are fixed and only the tile's wave-uniform base moves.
-__device__ __forceinline__ void dma_kv_tile_u(uint16_t* sk, uint16_t* sv, const uint16_t* kt,
-                                              const uint16_t* vt, const uint32_t (&voff)[kDmaGroups],
-                                              int wave) {
+// `lk` / `lv`: LDS byte addresses of this wave's first group in the destination buffers.
+__device__ __forceinline__ void dma_kv_tile_u(uint32_t lk, uint32_t lv, const uint16_t* kt,
+                                              const uint16_t* vt, const uint32_t (&voff)[kDmaGroups]) {
 #pragma unroll
   for (int u = 0; u < kDmaGroups; ++u) {
-    const int grp = wave * kDmaGroups + u;
-    dma16s(kt, voff[u], sk + grp * 4 * kHeadDim);
-    dma16s(vt, voff[u], sv + grp * 4 * kHeadDim);
+    dma16s(kt, voff[u], lk + u * 4 * kHeadDim * 2);
+    dma16s(vt, voff[u], lv + u * 4 * kHeadDim * 2);
   }
 }
 
@@ -304,12 +303,30 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
     const int row = 4 * (wave * kDmaGroups + u) + (lane >> 4);
     voff[u] = 2u * (uint32_t)(row * rs32 + 8 * ((lane & 15) ^ swz(row)));
   }
+  // LDS byte addresses of this wave's first DMA group in buffer 0 (taken once: the generic to LDS
+  // conversion carries a null test)
+  const uint32_t lk0 = lds_addr(sK + wave * kDmaGroups * 4 * kHeadDim);
+  const uint32_t lv0 = lds_addr(sV + wave * kDmaGroups * 4 * kHeadDim);
+  // copy of an unclamped tile (first key k0, k0 + BN - 1 <= kmax) into buffer b
+  auto issue_u = [&](int k0, int b) {
+    // byte offset of the tile: a 32-bit product when the narrow-offset bound holds
+    const uint16_t* kt;
+    const uint16_t* vt;
+    if (WIDE) {
+      kt = kbase + (int64_t)k0 * rs;
+      vt = vbase + (int64_t)k0 * rs;
+    } else {
+      const uint32_t tb = 2u * (uint32_t)k0 * (uint32_t)rs32;
+      kt = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(kbase) + tb);
+      vt = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(vbase) + tb);
+    }
+    dma_kv_tile_u(lk0 + b * T_TILE * 2, lv0 + b * T_TILE * 2, kt, vt, voff);
+  };
   // copy tile j into buffer b (= j % 4)
   auto issue_to = [&](int j, int b) {
     const int k0 = ts.start(j);
     if (__builtin_expect(k0 + BN - 1 <= kmax, 1))
-      dma_kv_tile_u(sK + b * T_TILE, sV + b * T_TILE, kbase + (int64_t)k0 * rs,
-                    vbase + (int64_t)k0 * rs, voff, wave);
+      issue_u(k0, b);
     else
       dma_kv_tile<WIDE>(sK + b * T_TILE, sV + b * T_TILE, kbase, vbase, rs32, k0, kmax, wave,
                         lane);
@@ -341,9 +358,12 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
   int n_plain = min(m / BN, ts.n_pre);
   if (pc && q0 < m) n_plain = min(n_plain, (q0 + 1) / BN);
   const int j_plain = min(n_plain - 1, nt - 3);
+  // leading prefix tiles whose copies need no clamp
+  const int n_fast = min(ts.n_pre, (kmax + 1) / BN);
   int j = 0;
-  // four tiles per iteration, so that every LDS buffer offset is a constant
-  for (; j + 4 <= j_plain; j += 4) {
+  // four tiles per iteration, so that every LDS buffer offset is a constant; the tiles it copies
+  // (j + 3 .. j + 6) are unclamped prefix tiles
+  for (; j + 4 <= j_plain && j + 7 <= n_fast; j += 4) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const uint16_t* k_j = sK + b * T_TILE;
@@ -351,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
       const uint16_t* k_n = sK + ((b + 1) & 3) * T_TILE;
       step(s0, s1, kf, k_j, 32, v_j, 0, mxs, [&] {
         dma_wait_barrier<kDmaPieces>();
-        issue_to(j + b + 3, (b + 3) & 3);
+        issue_u((j + b + 3) * BN, (b + 3) & 3);
       }, k_n, 0);
       step(s1, s0, kf, k_n, 0, v_j, 32, mxs, none, k_n, 32);
     }
