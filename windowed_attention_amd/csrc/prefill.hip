@@ -220,7 +220,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
                   int r_next, const uint16_t* sv_cur, int r_cur, float& mxs, auto&& mid,
                   const uint16_t* sk_after, int r_after) {
     float m_new = 0.f;
-    bool up = false;
+    uint64_t up_mask = 0;  // lanes whose reference max moves (a scalar ballot)
     float pr[16];
     u32x4 va[4];
     FENCE();
@@ -234,7 +234,8 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
       if (i >= 4) va[i - 4] = swz_ld_tr(sv_cur, sl_, r_cur, i - 4);
       if (i == 0) {
         // the reference max moves only when the block max passes it by kLazy
-        up = mxs > m_thr;
+        const bool up = mxs > m_thr;
+        up_mask = __builtin_amdgcn_ballot_w64(up);
         m_new = up ? mxs : m_run;
       } else {
         const int r = i - 1;  // exponentials 0..6 here, 7 below
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
     mid();
     // Rare: some lane's reference max moved. Its accumulators and row sum are rescaled (lanes whose
     // max stayed get exp2(0) = 1; the first block of a row scales zeros).
-    if (__builtin_expect(__any(up), 0)) {
+    if (__builtin_expect(up_mask != 0, 0)) {
       const float alpha = fast_exp2(m_run - m_new);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
