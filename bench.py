@@ -35,7 +35,8 @@ H, D = 16, 128
 DECODE_SOURCES = ["windowed_attention_amd/csrc/decode.hip", "windowed_attention_amd/csrc/device.h",
                   "windowed_attention_amd/csrc/kernels.h"]
 PREFILL_SOURCES = ["windowed_attention_amd/csrc/prefill.hip", "windowed_attention_amd/csrc/mfma.h",
-                   "windowed_attention_amd/csrc/device.h", "windowed_attention_amd/csrc/kernels.h"]
+                   "windowed_attention_amd/csrc/device.h", "windowed_attention_amd/csrc/kernels.h",
+                   "windowed_attention_amd/_build.py"]  # the build script carries per-source flags
 BACKWARD_SOURCES = ["windowed_attention_amd/csrc/prefill_bwd.hip",
                     "windowed_attention_amd/csrc/mfma.h", "windowed_attention_amd/csrc/device.h",
                     "windowed_attention_amd/csrc/kernels.h"]

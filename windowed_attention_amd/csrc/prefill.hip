@@ -20,13 +20,15 @@
 // registers; the V^T operand comes out of gfx950's transposing LDS read.
 //
 // Key loop. K and V tiles of 64 keys are copied by LDS DMA (no register staging) into four
-// XOR-swizzled buffers, three tiles ahead; one barrier per tile. The loop is software-pipelined
-// over 32-key blocks: step b issues the score MFMAs of block b + 1 in between the vector-ALU
-// softmax of block b, then the PV MFMAs of block b in between the rest of that softmax, so the
-// matrix cores and the vector ALUs of a wave work at the same time. Softmax runs in the log2
-// domain in float32 with a lazily moved reference max; P is rounded to bf16 for the PV product and
-// the output is normalised by the float32 row sum. With a non-null lse the natural log-sum-exp of
-// each query's scaled scores is written too (the training pass needs it).
+// XOR-swizzled buffers, three tiles ahead; one barrier per tile, in the middle of the tile's first
+// step. The loop is software-pipelined over 32-key blocks: step b issues the score MFMAs of block
+// b + 1 in between the vector-ALU softmax of block b, then the PV MFMAs of block b in between the
+// rest of that softmax, and under its last MFMAs forms block b + 1's maximum and reads block
+// b + 2's leading K fragments, so the matrix cores and the vector ALUs of a wave work at the same
+// time. Softmax runs in the log2 domain in float32 with a lazily moved reference max; P is rounded
+// to bf16 for the PV product and the output is normalised by the sum of P as rounded (so its
+// weights sum to one). With a non-null lse the natural log-sum-exp of each query's scaled scores,
+// from the float32 sum of the unrounded P, is written too (the training pass needs it).
 #include "kernels.h"
 #include "mfma.h"
 
