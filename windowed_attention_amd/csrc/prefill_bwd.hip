@@ -11,8 +11,8 @@
 // log2 e, so no softmax state is kept between the passes.
 //
 // Three kernels, no atomics and no partial sums:
-//   delta: one 16-lane group per (token, head) row, HBM-bound; it also stores lse in the log2
-//     domain next to delta in the caller's work array.
+//   delta: one 16-lane group per (token, head) row, HBM-bound; it stores -delta and lse in the
+//     log2 domain in the caller's work array.
 //   dK/dV: key-parallel. A workgroup owns 32 keys per wave; the wave keeps K and V of its keys in
 //     registers (B operands) and its dK^T, dV^T accumulators in registers, and streams the query
 //     tiles that can see its keys (every query for a prefix key, the n queries of the window for
@@ -55,7 +55,7 @@ __device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8]) {
 }
 
 // Also converts the forward's natural-log lse to the log2 domain the other kernels use:
-// work[0][row] = lse * log2(e), work[1][row] = delta.
+// work[0][row] = lse * log2(e), work[1][row] = -delta (the dP chains start from it).
 template <typename OT>
 __global__ __launch_bounds__(256) void delta_kernel(const OT* __restrict__ out,
                                                     const uint16_t* __restrict__ dout,
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void delta_kernel(const OT* __restrict__ out,
   for (int i = 0; i < 8; ++i) acc = fmaf(o[i], g[i], acc);
   acc = row16_sum(acc);
   if (row < rows) {
-    if (c == 0) work[rows + row] = acc;
+    if (c == 0) work[rows + row] = -acc;
     if (c == 1) work[row] = lse[row] * kLog2e;
   }
 }
@@ -112,7 +112,6 @@ __device__ __forceinline__ void dma_qtile(uint16_t* sq, uint16_t* sg, float* sl,
   }
 }
 
-
 // Each wave walks every 32-query block of the workgroup's query range (blocks its keys cannot see
 // are masked out); step b issues S and dP of block b + 1 in between the vector-ALU work of block b
 // (P, dS and their bf16 packing), then dV^T and dK^T of block b, so a wave's matrix cores are fed
@@ -146,7 +145,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
   const uint16_t* qbase = a.q + hoff;
   const uint16_t* gbase = a.dout + hoff;
   const float* lse = a.work + (int64_t)cu0 * a.heads + h;           // lse * log2(e)
-  const float* dlt = a.work + a.rows + (int64_t)cu0 * a.heads + h;  // delta
+  const float* dlt = a.work + a.rows + (int64_t)cu0 * a.heads + h;  // -delta
 
   const float c = a.scale_log2;
   const SwzLane sl_(lane);
@@ -236,10 +235,10 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg) {
         const float4 d4 = *reinterpret_cast<const float4*>(d_t + 8 * gg + 4 * half);
-        dpacc[4 * gg + 0] = -d4.x;  // the chain yields dP - delta
-        dpacc[4 * gg + 1] = -d4.y;
-        dpacc[4 * gg + 2] = -d4.z;
-        dpacc[4 * gg + 3] = -d4.w;
+        dpacc[4 * gg + 0] = d4.x;  // -delta: the chain yields dP - delta
+        dpacc[4 * gg + 1] = d4.y;
+        dpacc[4 * gg + 2] = d4.z;
+        dpacc[4 * gg + 3] = d4.w;
       }
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
@@ -334,11 +333,12 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
     zero16(dv[db]);
   }
 
-  auto issue = [&](int j) {
-    const int b = j & 3;
+  // copy tile j into buffer set b (= j % 4)
+  auto issue_to = [&](int j, int b) {
     dma_qtile(sQ + b * Q_TILE, sG + b * Q_TILE, sL + b * BMQ, sD + b * BMQ, qbase, gbase, lse,
               dlt, rs, a.heads, qlo + j * BMQ, S - 1, wave, lane);
   };
+  auto issue = [&](int j) { issue_to(j, j & 3); };
 
   // Scores of block b (queries qlo + 32 b + ...) that this lane's key cannot see set to -inf,
   // where the block is not fully visible (uniform per wave); P and dS are then exactly zero.
@@ -376,10 +376,10 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
     FENCE();
 #pragma unroll
     for (int g = 0; g < 4; ++g) {  // dP accumulates on top of -delta: the chain yields dP - delta
-      dn[4 * g + 0] = -d4[g].x;
-      dn[4 * g + 1] = -d4[g].y;
-      dn[4 * g + 2] = -d4[g].z;
-      dn[4 * g + 3] = -d4[g].w;
+      dn[4 * g + 0] = d4[g].x;
+      dn[4 * g + 1] = d4[g].y;
+      dn[4 * g + 2] = d4[g].z;
+      dn[4 * g + 3] = d4[g].w;
     }
     float pr[16], ds[16];
     u32x4 pb[2], sb[2], tg[2], tq[2];
@@ -443,10 +443,10 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const float4 d = *reinterpret_cast<const float4*>(sD + 8 * g + 4 * half);
-      d0[4 * g + 0] = -d.x;
-      d0[4 * g + 1] = -d.y;
-      d0[4 * g + 2] = -d.z;
-      d0[4 * g + 3] = -d.w;
+      d0[4 * g + 0] = d.x;  // -delta
+      d0[4 * g + 1] = d.y;
+      d0[4 * g + 2] = d.z;
+      d0[4 * g + 3] = d.w;
     }
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
@@ -456,7 +456,25 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
     mask_block(s0, 0);
   }
 
-  for (int j = 0; j < ntiles; ++j) {
+  int j = 0;
+  // four tiles per iteration while every wait and copy of them is the steady-state one, so that
+  // every LDS buffer offset is a constant
+  for (; j + 7 <= ntiles; j += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int b = u, bn = (u + 1) & 3;
+      const uint16_t* q_j = sQ + b * Q_TILE;
+      const uint16_t* g_j = sG + b * Q_TILE;
+      step(s0, d0, s1, d1, q_j, g_j, sD + b * BMQ, 32, q_j, g_j, sL + b * BMQ, 0);
+      mask_block(s1, 2 * (j + u) + 1);
+      dma_wait_barrier<kKvPieces>();
+      issue_to(j + u + 3, (u + 3) & 3);
+      step(s1, d1, s0, d0, sQ + bn * Q_TILE, sG + bn * Q_TILE, sD + bn * BMQ, 0, q_j, g_j,
+           sL + b * BMQ, 32);
+      mask_block(s0, 2 * (j + u) + 2);
+    }
+  }
+  for (; j < ntiles; ++j) {
     const int b = j & 3, bn = (j + 1) & 3;
     const uint16_t* q_j = sQ + b * Q_TILE;
     const uint16_t* g_j = sG + b * Q_TILE;
@@ -562,7 +580,7 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
   }
   const int64_t prow = (int64_t)(cu0 + pq) * a.heads + h;
   float lse2 = a.work[prow];
-  float dlt = a.work[a.rows + prow];
+  float dlt = a.work[a.rows + prow];  // -delta
   // Materialise the operands here: the compiler then waits for these loads once, before the
   // loop, instead of inside it, where its wait would also cover the tile DMA in flight.
 #pragma unroll
@@ -609,7 +627,7 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
     floatx16 sacc, dpacc;
     zero16(sacc);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dpacc[r] = -dlt;  // the chain yields dP - delta
+    for (int r = 0; r < 16; ++r) dpacc[r] = dlt;  // -delta: the chain yields dP - delta
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       const u32x4 ka = swz_ld_a(sk, sl_, kb * 32, st);
