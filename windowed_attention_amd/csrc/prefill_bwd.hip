@@ -35,6 +35,24 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Scheduling fence: the interleave of MFMAs, LDS reads and vector-ALU work stays as written.
 #define FENCE() __builtin_amdgcn_sched_barrier(0)
 
+// v_mfma_f32_32x32x16_bf16 with its accumulator in VGPRs (the vector ALU reads S and dP) and its B
+// operand in AGPRs. Written as inline assembly because the compiler gives every MFMA of a kernel
+// that uses AGPRs an AGPR accumulator and then copies S and dP out register by register. The
+// hazards the compiler cannot see are covered by construction: a chain accumulates in place (same
+// opcode, exact overlap: no wait states); the vector ALU reads the result only after the other
+// product half of the step (16 MFMAs, far beyond the 11 wait states an 8-pass result needs); a
+// start value written by the vector ALU gets two wait states (mfma_vacc_first); LDS-loaded operands
+// are covered by the compiler's lgkmcnt waits on the asm inputs.
+__device__ __forceinline__ void mfma_vacc_zero(floatx16& d, const u32x4& a, const u32x4& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_vacc(floatx16& d, const u32x4& a, const u32x4& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_vacc_first(floatx16& d, const u32x4& a, const u32x4& b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+
 // ------------------------------------------------------------------------------------------
 // delta_p = rowsum(dO * O) per (token, head) row: 16 lanes x 8 dims per row
 // ------------------------------------------------------------------------------------------
@@ -161,7 +179,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
     // Materialise the operands here: the compiler then waits for these loads once, before the
     // loop, instead of inside it, where its wait would also cover the tile DMA in flight.
 #pragma unroll
-    for (int st = 0; st < 8; ++st) asm volatile("" : "+v"(kf[st]), "+v"(vf[st]));
+    for (int st = 0; st < 8; ++st) asm volatile("" : "+a"(kf[st]), "+a"(vf[st]));
   };
   // queries that see key kw: [lo, hi)
   auto key_range = [&](int key, int& lo, int& hi) {
@@ -385,8 +403,13 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
     u32x4 pb[2], sb[2], tg[2], tq[2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      sn = mfma32(fq[i % 3], kf[i], i == 0 ? floatx16{} : sn);
-      dn = mfma32(fg[i % 3], vf[i], dn);
+      if (i == 0) {
+        mfma_vacc_zero(sn, fq[0], kf[0]);
+        mfma_vacc_first(dn, fg[0], vf[0]);
+      } else {
+        mfma_vacc(sn, fq[i % 3], kf[i]);
+        mfma_vacc(dn, fg[i % 3], vf[i]);
+      }
       if (i + 3 < 8) {
         fq[i % 3] = swz_ld_a(qn, sl_, rn, i + 3);
         fg[i % 3] = swz_ld_a(gn, sl_, rn, i + 3);
