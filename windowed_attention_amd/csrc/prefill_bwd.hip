@@ -629,10 +629,11 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
   for (int db = 0; db < 4; ++db) zero16(dq[db]);
   const SwzLane sl_(lane);
 
-  auto issue = [&](int j) {
-    const int b = j % 3;
+  // copy tile j into buffer pair b (= j % 3)
+  auto issue_to = [&](int j, int b) {
     dma_ktile(sK + b * K_TILE, sV + b * K_TILE, kbase, vbase, rs, tstart(j), S - 1, wave, lane);
   };
+  auto issue = [&](int j) { issue_to(j, j % 3); };
   issue(0);
   if (ntiles > 1) {
     issue(1);
@@ -648,13 +649,12 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
                     int hi, bool masked) {
     __builtin_amdgcn_sched_barrier(0);  // blocks do not interleave: registers stay bounded
     floatx16 sacc, dpacc;
-    zero16(sacc);
 #pragma unroll
     for (int r = 0; r < 16; ++r) dpacc[r] = dlt;  // -delta: the chain yields dP - delta
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       const u32x4 ka = swz_ld_a(sk, sl_, kb * 32, st);
-      sacc = mfma32(ka, qf[st], sacc);
+      sacc = mfma32(ka, qf[st], st == 0 ? floatx16{} : sacc);  // the first starts from 0
     }
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
@@ -699,6 +699,18 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
   if (pc && q0 < m) n_plain = min(n_plain, (q0 + 1) / BN);
   const int j_plain = min(n_plain, ntiles - 2);
   int j = 0;
+  // three tiles per iteration, so that every LDS buffer offset is a constant
+  for (; j + 3 <= j_plain; j += 3) {
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      issue_to(j + u + 2, (u + 2) % 3);
+      const uint16_t* sk = sK + u * K_TILE;
+      const uint16_t* sv = sV + u * K_TILE;
+      kblock(sk, sv, 0, 0, 0, 0, false);
+      kblock(sk, sv, 1, 0, 0, 0, false);
+      dma_wait_barrier<kDqPieces>();
+    }
+  }
   for (; j < j_plain; ++j) {
     const int buf = j % 3;
     issue(j + 2);
