@@ -174,3 +174,29 @@ def test_backward_packed_training_row_sampled(wa):
         ref = oracle_doc(pw, g, b, heads=heads, q_rows=rows, k_rows=rows)
         for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
             check_grads(f"packed doc {b} {name}", got[s0:s1][rows][:, heads], r)
+
+
+def test_work_array_holds_log2_lse_and_negated_delta(wa):
+    """The work array the backward fills: [0] = lse * log2(e) and [1] = -delta, with delta the
+    row sum of dO * O over the forward output as passed, checked against that definition on the
+    host (float64 sums of the same bf16 values; the kernel sums 128 products in float32)."""
+    pw = W.make_prefill("work", 4, [300, 90], [100, 0], [32, 16], seed=63)
+    g = W.make_output_grad(pw, seed=63)
+    q, k, v = upload(pw.q, "bf16"), upload(pw.k, "bf16"), upload(pw.v, "bf16")
+    dout = upload(g, "bf16")
+    cu = torch.tensor(pw.cu_seqlens, dtype=torch.int32, device="cuda")
+    m = torch.tensor(pw.prefix_len, dtype=torch.int32, device="cuda")
+    n = torch.tensor(pw.window, dtype=torch.int32, device="cuda")
+    out, lse = wa.rswa_prefill_fwd(q, k, v, cu, m, n, out_dtype=torch.bfloat16)
+    total, heads, _ = q.shape
+    work = torch.full((2, total, heads), float("nan"), dtype=torch.float32, device="cuda")
+    wa.rswa_prefill_bwd(q, k, v, out, dout, lse, cu, m, n, work=work)
+    torch.cuda.synchronize()
+    o = out.double().cpu().numpy()
+    d = dout.double().cpu().numpy()
+    delta = (o * d).sum(-1)
+    scale = (np.abs(o) * np.abs(d)).sum(-1).max()
+    w = work.double().cpu().numpy()
+    assert np.abs(w[1] + delta).max() <= 1e-5 * scale
+    lse64 = lse.double().cpu().numpy()
+    np.testing.assert_allclose(w[0], lse64 * np.log2(np.e), rtol=1e-6, atol=1e-6)
