@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
     u32x4 va[4];
     FENCE();
     // While its score MFMAs and softmax interleave, a wave issues ahead of the other wave on its
-    // SIMD (measured: 1.5 % faster than equal priorities; raising it over the PV half gains less).
+    // SIMD (in this step layout equal priorities measure the same, within 0.3 %).
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
