@@ -52,6 +52,7 @@ CASES = [
     ([129, 1, 0, 400, 64], [64, 1, 0, 17, 63], [128, 1, 5, 1, 2], False),  # packed, ragged
     ([640], [272], [128], False),         # single-page prefix, several tiles each side
     ([520], [300], [128], True),
+    ([1100], [700], [128], False),        # long prefix: the unrolled mask-free key loops
 ]
 
 
