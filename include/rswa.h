@@ -159,6 +159,9 @@ rswa_status rswa_decode_step(rswa_cache* cache, const void* q_dev, const void* k
  *    or m_s <= k <= p and p - k < n_s                                   (its own output window)
  * so prefix queries never see outputs; with n_s >= the sequence length this is causal attention
  * over the outputs (the full-causal comparison).
+ * Numerics: scores and the softmax run in float32; P is rounded to bf16 for the P V product
+ * (float32 accumulation) and each output row is divided by the sum of P as rounded, so its
+ * weights sum to one. rswa_prefill_fwd writes the same output bit for bit.
  * q/k/v_dev: [total][H][D] bf16, token-major; out_dev: [total][H][D] of out_dtype.
  * cu_seqlens_dev: device int32 [nseq + 1], nondecreasing, cu_seqlens[0] = 0;
  * prefix_len_dev / window_dev: device int32 [nseq]; m_s in [0, S_s], n_s >= 1.
