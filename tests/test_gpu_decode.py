@@ -97,7 +97,9 @@ def test_append_rows_bit_exact(wa, mode):
             np.testing.assert_array_equal(V[:, :m[b]], pv.transpose(1, 0, 2))
             if mode == 0:
                 occ = O.ring_occupants(n[b], t)
-                slots = [(m[b] + s, j) for s, j in enumerate(occ)]
+                slots = [(O.ring_row(m[b], n[b], j) if j >= 0 else m[b] + s, j)
+                         for s, j in enumerate(occ)]
+                assert sorted(r for r, _ in slots) == list(range(m[b], m[b] + n[b]))
             else:
                 slots = [(O.full_row(m[b], j), j if j < t else -1) for j in range(cap[b])]
             for r, j in slots:

@@ -52,6 +52,34 @@ def test_ring_slots_golden(golden):
         np.testing.assert_array_equal(O.ring_occupants(3, t), np.array([int(x) for x in row[1:]]))
 
 
+def _cache_contents(m, n, t, mode):
+    """Labels of the cache rows after t appends, built by writing output j into the row that the
+    oracle's row helper names (the ring's n slots after the prefix, or the growing cache)."""
+    rows = [f"P{i}" for i in range(m)] + ["-"] * (n if mode == O.RSWA else t)
+    for j in range(t):
+        r = O.ring_row(m, n, j) if mode == O.RSWA else O.full_row(m, j)
+        rows[r] = f"o{j}"
+    return rows
+
+
+def test_cache_rows_golden(golden):
+    """Where each output's K/V lives, for the ring and for the full-causal cache, against the
+    hand-derived contents of tests/golden/cache_rows_m3_n2.txt."""
+    m, n = 3, 2
+    fixture = golden("cache_rows_m3_n2.txt")
+    assert [int(r[0]) for r in fixture] == list(range(8))
+    for t, ring, full in fixture:
+        t = int(t)
+        assert _cache_contents(m, n, t, O.RSWA) == ring.split(","), t
+        assert _cache_contents(m, n, t, O.FULL) == full.split(","), t
+        # written rows = the cache sizes the pages state: L_m + min(n, t) and L_m + t
+        assert sum(x != "-" for x in ring.split(",")) == O.rswa_cache_rows(m, n, t)
+        assert len(full.split(",")) == O.full_cache_rows(m, t)
+        # the ring agrees with the slot occupants the other fixture pins
+        occ = O.ring_occupants(n, t)
+        assert [f"o{j}" if j >= 0 else "-" for j in occ] == ring.split(",")[m:]
+
+
 def test_queue_golden(golden):
     m, n, H, d, T = 3, 2, 1, 2, 5
     pk, pv = rnd((m, H, d), 1), rnd((m, H, d), 2)
@@ -221,8 +249,9 @@ def test_ring_order_gives_the_same_output():
                            for h in range(H)])
         np.testing.assert_allclose(o, o_ring, atol=1e-12)
         assert sorted(live.tolist()) == list(range(max(0, t - n), t))
-        for j in live:
-            assert O.ring_row(m, n, int(j)) == m + int(j) % n
+        # the ring rows of the live outputs are distinct rows of the n-row region after the prefix
+        rows = sorted(O.ring_row(m, n, int(j)) for j in live)
+        assert len(set(rows)) == len(rows) and all(m <= r < m + n for r in rows)
 
 
 def test_queue_equals_mask():
@@ -343,6 +372,32 @@ def test_mutation_wrong_scale_is_caught(monkeypatch):
         test_scale_and_window_closed_form()
     with pytest.raises(AssertionError):
         test_full_mode_matches_library_at_every_step()
+
+
+def test_mutation_ring_row_off_by_one_is_caught(monkeypatch, golden):
+    monkeypatch.setattr(Orswa, "ring_row", lambda m, n, j: m + (j + 1) % n)
+    monkeypatch.setattr(O, "ring_row", lambda m, n, j: m + (j + 1) % n)
+    with pytest.raises(AssertionError):
+        test_cache_rows_golden(golden)
+
+
+def test_mutation_ring_row_without_prefix_offset_is_caught(monkeypatch, golden):
+    monkeypatch.setattr(O, "ring_row", lambda m, n, j: j % n)
+    with pytest.raises(AssertionError):
+        test_cache_rows_golden(golden)
+
+
+def test_mutation_full_row_off_by_one_is_caught(monkeypatch, golden):
+    monkeypatch.setattr(Orswa, "full_row", lambda m, j: m + j - 1)
+    monkeypatch.setattr(O, "full_row", lambda m, j: m + j - 1)
+    with pytest.raises(AssertionError):
+        test_cache_rows_golden(golden)
+
+
+def test_mutation_full_row_as_ring_is_caught(monkeypatch, golden):
+    monkeypatch.setattr(O, "full_row", lambda m, j: m + j % 2)
+    with pytest.raises(AssertionError):
+        test_cache_rows_golden(golden)
 
 
 def test_mutation_transposed_value_is_caught(monkeypatch):
