@@ -2,16 +2,21 @@
 """Benchmark of the R-SWA hot path on one MI355X.
 
 A step is one decode step of the whole batch: K1 append of one new K/V row per sequence and head,
-then K2 split-K decode attention over prefix u window. The headline workload is the batched
-single-page decode (64 sequences, bf16 K/V with 1% x8 outliers, m = 272, n = 128, T = 6000):
-warmup steps t = 1..W, then K timed steps. Inputs for every step are resident in HBM before timing.
+then K2 split-K decode attention over prefix u window, fused in one launch. The headline workload
+is the multi-page decode (8 sequences of 20 pages, m = 5155, n = 128, bf16, T = 20000 steps):
+346 MB of K/V rows per step, more than the 256 MB Infinity Cache holds, so the rows stream from
+HBM. The cache is built untimed first (t = 1 .. T - K - W, timed in 64-step blocks for the
+latency-vs-t curve), then W warmup steps and the K timed steps, the workload's last ones: the
+window is full and the figure is the per-step cost that R-SWA keeps constant. Inputs for every
+step are resident in HBM before timing.
 
-Also reported: per-step latency vs t, the decode kernel's algorithmic HBM GB/s against the 8 TB/s
-peak (HIP events around every decode launch on the launch stream), the multi-page growth curve
-(R-SWA vs full causal, --growth), the masked prefill in TFLOP/s against the bf16 MFMA peak, the
-teacher-forced training pass (forward with log-sum-exp, then dQ / dK / dV) on the same 32K
-sequence, shared-document decode with the prefixes in a token pool vs copied per sequence, and the
-fp64 oracle timed on a bounded sample on the host cores (cpu_baseline).
+Also reported: the decode kernel's algorithmic HBM GB/s against the 8 TB/s peak, latency vs t and
+its flatness, the same workload in full-causal mode (the growth curve), the batched single-page
+decode (64 sequences; its 211 MB working set fits the Infinity Cache, so its GB/s are effective),
+the single-page fp32 decode (B = 1, latency-bound), the ragged batch, the masked prefill in
+TFLOP/s against the bf16 MFMA peak, the teacher-forced training pass on the same 32K sequence,
+shared-document decode with the prefixes in a token pool vs copied per sequence, and the fp64
+oracle timed on bounded samples on the host cores with one thread and with all (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -61,10 +66,12 @@ def source_hash(paths) -> str:
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5800)
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", choices=["batched", "single", "multipage", "ragged"],
-                    default="batched")
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", choices=["batched", "single", "multipage"],
+                    default="multipage")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the headline decode (for counter runs of its kernel)")
     ap.add_argument("--mode", choices=["rswa", "full"], default="rswa")
     ap.add_argument("--chunk", type=int, default=0, help="decode rows per split (0 = automatic)")
     ap.add_argument("--grid", type=int, default=0, help="decode workgroups (0 = automatic)")
@@ -74,7 +81,6 @@ def parse():
     ap.add_argument("--no-shared", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--growth", action="store_true", help="multi-page R-SWA vs full-causal curve")
     ap.add_argument("--kernel-events", action="store_true",
                     help="diagnostic: record HIP events around every launch (adds GPU time)")
     ap.add_argument("--unfused", action="store_true",
@@ -89,7 +95,8 @@ def parse():
                          "prefill kernel (KIND) into profiles/<KIND>_traffic.json and exit "
                          "(no GPU use)")
     ap.add_argument("--prefill-runs", type=int, default=20)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="oracle decode seconds per leg (1 thread, all cores)")
     return ap.parse_args()
 
 
@@ -126,9 +133,15 @@ def append_bytes(wl, t: int) -> int:
     return int((wl.steps >= t).sum()) * H * D * e * 4  # k, v read; k, v written
 
 
-def run_decode(args, wl, mode_full: bool, steps: int, warmup: int, kernel_events: bool,
-               paged=None):
-    """`paged` (workloads.PagedPrefix): the cache reads the prefixes from the shared token pool
+def run_decode(args, wl, mode_full: bool, steps: int, warmup: int, kernel_events: bool = False,
+               paged=None, setup: int = 0, block: int = 64):
+    """Run decode steps t = 1 .. setup + warmup + steps of one workload through the C ABI.
+
+    Steps 1 .. setup build the cache state (the ring fills, the full-causal cache grows); they are
+    timed in blocks of `block` steps with events between blocks, which gives the latency-vs-t
+    curve. After a synchronization, `warmup` untimed steps, another synchronization, then the
+    `steps` timed steps between two events (nothing recorded in between) and a synchronization.
+    `paged` (workloads.PagedPrefix): the cache reads the prefixes from the shared token pool
     through the page table instead of holding copies."""
     import torch
     import windowed_attention_amd as wa
@@ -144,9 +157,9 @@ def run_decode(args, wl, mode_full: bool, steps: int, warmup: int, kernel_events
                     prefix_table=torch.from_numpy(paged.table).cuda())
     mode = wa.MODE_FULL_CAUSAL if mode_full else wa.MODE_RSWA
     ragged = bool((wl.steps != wl.steps.max()).any())
-    total = warmup + steps
+    total = setup + warmup + steps
     if total > wl.T:
-        raise SystemExit(f"warmup + steps = {total} exceeds the workload's T = {wl.T}")
+        raise SystemExit(f"setup + warmup + steps = {total} exceeds the workload's T = {wl.T}")
     cache = wa.RswaCache(pk, pv, wl.prefix_len, None if mode_full else wl.window, mode=mode,
                          max_steps=wl.steps if mode_full else None, kv_dtype=kvdt, **pool)
     del pk, pv
@@ -185,50 +198,57 @@ def run_decode(args, wl, mode_full: bool, steps: int, warmup: int, kernel_events
         if r:
             raise RuntimeError(f"decode failed: {r} {lib.rswa_last_error()}")
 
-    for t in range(1, warmup + 1):
+    # state set-up, timed in blocks (the latency-vs-t curve)
+    nblk = (setup + block - 1) // block
+    ev_blk = [torch.cuda.Event(enable_timing=True) for _ in range(nblk + 1)]
+    torch.cuda.synchronize()
+    for t in range(1, setup + 1):
+        if (t - 1) % block == 0:
+            ev_blk[(t - 1) // block].record()
+        decode(*step(t))
+    if setup:
+        ev_blk[nblk].record()
+    torch.cuda.synchronize()
+    lat = []
+    for j in range(nblk):
+        t_lo = 1 + j * block
+        n_in = min(block, setup - t_lo + 1)
+        lat.append((t_lo + n_in // 2, ev_blk[j].elapsed_time(ev_blk[j + 1]) * 1e3 / n_in))
+
+    for t in range(setup + 1, setup + warmup + 1):
         decode(*step(t))
     torch.cuda.synchronize()
     grid_blocks, launches = cache.decode_plan(appending=fused)
     if not fused:
         launches += 1  # the separate append launch
 
+    t_first = setup + warmup + 1
     ev_k = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(steps)] if kernel_events else []
-    block = 64
-    ev_blk = [torch.cuda.Event(enable_timing=True) for _ in range(steps // block + 2)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
-    nb = 0
     for i in range(steps):
-        t = warmup + 1 + i
-        if i % block == 0:
-            ev_blk[nb].record()
-            nb += 1
-        o, a = step(t)
+        o, a = step(t_first + i)
         if kernel_events:
             ev_k[i][0].record()
             decode(o, a)
             ev_k[i][1].record()
         else:
             decode(o, a)
-    ev_blk[nb].record()
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    elapsed_ms = start.elapsed_time(end)
+    elapsed_ms = start.elapsed_time(end) if steps else 0.0
     steps_done = cache.steps()
     cache.close()
 
     kern_ms = np.array([a.elapsed_time(b) for a, b in ev_k]) if kernel_events else None
-    lat = []
-    for j in range(nb):
-        t_lo = warmup + 1 + j * block
-        n_in = min(block, warmup + steps - t_lo + 1)
-        lat.append((t_lo + n_in // 2, ev_blk[j].elapsed_time(ev_blk[j + 1]) * 1e3 / n_in))
+    if steps:
+        lat.append((t_first + steps // 2, elapsed_ms * 1e3 / steps))
     out_elem = out.element_size()
-    ts = range(warmup + 1, warmup + steps + 1)
+    ts = range(t_first, t_first + steps)
     dec_bytes = np.array([decode_bytes(wl, t, mode_full, out_elem) for t in ts], dtype=np.float64)
     app_bytes = np.array([append_bytes(wl, t) for t in ts], dtype=np.float64)
     tokens = int(sum(int((wl.steps >= t).sum()) for t in ts))
@@ -237,7 +257,8 @@ def run_decode(args, wl, mode_full: bool, steps: int, warmup: int, kernel_events
     return dict(elapsed_ms=elapsed_ms, wall_s=wall, kern_ms=kern_ms, lat=lat,
                 dec_bytes=dec_bytes, app_bytes=app_bytes, launch_bytes=launch_bytes,
                 tokens=tokens, fused=fused, steps_done=steps_done.tolist(),
-                launches_per_step=launches, grid_blocks=grid_blocks)
+                launches_per_step=launches, grid_blocks=grid_blocks,
+                timed_t=[t_first, t_first + steps - 1])
 
 
 def flatness(lat, n, T):
@@ -518,55 +539,109 @@ def run_backward(args):
 # ------------------------------------------------------------------------------------------------
 # cpu baseline: the fp64 oracle on a bounded sample
 # ------------------------------------------------------------------------------------------------
-def cpu_baseline(wl, seconds: float):
-    import oracle as O
-    from workloads import to_f64
-    from threadpoolctl import threadpool_limits
-    with threadpool_limits(limits=1):
-        return _cpu_baseline(wl, seconds, O, to_f64)
+def oracle_step_sample(wl, extra: int = 16, seed: int = 0):
+    """Sampled decode steps: {1, 2, n-1, n, n+1, 2n, 1000, T-1, T}, the steps where the live row
+    count m + min(n, t) crosses a multiple of 64, and `extra` seeded random steps."""
+    n, m, T = int(wl.window[0]), int(wl.prefix_len[0]), int(wl.T)
+    s = {1, 2, n - 1, n, n + 1, 2 * n, 1000, T - 1, T}
+    s |= {t for t in range(1, min(T, n) + 1) if (m + t - 1) // 64 != (m + t) // 64}
+    s |= set(np.random.default_rng(seed).integers(1, T + 1, size=extra).tolist())
+    return sorted(t for t in s if 1 <= t <= T)
 
 
-def _cpu_baseline(wl, seconds, O, to_f64):
-    rng = np.random.default_rng(0)
-    n = int(wl.window[0])
-    cand = sorted({1, 2, n - 1, n, n + 1, 2 * n, 1000, wl.T - 1, wl.T} |
-                  set(rng.integers(1, wl.T + 1, size=16).tolist()))
-    cand = [t for t in cand if 1 <= t <= wl.T]
+def _oracle_decode_leg(wl, steps, seconds, O, to_f64):
+    rng = np.random.default_rng(1)
     pre = {}
-    tokens = 0
+    done, per_step = 0, []
     t0 = time.perf_counter()
-    done = []
     while time.perf_counter() - t0 < seconds:
-        t = cand[len(done) % len(cand)]
+        t = steps[done % len(steps)]
         b = int(rng.integers(0, wl.batch))
         if wl.steps[b] < t:
             continue
         if b not in pre:
             pk, pv = wl.prefix(b)
             pre[b] = (to_f64(pk, wl.dtype), to_f64(pv, wl.dtype))
+        a = time.perf_counter()
         O.decode_step(to_f64(wl.q[t - 1, b], wl.dtype), pre[b][0], pre[b][1],
                       to_f64(wl.k[:t, b], wl.dtype), to_f64(wl.v[:t, b], wl.dtype), t,
                       int(wl.window[b]))
-        tokens += 1
-        done.append(t)
+        per_step.append(time.perf_counter() - a)
+        done += 1
     el = time.perf_counter() - t0
-    return dict(value=tokens / el, unit="tok/s", cores=1, kind="oracle",
-                sample=f"{tokens} (sequence, step) decode outputs of this workload, steps drawn from "
-                       f"{{1,2,n-1,n,n+1,2n,1000,T-1,T}} + 16 seeded random, each computed "
-                       f"independently from the growing cache in fp64 ({el:.1f} s, 1 thread)")
+    return dict(tok_s=done / el, outputs=done, seconds=el,
+                median_ms_per_step=float(np.median(per_step)) * 1e3 if per_step else None)
+
+
+def _oracle_prefill_leg(pw, qkv, blocks, O):
+    """The oracle's prefill on the given query blocks of the 32K sequence (its own 512-row
+    blocking); algorithmic FLOPs of those rows: 4 D H per visible (query, key) pair."""
+    S, m, n = int(pw.cu_seqlens[-1]), int(pw.prefix_len[0]), int(pw.window[0])
+    q, k, v = qkv
+    pairs = 0
+    t0 = time.perf_counter()
+    for b0 in blocks:
+        rows = np.arange(b0, min(S, b0 + 512))
+        O.prefill(q, k, v, m, n, rows=rows)
+        for p in rows:  # visible keys of query p (prefix, then its output window)
+            pairs += m if p < m else m + min(n, p - m + 1)
+    el = time.perf_counter() - t0
+    flops = 4.0 * D * H * pairs
+    return dict(seconds=el, rows=int(sum(min(S, b + 512) - b for b in blocks)),
+                gflops=flops / el / 1e9, flop=flops)
+
+
+def cpu_baseline(wl, seconds: float):
+    """The fp64 oracle as it stands, on the host cores of this run: decode on sampled steps of the
+    headline workload (each computed independently from the growing cache) and the masked
+    prefill on sampled 512-query blocks of the 32K sequence, each with one BLAS thread and with
+    every thread the BLAS pool has. Reported only; never a target."""
+    import oracle as O
+    import workloads as W
+    from workloads import to_f64
+    from threadpoolctl import threadpool_info, threadpool_limits
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    pools = threadpool_info()
+    blas_threads = max([p.get("num_threads", 1) for p in pools] or [1])
+    steps = oracle_step_sample(wl)
+    pw = W.prefill_config()
+    S, m = int(pw.cu_seqlens[-1]), int(pw.prefix_len[0])
+    blocks = [(m // 512 + 1) * 512]  # the first 512-row block of outputs (prefix + window keys)
+    qkv = tuple(to_f64(x, "bf16") for x in (pw.q, pw.k, pw.v))
+    legs = {}
+    for name, lim in (("1_thread", 1), ("all_cores", blas_threads)):
+        with threadpool_limits(limits=lim):
+            dec = _oracle_decode_leg(wl, steps, seconds, O, to_f64)
+            pre = _oracle_prefill_leg(pw, qkv, blocks, O)
+        total_pairs = visible_pairs(S, m, int(pw.window[0]))
+        pre["full_prefill_seconds_extrapolated"] = 4.0 * D * H * total_pairs / (pre["gflops"] * 1e9)
+        legs[name] = dict(threads=lim, decode=dec, prefill=pre)
+        log(f"[bench] oracle {name}: decode {dec['tok_s']:.2f} tok/s, prefill "
+            f"{pre['gflops']:.1f} GFLOP/s")
+    best = legs["all_cores"]
+    return dict(value=best["decode"]["tok_s"], unit="tok/s", cores=blas_threads, kind="oracle",
+                sample=(f"{best['decode']['outputs']} (sequence, step) decode outputs of the "
+                        f"headline workload at steps {{1,2,n-1,n,n+1,2n,1000,T-1,T}} + the "
+                        f"64-row crossings + 16 seeded random steps, each from the growing cache "
+                        f"in fp64 ({seconds:.0f} s per leg); prefill: "
+                        f"{best['prefill']['rows']} of the {S} query rows of the 32K sequence "
+                        f"(the first 512-row block of output queries)"),
+                cpu_count=os.cpu_count(), affinity=aff, blas_threads=blas_threads, legs=legs)
 
 
 # ------------------------------------------------------------------------------------------------
-def growth_curve(args):
-    """Multi-page decode (B=8, m=5155, n=128, T=20000): per-step latency vs t for R-SWA (flat) and
-    for the full-causal mode (cache m + t, growing), same inputs and launch path."""
+def growth_curve(args, wl, rswa_lat):
+    """Multi-page decode (B=8, m=5155, n=128, T=20000): per-step latency vs t for R-SWA (flat;
+    the headline run's curve) and for the full-causal mode (cache m + t, growing), same inputs
+    and launch path."""
     import types
-    wl = decode_workload("multipage")
     out = {}
     for mode in ("rswa", "full"):
-        a = types.SimpleNamespace(chunk=args.chunk, grid=args.grid, unfused=args.unfused)
-        r = run_decode(a, wl, mode == "full", wl.T - 1, 1, False)
-        lat = r["lat"]
+        if mode == "rswa":
+            lat = rswa_lat
+        else:
+            a = types.SimpleNamespace(chunk=args.chunk, grid=args.grid, unfused=args.unfused)
+            lat = run_decode(a, wl, True, 0, 0, setup=wl.T)["lat"]
         ts = np.array([t for t, _ in lat], dtype=np.float64)
         us = np.array([u for _, u in lat])
         byt = np.array([decode_bytes(wl, int(t), mode == "full", 2) + append_bytes(wl, int(t))
@@ -575,20 +650,38 @@ def growth_curve(args):
         rec = dict(us_per_step_vs_t=[[int(ts[i]), round(float(us[i]), 2)] for i in keep],
                    gbs_vs_t=[[int(ts[i]), round(float(byt[i] / (us[i] * 1e-6) / 1e9))]
                              for i in keep],
-                   median_us=float(np.median(us)), tok_s=r["tokens"] / (r["elapsed_ms"] * 1e-3))
+                   median_us=float(np.median(us)))
         if mode == "full":
-            rows = 5155 + ts
-            slope = np.polyfit(rows, us, 1)[0] * 1000.0
-            rec["slope_us_per_1k_rows"] = float(slope)
+            rows = int(wl.prefix_len[0]) + ts
+            rec["slope_us_per_1k_rows"] = float(np.polyfit(rows, us, 1)[0] * 1000.0)
         else:
-            rec["flatness"] = flatness(lat, 128, int(wl.T))
-        jumps = [[int(ts[i]), round(float(us[i] / us[i - 1]), 3)] for i in range(1, len(us))
-                 if abs(us[i] / us[i - 1] - 1) > 0.10]
-        rec["jumps_over_10pct"] = jumps
+            rec["flatness"] = flatness(lat, int(wl.window[0]), int(wl.T))
+        rec["jumps_over_10pct"] = [[int(ts[i]), round(float(us[i] / us[i - 1]), 3)]
+                                   for i in range(1, len(us)) if abs(us[i] / us[i - 1] - 1) > 0.10]
         out[mode] = rec
         log(f"[bench] growth {mode}: median {rec['median_us']:.1f} us/step")
     out["workload"] = wl.name
     return out
+
+
+def steady_leg(args, name: str, steps: int, warmup: int):
+    """Another decode workload at steady state: the cache is built untimed (block-timed for the
+    latency curve), then `warmup` steps, then `steps` timed steps ending at its last step."""
+    import types
+    wl = decode_workload(name)
+    a = types.SimpleNamespace(chunk=args.chunk, grid=args.grid, unfused=args.unfused)
+    setup = int(wl.T) - steps - warmup
+    r = run_decode(a, wl, False, steps, warmup, setup=setup)
+    ms = r["elapsed_ms"] / steps
+    gbs = float((r["dec_bytes"] + r["app_bytes"]).mean()) / (ms * 1e-3) / 1e9
+    lat = r["lat"]
+    keep = np.linspace(0, len(lat) - 1, min(len(lat), 24)).round().astype(int)
+    return dict(workload=wl.name, timed_t=r["timed_t"], steps=steps,
+                tok_s=r["tokens"] / (r["elapsed_ms"] * 1e-3), us_per_step=ms * 1e3,
+                step_bytes=float((r["dec_bytes"] + r["app_bytes"]).mean()), step_gbs=gbs,
+                frac=gbs / PEAK_HBM_GBS, launches_per_step=r["launches_per_step"],
+                latency_vs_t=[[int(lat[i][0]), round(float(lat[i][1]), 3)] for i in keep],
+                flatness=flatness(lat, int(wl.window[0]), int(wl.T)))
 
 
 def ragged_decode(args, steps=3000):
@@ -622,77 +715,101 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     res = dict(metric=METRIC, n_gpus=1, higher_is_better=True, scaling="weak", vs_baseline=None,
                data="synthetic")
+    legs_on = not args.headline_only
     wl = None
     if not args.no_decode:
         t0 = time.perf_counter()
         wl = decode_workload(args.workload)
         log(f"[bench] generated {wl.name} in {time.perf_counter() - t0:.1f} s")
         full = args.mode == "full"
+        n = int(wl.window.max())
         warmup = args.warmup
-        steps = min(args.steps, wl.T - warmup)
-        r = run_decode(args, wl, full, steps, warmup, args.kernel_events)
-        log(f"[bench] decode: {steps} steps in {r['elapsed_ms']:.1f} ms "
-            f"(host wall {r['wall_s']:.2f} s)")
+        steps = args.steps
+        # Whatever --steps / --warmup say, the timed steps are the workload's last ones: the cache
+        # is first built untimed (ring full, steady state), so the figure is the per-step cost
+        # the method keeps constant, not the fill transient.
+        setup = int(wl.T) - steps - warmup
+        if setup < n and not full:
+            raise SystemExit(f"--steps + --warmup = {steps + warmup} leave fewer than n = {n} "
+                             f"set-up steps of T = {wl.T}: the timed steps would fill the ring")
+        r = run_decode(args, wl, full, steps, warmup, args.kernel_events, setup=setup)
+        log(f"[bench] decode: {steps} steps (t = {r['timed_t'][0]}..{r['timed_t'][1]}) in "
+            f"{r['elapsed_ms']:.3f} ms (host wall {r['wall_s']:.3f} s)")
         ms_step = r["elapsed_ms"] / steps
         tok_s = r["tokens"] / (r["elapsed_ms"] * 1e-3)
         step_bytes = float((r["dec_bytes"] + r["app_bytes"]).mean())
         res.update(value=tok_s, unit="tok/s", steps=steps, warmup=warmup, ms_per_step=ms_step,
-                   dtype="f32",
+                   dtype="bf16" if wl.dtype == "bf16" else "f32",
+                   math="fp32 (scores, softmax, accumulation)",
                    config=dict(workload=wl.name, batch=wl.batch, prefix_len=int(wl.prefix_len[0]),
                                window=int(wl.window[0]), T=int(wl.T), kv_dtype=wl.dtype,
-                               mode=args.mode, timed_t=[warmup + 1, warmup + steps]))
+                               mode=args.mode, timed_t=r["timed_t"], setup_steps=setup,
+                               state="ring full (steady state)" if not full else "full causal"))
         res["hbm_gbs_step"] = step_bytes / (ms_step * 1e-3) / 1e9
-        # The dominant kernel is the fused append + decode launch; with equal ranges it is the
-        # step's only launch, so its average duration is the event-bracketed timed region over
-        # the number of steps (no events between launches: recording one per launch costs
-        # several microseconds of GPU time per step and would inflate the figure).
-        per_launch_ms = ms_step if r["launches_per_step"] == 1 else None
+        # The dominant kernel is the fused append + decode launch. When it is the step's only
+        # launch, its average duration is the event-bracketed timed region over the number of
+        # steps (no events between launches: recording one per launch costs several microseconds
+        # of GPU time per step and would inflate the figure).
+        one_launch = r["launches_per_step"] == 1
+        per_launch_ms = ms_step if one_launch else None
         if r["kern_ms"] is not None:  # --kernel-events: bracket every launch (diagnostic)
             per_launch_ms = float(r["kern_ms"].mean())
         if per_launch_ms is not None:
             ach = float(r["launch_bytes"].mean()) / (per_launch_ms * 1e-3) / 1e9
-        else:  # decode + merge launches per step: report the step as the unit
+        else:  # decode + merge launches per step: the step is the unit
             ach = step_bytes / (ms_step * 1e-3) / 1e9
         res["roofline"] = dict(bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
                                frac=ach / PEAK_HBM_GBS,
                                traffic=traffic_from_profile("decode", source_hash(DECODE_SOURCES)),
                                kernel=("fused append + decode step" if r["fused"] else
-                                       "decode (separate append)"),
+                                       "decode (separate append)")
+                               + ("" if one_launch else " (decode + merge launches)"),
                                launches_per_step=r["launches_per_step"],
                                workgroups=r["grid_blocks"],
                                avg_launch_us=(per_launch_ms or ms_step) * 1e3,
                                bytes_per_launch=float(r["launch_bytes"].mean()))
-        res["latency_vs_t"] = [[int(t), round(u, 3)] for t, u in r["lat"]]
-        res["flatness"] = flatness(r["lat"], int(wl.window[0]), warmup + steps)
+        lat = r["lat"]
+        keep = np.linspace(0, len(lat) - 1, min(len(lat), 40)).round().astype(int)
+        res["latency_vs_t"] = [[int(lat[i][0]), round(float(lat[i][1]), 3)] for i in keep]
+        res["flatness"] = flatness(lat, n, int(wl.T))
+        if legs_on and not args.no_growth and args.workload == "multipage" and not full:
+            res["growth"] = growth_curve(args, wl, lat)
     if args.copy_calibration:
         res["copy_calibration"] = copy_calibration()
         log(f"[bench] 1 GiB copy: {res['copy_calibration']['gbs']:.0f} GB/s")
-    if not args.no_decode and not args.no_growth:
-        res["growth"] = growth_curve(args)
-    if not args.no_decode and not args.no_ragged:
+    if legs_on and not args.no_decode:
+        res["batched_mall_resident"] = b = steady_leg(args, "batched", 2000, 100)
+        b["note"] = ("effective GB/s: the 211 MB step working set fits the 256 MB Infinity Cache, "
+                     "so rows are partly served from it rather than from HBM")
+        log(f"[bench] batched (MALL-resident): {b['us_per_step']:.2f} us/step, "
+            f"{b['step_gbs']:.0f} GB/s effective")
+        res["single_fp32"] = s1 = steady_leg(args, "single", 64, 64)
+        s1["note"] = "latency-bound (6.6 MB per step, cache-resident); GB/s effective"
+        log(f"[bench] single-page fp32 B=1: {s1['us_per_step']:.2f} us/step")
+    if legs_on and not args.no_decode and not args.no_ragged:
         res["ragged"] = ragged_decode(args)
         log(f"[bench] ragged: {res['ragged']['us_per_step']:.1f} us/step, "
             f"{res['ragged']['step_gbs']:.0f} GB/s")
-    if not args.no_decode and not args.no_shared:
+    if legs_on and not args.no_decode and not args.no_shared:
         res["shared_documents"] = sd = shared_documents(args)
         log(f"[bench] shared documents: paged {sd['paged']['us_per_step']:.1f} us/step, "
             f"copied {sd['copied']['us_per_step']:.1f} us/step ({sd['speedup']:.2f}x)")
-    if not args.no_decode and not args.no_graph:
+    if legs_on and not args.no_decode and not args.no_graph:
         res["graph_loop"] = gl = graph_loop(args)
         for k2, r2 in gl.items():
             log(f"[bench] graph loop {k2}: eager {r2['eager_us_per_step']:.2f} us/step, "
                 f"graph {r2['graph_us_per_step']:.2f} us/step")
-    if not args.no_prefill:
+    if legs_on and not args.no_prefill:
         p = run_prefill(args)
         if p is not None:
             res["prefill"] = p
             log(f"[bench] prefill: {p['ms']:.3f} ms, {p['tflops']:.1f} TFLOP/s")
-    if not args.no_backward:
+    if legs_on and not args.no_backward:
         bw = run_backward(args)
         res["backward"] = bw
         log(f"[bench] training pass: forward {bw['fwd_ms']:.3f} ms, backward {bw['bwd_ms']:.3f} ms "
             f"({bw['bwd_tflops']:.1f} TFLOP/s), fwd+bwd {bw['train_tflops']:.1f} TFLOP/s")
-    if wl is not None and not args.no_cpu_baseline:
+    if wl is not None and legs_on and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(res))
 

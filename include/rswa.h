@@ -103,8 +103,9 @@ rswa_status rswa_cache_create(const rswa_cache_desc* desc, const void* prefix_k_
                               const void* prefix_v_dev, void* stream, rswa_cache** out);
 
 /* Create a cache whose prefixes live in a shared, token-granular page pool (paged / shared prefix
- * KV; the pages serve the model with a page size of one token and plan a pool of prefill KV
- * chunks: GeekNews "Unlimited OCR", serving flags and limitations). desc->prefix_paged
+ * KV: the SGLang server that the deep dive "Unlimited-OCR" shows infer.py launching runs with a
+ * page size of one token, and GeekNews "Unlimited OCR", limitations and future work, plans a pool
+ * of prefill KV chunks that the model fetches). desc->prefix_paged
  * must be 1. pool_k_dev / pool_v_dev: caller-owned device arrays [pool_rows][H][D] of kv_dtype
  * (token-major: one row per token, 256 B per head in bf16), read during every decode, unchanged
  * and alive until rswa_cache_destroy. prefix_table_dev: device int32 [sum_b m_b]; prefix token j
@@ -124,17 +125,22 @@ rswa_status rswa_cache_create_paged(const rswa_cache_desc* desc, const void* poo
  * head (RSWA: overwriting output t_b - n_b once the ring is full, i.e. the oldest output is
  * evicted; deep dive N(t) code block, GeekNews model architecture section) or to row m_b + t_b
  * (FULL_CAUSAL), then t_b += 1. The counters live on the device, so calls need no host sync.
- * Errors: RSWA_E_INVALID; RSWA_E_CAPACITY when active_dev is NULL and a FULL_CAUSAL sequence
- * already holds max_steps outputs (checked on the host before enqueuing). With an active mask the
- * host cannot see which sequences append; a FULL_CAUSAL append past capacity is then skipped on
- * the device and reported by rswa_cache_steps(). */
+ * Errors: RSWA_E_INVALID; RSWA_E_CAPACITY when a FULL_CAUSAL sequence already holds max_steps
+ * outputs, checked on the host before enqueuing as long as no call on this cache has used an
+ * active mask. Once one has, the host no longer knows each t_b: a FULL_CAUSAL append past capacity
+ * is then skipped on the device (that sequence's counter stays) and reported by rswa_cache_steps()
+ * and rswa_cache_query(). */
 rswa_status rswa_append_kv(rswa_cache* cache, const void* k_dev, const void* v_dev,
                            const uint8_t* active_dev /* [B] or NULL */, void* stream);
 
 /* K2, decode attention (split-K flash decode + merge). For every active sequence b and head h:
  *   out[b][h] = softmax(scale * K_L q[b][h]) V_L
  * over the L_b = m_b + min(n_b, t_b) live rows (RSWA) or m_b + t_b rows (FULL_CAUSAL), i.e. the
- * prefix and the last min(n_b, t_b) appended outputs, the latest one included. q_dev: [B][H][D] of
+ * prefix and the last min(n_b, t_b) appended outputs, the latest one included. This is attention
+ * over the set N(t) = P u D_n(t) of the deep dive "Unlimited-OCR" (N(t) code block: the whole
+ * prefix P plus the previous n outputs) and of GeekNews "Unlimited OCR", R-SWA section (every
+ * token sees all reference tokens; output attention is limited to the previous n tokens, a
+ * two-segment window of size m + n). q_dev: [B][H][D] of
  * kv_dtype; out_dev: [B][H][D] of out_dtype (rows of inactive sequences are left untouched).
  * softmax_scale <= 0 selects 1/sqrt(D). active_dev: [B] or NULL (all).
  * Errors: RSWA_E_INVALID (pointers, out_dtype, or a sequence with m_b = 0 that has had no append
@@ -153,6 +159,10 @@ rswa_status rswa_decode_step(rswa_cache* cache, const void* q_dev, const void* k
                              float softmax_scale, const uint8_t* active_dev, void* stream);
 
 /* K3, R-SWA-masked prefill / teacher-forced pass over packed sequences (bf16 MFMA, fp32 softmax).
+ * The mask is R-SWA's during training: every token sees all reference (prefix) tokens and an
+ * output token sees only its previous n output tokens (GeekNews "Unlimited OCR", R-SWA section;
+ * deep dive "Unlimited-OCR", N(t) code block), over multi-page documents packed into 32K-token
+ * sequences (GeekNews "Unlimited OCR", training section).
  * Sequence s occupies token rows [cu_seqlens[s], cu_seqlens[s+1]) of q/k/v/out, its first
  * m_s = prefix_len[s] tokens being the prefix. Query p (position within the sequence) sees key k
  * iff   k < m_s  and (prefix_causal == 0 or p >= m_s or k <= p)          (the reference prefix)
@@ -167,7 +177,9 @@ rswa_status rswa_decode_step(rswa_cache* cache, const void* q_dev, const void* k
  * prefix_len_dev / window_dev: device int32 [nseq]; m_s in [0, S_s], n_s >= 1.
  * max_seqlen (host) must be >= every S_s; it sizes the launch grid.
  * Errors: RSWA_E_INVALID (host-checkable arguments), RSWA_E_UNSUPPORTED (head_dim), RSWA_E_HIP.
- * Device-side metadata is trusted: the caller guarantees it matches the description above. */
+ * Device-side metadata cannot be checked before the launch. The kernels check it on the device:
+ * a sequence longer than max_seqlen (its rows past max_seqlen are then not written), m_s > S_s,
+ * S_s < 0 or n_s < 1 sets a per-device error word that rswa_prefill_check() reports. */
 rswa_status rswa_prefill_attn(const void* q_dev, const void* k_dev, const void* v_dev,
                               void* out_dev, int32_t out_dtype, const int32_t* cu_seqlens_dev,
                               const int32_t* prefix_len_dev, const int32_t* window_dev,
@@ -201,7 +213,9 @@ rswa_status rswa_prefill_fwd(const void* q_dev, const void* k_dev, const void* v
  * cu_seqlens[nseq]; the work array covers all of them.
  * The library allocates nothing; all work is enqueued on `stream`.
  * Errors: as rswa_prefill_attn, plus RSWA_E_INVALID for NULL dout/lse/work/dq/dk/dv, a bad
- * grad_dtype or total_tokens < 0. Device-side metadata is trusted. */
+ * grad_dtype or total_tokens < 0. Device-side metadata is checked on the device as in
+ * rswa_prefill_attn (a sequence past max_seqlen leaves gradient rows unwritten) and reported by
+ * rswa_prefill_check(). */
 rswa_status rswa_prefill_bwd(const void* q_dev, const void* k_dev, const void* v_dev,
                              const void* out_dev, int32_t out_dtype, const void* dout_dev,
                              const float* lse_dev, float* work_dev, void* dq_dev, void* dk_dev,
@@ -227,12 +241,16 @@ rswa_status rswa_step_graph_create(rswa_cache* cache, int32_t steps, const void*
                                    void* out_slots_dev, int32_t out_dtype, float softmax_scale,
                                    rswa_step_graph** out);
 
-/* Replay the captured steps on `stream` (appends `steps` outputs to every sequence). In
- * FULL_CAUSAL mode RSWA_E_CAPACITY if a replay would pass max_steps. */
+/* Replay the captured steps on `stream` (appends `steps` outputs to every sequence). Eager calls
+ * on the same cache may come between replays: when they leave the step counters in the other
+ * of the two counter buffers, the launch first enqueues a 4*B-byte device copy into the buffer
+ * the graph reads. In FULL_CAUSAL mode RSWA_E_CAPACITY if a replay would pass max_steps (checked
+ * on the host while no active mask has been used on the cache, else on the device). */
 rswa_status rswa_step_graph_launch(rswa_step_graph* graph, void* stream);
 
 /* Release the graph (does not synchronize; the caller must not destroy it while a replay that
- * it enqueued may still be pending). NULL is accepted. */
+ * it enqueued may still be pending). NULL is accepted. Every graph of a cache must be destroyed
+ * before the cache (rswa_cache_destroy refuses otherwise). */
 rswa_status rswa_step_graph_destroy(rswa_step_graph* graph);
 
 /* Copy the per-sequence step counters t_b to steps_host [B]. BLOCKS until `stream` has passed
@@ -259,9 +277,29 @@ rswa_status rswa_cache_set_decode_split(rswa_cache* cache, int32_t chunk_rows, i
 rswa_status rswa_cache_decode_plan(const rswa_cache* cache, int32_t appending,
                                    int32_t* grid_blocks, int32_t* launches);
 
-/* Release the cache: synchronizes the stream it was created on, frees library-owned memory.
- * NULL is accepted. Caller-owned storage is left as is. */
+/* Release the cache: BLOCKS until the whole device is idle (the cache may have been used on any
+ * stream, and freeing device memory waits for the device in any case), then frees library-owned
+ * memory. NULL is accepted. Caller-owned storage is left as is. RSWA_E_INVALID (and nothing is
+ * released) while a step graph of this cache still exists. */
 rswa_status rswa_cache_destroy(rswa_cache* cache);
+
+/* Inspection of a live cache in one call (for tests and snapshots): the storage base pointer and,
+ * per sequence b, the element offsets of its K block and V block (K[b][h][r][i] at
+ * k_offset[b] + (h * R_b + r) * D + i, V likewise from v_offset[b]), R_b, and the step counters
+ * t_b. Layout outputs are host-only; when steps_host is not NULL the call BLOCKS until `stream`
+ * has passed all prior work and returns RSWA_E_CAPACITY as rswa_cache_steps() does. Any output
+ * pointer may be NULL. */
+rswa_status rswa_cache_query(rswa_cache* cache, void** storage_dev,
+                             int64_t* k_offset_host /* [B] */, int64_t* v_offset_host /* [B] */,
+                             int32_t* rows_host /* [B] */, int32_t* steps_host /* [B] */,
+                             void* stream);
+
+/* Report the metadata errors that prefill and backward launches on the current device found on
+ * the device (see rswa_prefill_attn) since the last call, and clear them. BLOCKS until `stream`
+ * has passed all prior work (launches on other streams must be complete too). RSWA_E_INVALID if
+ * any launch found an error, else RSWA_OK. One error word per device: concurrent prefill calls
+ * on one device share it. */
+rswa_status rswa_prefill_check(void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* rswa_status_str(int32_t status);

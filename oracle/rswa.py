@@ -371,8 +371,9 @@ def prefill_backward(Q, K, V, dO, m: int, n: int, prefix_causal: bool = False,
 # ------------------------------------------------------------------------------------------
 def paged_prefix(pool, table, start: int, m: int) -> np.ndarray:
     """Prefix rows of one sequence whose prefix lives in a token pool: prefix token j is pool row
-    table[start + j] (a page table with one token per page, the granularity the pages serve the
-    model with [GeekNews, serving flags]; several sequences may share rows). The attention over
+    table[start + j] (a page table with one token per page, the page size of the SGLang server
+    that infer.py launches [deep dive, the SGLang launch flags]; several sequences may share rows).
+    The attention over
     them is unchanged: `decode_step` with these rows as the prefix."""
     idx = np.asarray(table[start:start + m], dtype=np.int64)
     return np.asarray(pool)[idx]

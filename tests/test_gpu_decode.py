@@ -126,8 +126,34 @@ def test_active_mask_and_capacity(wa):
     with pytest.raises(wa.RswaError) as e:
         tr.cache.steps()
     assert e.value.status == -3
-    with pytest.raises(wa.RswaError) as e:  # without a mask the host sees the overflow first
-        tr.cache.append(tr.k[0], tr.v[0])
+    # after a masked call the host no longer knows t_b: an unmasked append is enqueued, and the
+    # device skips the full sequence (its counter stays) and keeps reporting the overflow
+    tr.cache.append(tr.k[0], tr.v[0])
+    with pytest.raises(wa.RswaError) as e:
+        tr.cache.steps()
+    assert e.value.status == -3
+    tr.cache.close()
+
+
+def test_alternating_masks_then_unmasked_appends(wa):
+    """Full causal, max_steps 6: ten masked calls (alternate sequences) leave t = [5, 5]; an
+    unmasked append must then go through (no spurious capacity error from the host's call count)
+    and a second one must be refused on the device."""
+    wl = W.make_decode("cap-alt", 95, "bf16", [3, 4], [8, 8], [6, 6], seed=5)
+    tr = Trajectory(wa, wl, wa.MODE_FULL_CAUSAL)
+    masks = [torch.tensor(x, dtype=torch.uint8, device="cuda") for x in ([1, 0], [0, 1])]
+    for i in range(10):
+        tr.cache.append(tr.k[i // 2], tr.v[i // 2], masks[i % 2])
+    np.testing.assert_array_equal(tr.cache.steps(), [5, 5])
+    tr.cache.append(tr.k[5], tr.v[5])
+    np.testing.assert_array_equal(tr.cache.steps(), [6, 6])
+    _, ko, vo, rows, st = tr.cache.query()
+    np.testing.assert_array_equal(st, [6, 6])
+    np.testing.assert_array_equal(rows, [3 + 6, 4 + 6])
+    np.testing.assert_array_equal(vo - ko, 16 * rows * 128)
+    tr.cache.append(tr.k[0], tr.v[0])  # past max_steps: skipped on the device, then reported
+    with pytest.raises(wa.RswaError) as e:
+        tr.cache.steps()
     assert e.value.status == -3
     tr.cache.close()
 

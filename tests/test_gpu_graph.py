@@ -104,3 +104,43 @@ def test_odd_step_count_is_rejected(wa):
         wa.StepGraph(tr.cache, 3)
     assert e.value.status == -1
     tr.cache.close()
+
+
+def test_eager_steps_between_replays(wa):
+    """An eager step, a replay, an eager step, a replay ...: the replays must read the counters
+    the eager steps left (in either counter buffer) and give what all-eager steps give."""
+    wl = W.make_decode("graph-mixed", 10, "bf16", [100] * 4, [32] * 4, [40] * 4, seed=14)
+    split = (0, 64)
+    T = 40
+    ref = eager(wa, wl, T, wa.MODE_RSWA, split)
+    tr = Trajectory(wa, wl, wa.MODE_RSWA)
+    tr.cache.set_decode_split(*split)
+    g = wa.StepGraph(tr.cache, 2)
+    out = torch.empty((4, 16, 128), dtype=torch.float32, device="cuda")
+    got = {}
+    t = 0
+    pattern = ["e", "g", "e", "g", "g", "e", "e", "g", "e"] * 3
+    for kind in pattern:
+        if kind == "e" and t + 1 <= T:
+            tr.cache.step(tr.q[t], tr.k[t], tr.v[t], out)
+            torch.cuda.synchronize()
+            got[t + 1] = out.clone()
+            t += 1
+        elif kind == "g" and t + 2 <= T:
+            g.q.copy_(tr.q[t:t + 2])
+            g.k.copy_(tr.k[t:t + 2])
+            g.v.copy_(tr.v[t:t + 2])
+            g.launch()
+            torch.cuda.synchronize()
+            got[t + 1], got[t + 2] = g.out[0].clone(), g.out[1].clone()
+            t += 2
+    assert t >= 20
+    np.testing.assert_array_equal(tr.cache.steps(), t)
+    for s in range(1, t + 1):
+        assert torch.equal(got[s].view(torch.int32), ref[s].view(torch.int32)), s
+    # the cache refuses to go while its graph exists; the graph first, then the cache
+    with pytest.raises(wa.RswaError) as e:
+        tr.cache.close()
+    assert e.value.status == -1
+    g.close()
+    tr.cache.close()

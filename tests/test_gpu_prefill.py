@@ -135,3 +135,30 @@ def test_prefill_full_sequence_sampled_rows(wa):
     err = float(np.abs(got[rows] - ref).max())
     print(f"prefill S={S} m={m}: max abs err {err:.3e} over {rows.size} sampled rows")
     assert err <= TOL
+
+
+def test_prefill_metadata_checked_on_device(wa):
+    """max_seqlen below a sequence's length leaves that sequence's rows past max_seqlen unwritten:
+    the kernels report it through the device error word that rswa_prefill_check() reads (and
+    clears); a launch whose metadata is right reports nothing. Forward and backward."""
+    pw = W.make_prefill("meta", 4, [300, 129], [70, 64], [16, 128], seed=22)
+    q, k, v = upload(pw.q, "bf16"), upload(pw.k, "bf16"), upload(pw.v, "bf16")
+    cu = torch.tensor(pw.cu_seqlens, dtype=torch.int32, device="cuda")
+    m = torch.tensor(pw.prefix_len, dtype=torch.int32, device="cuda")
+    n = torch.tensor(pw.window, dtype=torch.int32, device="cuda")
+    wa.rswa_prefill_check()  # start clean (raises if an earlier test left an error behind)
+    out, lse = wa.rswa_prefill_fwd(q, k, v, cu, m, n, max_seqlen=300)
+    wa.rswa_prefill_check()
+    wa.rswa_prefill_attn(q, k, v, cu, m, n, max_seqlen=200)  # enqueued: the host cannot know
+    with pytest.raises(wa.RswaError) as e:
+        wa.rswa_prefill_check()
+    assert e.value.status == -1
+    wa.rswa_prefill_check()  # cleared by the read
+    dout = upload(W.make_output_grad(pw, seed=1), "bf16")
+    wa.rswa_prefill_bwd(q, k, v, out, dout, lse, cu, m, n, max_seqlen=300)
+    wa.rswa_prefill_check()
+    wa.rswa_prefill_bwd(q, k, v, out, dout, lse, cu, m, n, max_seqlen=100)
+    with pytest.raises(wa.RswaError) as e:
+        wa.rswa_prefill_check()
+    assert e.value.status == -1
+    wa.rswa_prefill_check()

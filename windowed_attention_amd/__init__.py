@@ -29,7 +29,7 @@ EXPORTS = ("rswa_cache_plan", "rswa_cache_bytes", "rswa_cache_create", "rswa_cac
            "rswa_prefill_bwd", "rswa_cache_steps", "rswa_cache_info",
            "rswa_cache_set_decode_split", "rswa_cache_decode_plan", "rswa_cache_destroy",
            "rswa_step_graph_create", "rswa_step_graph_launch", "rswa_step_graph_destroy",
-           "rswa_status_str",
+           "rswa_cache_query", "rswa_prefill_check", "rswa_status_str",
            "rswa_last_error")
 
 
@@ -81,6 +81,8 @@ def _load():
         "rswa_step_graph_create": (i32, [vp, i32, vp, vp, vp, vp, i32, f32, ctypes.POINTER(vp)]),
         "rswa_step_graph_launch": (i32, [vp, vp]),
         "rswa_step_graph_destroy": (i32, [vp]),
+        "rswa_cache_query": (i32, [vp, ctypes.POINTER(vp), pi64, pi64, pi32, pi32, vp]),
+        "rswa_prefill_check": (i32, [vp]),
         "rswa_status_str": (ctypes.c_char_p, [i32]),
         "rswa_last_error": (ctypes.c_char_p, []),
     }
@@ -281,6 +283,22 @@ class RswaCache:
                "rswa_cache_info")
         return p.value, off, rows
 
+    def query(self, stream=None):
+        """(storage pointer, K element offsets [B], V element offsets [B], rows [B], t_b [B]);
+        blocks until `stream` has passed all prior work."""
+        p = ctypes.c_void_p(None)
+        ko = np.zeros(self.batch, dtype=np.int64)
+        vo = np.zeros(self.batch, dtype=np.int64)
+        rows = np.zeros(self.batch, dtype=np.int32)
+        st = np.zeros(self.batch, dtype=np.int32)
+        _check(_lib.rswa_cache_query(self.handle, ctypes.byref(p),
+                                     ko.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                     vo.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                     rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                     st.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                     _stream(stream)), "rswa_cache_query")
+        return p.value, ko, vo, rows, st
+
     def set_decode_split(self, chunk_rows: int = 0, grid_blocks: int = 0) -> None:
         _check(_lib.rswa_cache_set_decode_split(self.handle, chunk_rows, grid_blocks),
                "rswa_cache_set_decode_split")
@@ -475,6 +493,12 @@ def rswa_prefill_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: tor
         _dev(window, "window", torch.int32, (nseq,)), nseq, total, H, D, max_seqlen,
         int(bool(prefix_causal)), ctypes.c_float(scale), _stream(stream)), "rswa_prefill_bwd")
     return dq, dk, dv
+
+
+def rswa_prefill_check(stream=None) -> None:
+    """Raise RswaError if a prefill / backward launch on the current device found bad sequence
+    metadata on the device since the last check (blocks until `stream` is idle)."""
+    _check(_lib.rswa_prefill_check(_stream(stream)), "rswa_prefill_check")
 
 
 def status_str(code: int) -> str:

@@ -81,6 +81,7 @@ struct PrefillArgs {
   int32_t max_seqlen;
   int32_t prefix_causal;
   float scale_log2;
+  int32_t* err;             // [1] set to 1 when the device finds metadata the launch cannot serve
 };
 
 struct BwdArgs {
@@ -104,6 +105,7 @@ struct BwdArgs {
   int32_t prefix_causal;
   float scale;
   float scale_log2;
+  int32_t* err;             // [1] set to 1 when the device finds metadata the launch cannot serve
 };
 
 // Launchers (return the hipError_t of the launch).

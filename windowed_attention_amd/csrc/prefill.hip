@@ -114,6 +114,13 @@ __global__ __launch_bounds__(kThreads, 8 / kWavesPF) void prefill_kernel(Prefill
   const int s = bz, h = by;
   const int cu0 = a.cu_seqlens[s];
   const int S = a.cu_seqlens[s + 1] - cu0;
+  // Metadata the host cannot see, checked once per (sequence, head) by the last tile of the grid:
+  // a sequence longer than the grid covers (its rows past max_seqlen stay unwritten), a prefix
+  // longer than its sequence or a window below 1 set the error word that rswa_prefill_check reads.
+  if (bx == (int)gridDim.x - 1 && threadIdx.x == 0) {
+    const int mm = a.prefix_len[s], nn = a.window[s];
+    if (S < 0 || S > (int)gridDim.x * BMQ || mm < 0 || mm > S || nn < 1) *a.err = 1;
+  }
   const int q0 = bx * BMQ;
   if (q0 >= S) return;
   const int q1 = min(q0 + BMQ, S);

@@ -149,6 +149,11 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
   const int s = idx / (a.heads * nkb);
   const int cu0 = a.cu_seqlens[s];
   const int S = a.cu_seqlens[s + 1] - cu0;
+  // metadata check, as in the forward: the last key block of the grid covers the sequence end
+  if (kblk == nkb - 1 && threadIdx.x == 0) {
+    const int mm = a.prefix_len[s], nn = a.window[s];
+    if (S < 0 || S > nkb * BNK || mm < 0 || mm > S || nn < 1) *a.err = 1;
+  }
   const int k0 = kblk * BNK;
   if (k0 >= S) return;
   const int m = a.prefix_len[s];
@@ -577,6 +582,13 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
   const int s = bz, h = by;
   const int cu0 = a.cu_seqlens[s];
   const int S = a.cu_seqlens[s + 1] - cu0;
+  // Metadata the host cannot see, checked once per (sequence, head) by the last tile of the grid:
+  // a sequence longer than the grid covers (its rows past max_seqlen stay unwritten), a prefix
+  // longer than its sequence or a window below 1 set the error word that rswa_prefill_check reads.
+  if (bx == (int)gridDim.x - 1 && threadIdx.x == 0) {
+    const int mm = a.prefix_len[s], nn = a.window[s];
+    if (S < 0 || S > (int)gridDim.x * BNQ || mm < 0 || mm > S || nn < 1) *a.err = 1;
+  }
   const int q0 = bx * BNQ;
   if (q0 >= S) return;
   const int q1 = min(q0 + BNQ, S);

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -40,12 +41,45 @@ struct DeviceGuard {
   }
 };
 
+// Metadata errors that the prefill and backward kernels find on the device (a sequence longer
+// than its launch's max_seqlen, a prefix longer than its sequence, a window below 1), OR-ed
+// together until rswa_prefill_check() reads and clears them. Each device holds its own copy of
+// this word; host code uses the address hipGetSymbolAddress gives for the current device, never
+// the variable's name (which is only a host-side stand-in).
+__device__ __align__(256) int32_t g_prefill_err;
+
+constexpr int kMaxDevices = 64;
+int32_t* g_prefill_err_ptr[kMaxDevices] = {};
+std::mutex g_statics_mutex;
+
+// Device address of the current device's error word, or nullptr (reason in *e).
+int32_t* prefill_err_word(hipError_t* e) {
+  int dev = -1;
+  *e = hipGetDevice(&dev);
+  if (*e != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *e = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_statics_mutex);
+  if (!g_prefill_err_ptr[dev]) {
+    void* ptr = nullptr;
+    *e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_prefill_err));
+    if (*e != hipSuccess) return nullptr;
+    g_prefill_err_ptr[dev] = reinterpret_cast<int32_t*>(ptr);
+  }
+  return g_prefill_err_ptr[dev];
+}
+
 }  // namespace
 
 struct rswa_cache {
   int32_t B = 0, H = 0, D = 0, kv_dtype = 0, mode = 0;
   rswa::Plan plan;
   std::vector<int64_t> calls;  // appends enqueued per sequence: an upper bound of t_b
+  bool masked = false;         // an active mask has been used: calls[] may overstate t_b, so the
+                               // full-causal capacity check is left to the device
+  int graphs = 0;              // live step graphs that reference this cache
   void* storage = nullptr;
   bool owns_storage = false;
   void* meta_dev = nullptr;
@@ -355,7 +389,7 @@ rswa_status rswa_append_kv(rswa_cache* c, const void* k_dev, const void* v_dev,
   if (!c) return fail(RSWA_E_INVALID, "cache is NULL");
   if (!k_dev || !v_dev) return fail(RSWA_E_INVALID, "k_dev / v_dev is NULL");
   try {
-    if (c->full() && !active_dev) {
+    if (c->full() && !active_dev && !c->masked) {
       for (int b = 0; b < c->B; ++b)
         if (c->calls[b] >= c->plan.cap[b])
           return fail(RSWA_E_CAPACITY, "full-causal append past max_steps");
@@ -376,6 +410,7 @@ rswa_status rswa_append_kv(rswa_cache* c, const void* k_dev, const void* v_dev,
     if (e != hipSuccess) return hip_fail(e, "append launch");
     c->cur ^= 1;
     for (int b = 0; b < c->B; ++b) c->calls[b] += 1;
+    if (active_dev) c->masked = true;
     return RSWA_OK;
   } catch (...) {
     return fail(RSWA_E_INTERNAL, "exception in rswa_append_kv");
@@ -396,7 +431,7 @@ rswa_status decode_launch(rswa_cache* c, const void* q_dev, const void* k_dev, c
     return fail(RSWA_E_INVALID, "softmax_scale must be finite");
   const bool append = k_dev != nullptr;
   try {
-    if (append && c->full() && !active_dev) {
+    if (append && c->full() && !active_dev && !c->masked) {
       for (int b = 0; b < c->B; ++b)
         if (c->calls[b] >= c->plan.cap[b])
           return fail(RSWA_E_CAPACITY, "full-causal append past max_steps");
@@ -441,6 +476,7 @@ rswa_status decode_launch(rswa_cache* c, const void* q_dev, const void* k_dev, c
     if (append) {
       c->cur ^= 1;
       for (int b = 0; b < c->B; ++b) c->calls[b] += 1;
+      if (active_dev) c->masked = true;
     }
     return RSWA_OK;
   } catch (...) {
@@ -469,6 +505,7 @@ struct rswa_step_graph {
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
   int32_t steps = 0;
+  int cur0 = 0;  // counter buffer the captured steps start from (and, steps being even, end in)
 };
 
 namespace {
@@ -504,6 +541,7 @@ rswa_status rswa_step_graph_create(rswa_cache* c, int32_t steps, const void* q_s
     g = new rswa_step_graph();
     g->c = c;
     g->steps = steps;
+    g->cur0 = cur;
     hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
     if (e != hipSuccess) {
       release_graph(g);
@@ -546,6 +584,7 @@ rswa_status rswa_step_graph_create(rswa_cache* c, int32_t steps, const void* q_s
       return hip_fail(e, "hipGraphInstantiate");
     }
     *out = g;
+    c->graphs += 1;
     return RSWA_OK;
   } catch (...) {
     c->calls = calls;
@@ -560,13 +599,23 @@ rswa_status rswa_step_graph_launch(rswa_step_graph* g, void* stream) {
   if (!g) return fail(RSWA_E_INVALID, "graph is NULL");
   rswa_cache* c = g->c;
   try {
-    if (c->full()) {
+    if (c->full() && !c->masked) {
       for (int b = 0; b < c->B; ++b)
         if (c->calls[b] + g->steps > c->plan.cap[b])
           return fail(RSWA_E_CAPACITY, "full-causal append past max_steps");
     }
     DeviceGuard dg(c->device);
-    const hipError_t e = hipGraphLaunch(g->exec, reinterpret_cast<hipStream_t>(stream));
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    // The captured kernels read the counters from buffer cur0. After an odd number of eager
+    // appends since the capture the current counters sit in the other buffer: move them first.
+    if (c->cur != g->cur0) {
+      const hipError_t e = hipMemcpyAsync(c->steps_dev[g->cur0], c->steps_dev[c->cur],
+                                          sizeof(int32_t) * (size_t)c->B,
+                                          hipMemcpyDeviceToDevice, st);
+      if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(step counters)");
+      c->cur = g->cur0;
+    }
+    const hipError_t e = hipGraphLaunch(g->exec, st);
     if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
     for (int b = 0; b < c->B; ++b) c->calls[b] += g->steps;
     return RSWA_OK;
@@ -578,6 +627,7 @@ rswa_status rswa_step_graph_launch(rswa_step_graph* g, void* stream) {
 rswa_status rswa_step_graph_destroy(rswa_step_graph* g) {
   if (!g) return RSWA_OK;
   DeviceGuard dg(g->c->device);
+  g->c->graphs -= 1;
   release_graph(g);
   return RSWA_OK;
 }
@@ -639,11 +689,30 @@ rswa_status rswa_cache_set_decode_split(rswa_cache* c, int32_t chunk_rows, int32
 
 rswa_status rswa_cache_destroy(rswa_cache* c) {
   if (!c) return RSWA_OK;
+  if (c->graphs > 0)
+    return fail(RSWA_E_INVALID, "destroy every step graph of this cache before the cache");
   DeviceGuard g(c->device);
+  // The cache may have been used on any stream; freeing device memory waits for the whole
+  // device anyway, so wait for it once, explicitly, and report its status.
   const hipError_t e = hipDeviceSynchronize();
   release(c);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize(destroy)");
   return RSWA_OK;
+}
+
+rswa_status rswa_cache_query(rswa_cache* c, void** storage_dev, int64_t* k_offset_host,
+                             int64_t* v_offset_host, int32_t* rows_host, int32_t* steps_host,
+                             void* stream) {
+  if (!c) return fail(RSWA_E_INVALID, "cache is NULL");
+  if (storage_dev) *storage_dev = c->storage;
+  for (int b = 0; b < c->B; ++b) {
+    const int64_t k0 = c->plan.seq_off[b];
+    if (k_offset_host) k_offset_host[b] = k0;
+    if (v_offset_host) v_offset_host[b] = k0 + (int64_t)c->H * c->plan.rows[b] * c->D;
+    if (rows_host) rows_host[b] = c->plan.rows[b];
+  }
+  if (!steps_host) return RSWA_OK;
+  return rswa_cache_steps(c, steps_host, stream);
 }
 
 namespace {
@@ -701,8 +770,10 @@ rswa_status prefill_forward(const void* q_dev, const void* k_dev, const void* v_
     a.max_seqlen = max_seqlen;
     a.prefix_causal = prefix_causal;
     a.scale_log2 = scale * 1.4426950408889634f;
-    const hipError_t e = rswa::launch_prefill(a, out_dtype == RSWA_F32,
-                                              reinterpret_cast<hipStream_t>(stream));
+    hipError_t e = hipSuccess;
+    a.err = prefill_err_word(&e);
+    if (!a.err) return hip_fail(e, "hipGetSymbolAddress(error word)");
+    e = rswa::launch_prefill(a, out_dtype == RSWA_F32, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
     return RSWA_OK;
   } catch (...) {
@@ -777,12 +848,40 @@ rswa_status rswa_prefill_bwd(const void* q_dev, const void* k_dev, const void* v
     a.prefix_causal = prefix_causal;
     a.scale = scale;
     a.scale_log2 = scale * 1.4426950408889634f;
-    const hipError_t e = rswa::launch_prefill_bwd(a, out_dtype == RSWA_F32, grad_dtype == RSWA_F32,
-                                                  reinterpret_cast<hipStream_t>(stream));
+    hipError_t e = hipSuccess;
+    a.err = prefill_err_word(&e);
+    if (!a.err) return hip_fail(e, "hipGetSymbolAddress(error word)");
+    e = rswa::launch_prefill_bwd(a, out_dtype == RSWA_F32, grad_dtype == RSWA_F32,
+                                 reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "prefill backward launch");
     return RSWA_OK;
   } catch (...) {
     return fail(RSWA_E_INTERNAL, "exception in rswa_prefill_bwd");
+  }
+}
+
+rswa_status rswa_prefill_check(void* stream) {
+  try {
+    hipError_t e = hipSuccess;
+    int32_t* word = prefill_err_word(&e);
+    if (!word) return hip_fail(e, "hipGetSymbolAddress(error word)");
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    int32_t err = 0;
+    e = hipMemcpyAsync(&err, word, sizeof(err), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e == hipSuccess && err) {
+      const int32_t zero = 0;
+      e = hipMemcpyAsync(word, &zero, sizeof(zero), hipMemcpyHostToDevice, st);
+      if (e == hipSuccess) e = hipStreamSynchronize(st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "reading the prefill error word");
+    if (err)
+      return fail(RSWA_E_INVALID,
+                  "a prefill or backward launch found a sequence longer than its max_seqlen (rows "
+                  "past it were not written), a prefix longer than its sequence, or a window < 1");
+    return RSWA_OK;
+  } catch (...) {
+    return fail(RSWA_E_INTERNAL, "exception in rswa_prefill_check");
   }
 }
 
