@@ -60,7 +60,7 @@ int main() {
       pre += m[b];
     }
     CHECK(p.total_prefix_rows == pre);
-    CHECK(p.bytes == (uint64_t)(off * e));
+    CHECK(p.bytes == (uint64_t)(off * e) + rswa::kStorageTailBytes);
   }
   // invalid descriptions are rejected with a reason
   {
@@ -108,10 +108,10 @@ int main() {
     if (dp.aligned) {
       CHECK(!masked && min_rows == 0 && grid_user == 0);
       for (int b = 0; b < B; ++b) CHECK(L[b] == L[0]);
-      CHECK(dp.grid == (int64_t)B * H && !dp.need_merge);
+      CHECK(dp.grid == (int64_t)B * H && !dp.stream_k);
       CHECK(dp.grid <= std::min(resident, grid_max));
     } else {
-      CHECK(dp.need_merge);
+      CHECK(dp.stream_k);
       CHECK(dp.rows_per_piece >= (min_rows > 0 ? min_rows : 64));
       CHECK(dp.grid * dp.rows_per_piece >= total);
       CHECK((dp.grid - 1) * dp.rows_per_piece < total);

@@ -62,13 +62,13 @@ def test_plan_layout_matches_row_counts(wa):
     np.testing.assert_array_equal(rows, [400, 5, 5219])
     per_seq = 2 * 16 * rows.astype(np.int64) * 128  # K and V, elements
     np.testing.assert_array_equal(off, np.concatenate([[0], np.cumsum(per_seq)[:-1]]))
-    assert nbytes == int(per_seq.sum()) * 2
+    assert nbytes == int(per_seq.sum()) * 2 + 4096  # plus the tail the decode tiles may read
     # batched single-page decode: 64 sequences x (272 + 128) rows x 16 heads x 128 x K,V x bf16
-    assert wa.rswa_cache_bytes([272] * 64, [128] * 64) == 64 * 400 * 16 * 128 * 2 * 2
+    assert wa.rswa_cache_bytes([272] * 64, [128] * 64) == 64 * 400 * 16 * 128 * 2 * 2 + 4096
     # full causal: m + max_steps rows, fp32
     _, rows, nbytes = wa.rswa_cache_plan([7], None, [20], mode=wa.MODE_FULL_CAUSAL,
                                          num_heads=2, kv_dtype=torch.float32)
-    assert rows.tolist() == [27] and nbytes == 2 * 2 * 27 * 128 * 4
+    assert rows.tolist() == [27] and nbytes == 2 * 2 * 27 * 128 * 4 + 4096
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -149,7 +149,7 @@ def test_paged_plan_stores_only_output_rows(wa):
     _, rows_p, bytes_p = wa.rswa_cache_plan(m, n, paged=True)
     np.testing.assert_array_equal(rows_c, m + n)
     np.testing.assert_array_equal(rows_p, n)
-    assert bytes_p == 2 * 16 * 128 * 2 * int(n.sum())
+    assert bytes_p == 2 * 16 * 128 * 2 * int(n.sum()) + 4096
     assert bytes_c - bytes_p == 2 * 16 * 128 * 2 * int(m.sum())
 
 

@@ -14,14 +14,24 @@
 //  * stream-K: the concatenation of all (b, h) key ranges is cut into equal contiguous pieces, one
 //    per resident workgroup, so every workgroup streams the same number of rows (no tail round,
 //    balanced for ragged batches). A piece may cover parts of several ranges; a range split over
-//    several pieces leaves float32 partials (max, sum, numerator[128]) that a second kernel merges:
+//    several pieces leaves float32 partials (max, sum, numerator[128]), and the last of its
+//    pieces to finish merges them in the same launch:
 //      o = sum_s 2^(M_s - M) A_s / sum_s 2^(M_s - M) l_s,   M = max_s M_s.
 //
+// The in-launch merge. A piece publishes its partial with device-scope (agent) stores, waits until
+// they are complete, then adds one to the range's counter with a device-scope atomic; the piece
+// that brings the counter to the range's piece count reads every partial with device-scope loads,
+// writes the output and resets the counter for the next launch. Device-scope stores and loads
+// reach the point where the XCDs' L2 caches are coherent, so no L2 write-back or invalidate (what
+// a release / acquire fence at device scope costs, once per workgroup) is needed; measured, those
+// fences made the step several times slower, and a separate merge launch costs a kernel dispatch
+// (about 2.7 us back to back on MI355X) plus a memory round trip for its plan.
+//
 // Inside a piece. A row of K or V is 256 B (bf16) or 512 B (fp32): 16 or 32 lanes each load 16 B of
-// it, so a wave streams 4 (bf16) or 2 (fp32) rows per load instruction, 1 KiB contiguous. Load
-// latency is covered by the other resident waves of the CU (loading the next tile into registers
-// ahead of the current one's reduction, RSWA_DECODE_PREFETCH=1, measured no faster and costs
-// registers, so it is off). Each lane group keeps its own
+// it, so a wave streams 4 (bf16) or 2 (fp32) rows per load instruction, 1 KiB contiguous. Two
+// register sets alternate: the loads of the next tile are issued before the current tile is
+// reduced, always (rows clamped to the range; past its end they re-read its last row, which the
+// caches hold), so the compiler's waits leave them in flight. Each lane group keeps its own
 // float32 online-softmax state (running max in the log2 domain, running sum, 8 or 4 output dims);
 // q.k partial dot products are summed across the group with DPP row operations. At the end of a
 // range the group states are merged through LDS.
@@ -37,13 +47,10 @@
 namespace rswa {
 namespace {
 
-#ifndef RSWA_DECODE_PREFETCH
-#define RSWA_DECODE_PREFETCH 0  // 1: load the next row tile while reducing the current one
-#endif
-
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxGroups = kWaves * 4;  // bf16: 4 row groups per wave
+constexpr float kLazy = 8.f;            // log2-domain slack before the reference max moves
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -70,8 +77,7 @@ __device__ __forceinline__ SeqState seq_state(const DecodeArgs& a, int b) {
 }
 
 // Work table in LDS: s_len[b] = live rows, s_new[b] = cache row of this launch's new k/v (or -1),
-// s_cum[b] = sum over b' < b of H * L_b' (int64). Block 0 also publishes the plan for the merge
-// kernel and advances the step counters.
+// s_cum[b] = sum over b' < b of H * L_b' (int64). Block 0 also advances the step counters.
 __device__ void build_work_table(const DecodeArgs& a, int* s_len, int* s_new, int64_t* s_cum) {
   __shared__ int64_t s_wave_tot[kWaves];
   __shared__ int64_t s_carry;
@@ -169,15 +175,23 @@ __device__ __forceinline__ void unpack_v<float>(const u32x4& v, float* f) {
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Device-scope (agent) accesses of the merge workspace: coherent across the XCDs' L2 caches
+// without a cache write-back or invalidate.
+__device__ __forceinline__ void st_dev(float* p, float x) {
+  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this thread's stores are complete (device-scope stores: visible to every XCD).
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Combine the np partials of range s stored at workspace slots f + s .. f + s + np - 1 and write
-// the output; threads [0, 128) hold one output dim each. (Merging inside the decode kernel, by the
-// last workgroup to publish a partial, needs agent-scope release/acquire fences in every
-// workgroup; measured on MI355X that costs about 5x the whole step, so the merge is its own
-// launch.)
-// The (max, sum) pairs are loaded in parallel and reduced in LDS; the numerators are accumulated
-// with independent loads, so the merge costs a few memory round trips, not one per partial.
+// the output; threads [0, 128) hold one output dim each. Partial (max, sum) pairs sit at
+// ws_ml[2 slot], ws_ml[2 slot + 1]. Every partial of the range is requested at once (up to
+// kMergeFast), so the merge waits for memory once instead of once per piece.
 constexpr int kMergeChunk = kHeadDim;
-constexpr int kMergeFast = 16;  // pieces per range merged from registers in one memory round trip
+constexpr int kMergeFast = 16;
 
 template <typename OUT>
 __device__ __forceinline__ void merge_range(const DecodeArgs& a, int64_t s, int64_t f, int np,
@@ -185,17 +199,16 @@ __device__ __forceinline__ void merge_range(const DecodeArgs& a, int64_t s, int6
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   constexpr int NW = kHeadDim / kWave;
   const bool worker = tid < kHeadDim;
-  const float2* ml = a.ws_ml + f + s;
+  const float* ml = a.ws_ml + 2 * (f + s);
   const float* acc = a.ws_acc + (f + s) * kHeadDim + (worker ? tid : 0);
   float M = kNegBig;
   if (np <= kMergeFast) {
-    // Few pieces (the usual case): every partial of the range is requested at once, so the merge
-    // waits for memory once instead of once per dependent step.
-    const float2 p = tid < np ? ml[tid] : make_float2(kNegBig, 0.f);
+    const float pm = tid < np ? ld_dev(ml + 2 * tid) : kNegBig;
+    const float pl = tid < np ? ld_dev(ml + 2 * tid + 1) : 0.f;
     float x[kMergeFast];
 #pragma unroll
-    for (int i = 0; i < kMergeFast; ++i) x[i] = i < np ? acc[(int64_t)i * kHeadDim] : 0.f;
-    M = p.x;
+    for (int i = 0; i < kMergeFast; ++i) x[i] = (worker && i < np) ? ld_dev(acc + (int64_t)i * kHeadDim) : 0.f;
+    M = pm;
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     if (lane == 0 && wave < NW) s_red[wave] = M;
@@ -204,8 +217,8 @@ __device__ __forceinline__ void merge_range(const DecodeArgs& a, int64_t s, int6
 #pragma unroll
     for (int w = 1; w < NW; ++w) M = fmaxf(M, s_red[w]);
     if (tid < np) {
-      s_w[tid] = fast_exp2(p.x - M);
-      s_l[tid] = p.y;
+      s_w[tid] = fast_exp2(pm - M);
+      s_l[tid] = pl;
     }
     __syncthreads();
     float lsum = 0.f, num = 0.f;
@@ -220,7 +233,7 @@ __device__ __forceinline__ void merge_range(const DecodeArgs& a, int64_t s, int6
     return;
   }
   if (worker)
-    for (int i = tid; i < np; i += kHeadDim) M = fmaxf(M, ml[i].x);
+    for (int i = tid; i < np; i += kHeadDim) M = fmaxf(M, ld_dev(ml + 2 * i));
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   if (lane == 0 && wave < NW) s_red[wave] = M;
@@ -233,24 +246,23 @@ __device__ __forceinline__ void merge_range(const DecodeArgs& a, int64_t s, int6
     const int n = min(kMergeChunk, np - c);
     __syncthreads();
     if (tid < n) {
-      const float2 p = ml[c + tid];
-      s_w[tid] = fast_exp2(p.x - M);
-      s_l[tid] = p.y;
+      s_w[tid] = fast_exp2(ld_dev(ml + 2 * (c + tid)) - M);
+      s_l[tid] = ld_dev(ml + 2 * (c + tid) + 1);
     }
     __syncthreads();
     if (worker) {
       int i = 0;
       for (; i + 4 <= n; i += 4) {
-        const float x0 = acc[(int64_t)(c + i) * kHeadDim];
-        const float x1 = acc[(int64_t)(c + i + 1) * kHeadDim];
-        const float x2 = acc[(int64_t)(c + i + 2) * kHeadDim];
-        const float x3 = acc[(int64_t)(c + i + 3) * kHeadDim];
+        const float x0 = ld_dev(acc + (int64_t)(c + i) * kHeadDim);
+        const float x1 = ld_dev(acc + (int64_t)(c + i + 1) * kHeadDim);
+        const float x2 = ld_dev(acc + (int64_t)(c + i + 2) * kHeadDim);
+        const float x3 = ld_dev(acc + (int64_t)(c + i + 3) * kHeadDim);
         num = fmaf(x0, s_w[i], num);
         num = fmaf(x1, s_w[i + 1], num);
         num = fmaf(x2, s_w[i + 2], num);
         num = fmaf(x3, s_w[i + 3], num);
       }
-      for (; i < n; ++i) num = fmaf(acc[(int64_t)(c + i) * kHeadDim], s_w[i], num);
+      for (; i < n; ++i) num = fmaf(ld_dev(acc + (int64_t)(c + i) * kHeadDim), s_w[i], num);
       for (int j = 0; j < n; ++j) lsum = fmaf(s_l[j], s_w[j], lsum);
     }
   }
@@ -259,25 +271,31 @@ __device__ __forceinline__ void merge_range(const DecodeArgs& a, int64_t s, int6
 }
 
 // Stream rows [r0, r1) of range (b, h); finish with the group merge through LDS, then either the
-// output (the range is not split) or a partial in workspace slot `slot`.
+// output (the range is not split) or a partial in workspace slot `slot`, published at device
+// scope. Returns (in every thread) whether this piece is the last of the range's np pieces to
+// publish, in which case the caller merges.
 template <typename KV, typename OUT, int U>
-__device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int h, int r0, int r1,
-                                             int rnew, bool direct, int64_t slot, float* s_m,
-                                             float* s_l, float* s_acc) {
+__device__ __forceinline__ bool decode_range(const DecodeArgs& a, int b, int h, int r0, int r1,
+                                             int rnew, bool direct, int64_t slot, int np,
+                                             float* s_m, float* s_l, float* s_acc, int* s_flag) {
   constexpr int VEC = Lanes<KV>::VEC, GL = Lanes<KV>::GL, G = kWave / GL, NG = kWaves * G;
   constexpr int STEP = kWaves * G * U;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // tile decisions are scalar
   const int g = lane / GL, li = lane % GL;
   const int H = a.heads;
   const int64_t R = a.meta.rows[b];
   const int m = a.meta.prefix_len[b];
-  // Cache row r lives at Kp + r * D; with a paged prefix the storage starts at row m, and rows
+  // Cache row r lives at Kh + r * D; with a paged prefix the storage starts at row m, and rows
   // r < m are pool rows found through the page table (one 4-byte lookup per row and group).
   const bool paged = a.meta.table != nullptr;
   const int64_t shift = paged ? m : 0;
   KV* seq = reinterpret_cast<KV*>(a.storage) + a.meta.seq_off[b];
-  KV* Kp = seq + ((int64_t)h * R - shift) * kHeadDim + li * VEC;
-  KV* Vp = seq + ((int64_t)(H + h) * R - shift) * kHeadDim + li * VEC;
+  KV* Kh = seq + ((int64_t)h * R - shift) * kHeadDim;
+  KV* Vh = seq + ((int64_t)(H + h) * R - shift) * kHeadDim;
+  KV* Kp = Kh + li * VEC;
+  KV* Vp = Vh + li * VEC;
+  const int lane_el = g * kHeadDim + li * VEC;  // this lane's 16 B in a tile's first row group
   const int32_t* tab = paged ? a.meta.table + a.meta.table_off[b] : nullptr;
   const KV* PKp = paged ? reinterpret_cast<const KV*>(a.meta.pool_k) + h * kHeadDim + li * VEC
                         : nullptr;
@@ -288,70 +306,122 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int h, 
   const u32x4 qv = ld16(reinterpret_cast<const KV*>(a.q) + bh * kHeadDim + li * VEC);
   const KV* kin = a.k_new ? reinterpret_cast<const KV*>(a.k_new) + bh * kHeadDim + li * VEC : nullptr;
   const KV* vin = a.v_new ? reinterpret_cast<const KV*>(a.v_new) + bh * kHeadDim + li * VEC : nullptr;
+  const float c = a.scale_log2;
 
-  float m_run = kNegBig, l_run = 0.f;
+  // Softmax state per lane group, log2 domain, against a lazily moved reference max: the state is
+  // rescaled only when a score passes the reference by kLazy, so a probability never exceeds
+  // 2^kLazy and most tiles skip the rescale (a scalar branch on a wave ballot).
+  float m_ref = kNegBig, m_thr = kNegBig, l_run = 0.f;
   float acc[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
 
-  u32x4 kc[U], vc[U];
-  int rb = r0 + wave * (G * U);
-  auto load = [&](int base, u32x4* kr, u32x4* vr) {
+  // The new row (fused append): its k / v come from the input, loaded once into registers; the
+  // tile that holds it swaps them in and writes them into the ring slot.
+  // Only the piece whose rows hold the new row touches it (a tile running past the piece's end
+  // may reach the next piece's new row; that row is masked there).
+  u32x4 knew = {0u, 0u, 0u, 0u}, vnew = {0u, 0u, 0u, 0u};
+  const int rn = (rnew >= r0 && rnew < r1) ? rnew : -1;
+  if (rn >= 0) {
+    knew = ld16(kin);
+    vnew = ld16(vin);
+  }
+
+  auto reduce = [&](int base, u32x4* kc, u32x4* vc) {
+    if ((unsigned)(rn - base) < (unsigned)(G * U)) {  // this tile holds the new row
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int row = base + u * G + g;
-      const int rr = min(row, r1 - 1);
-      const bool fresh = rr == rnew;
-      if (paged && rr < m) {
-        const int64_t pr = (int64_t)tab[rr] * pool_stride;
-        kr[u] = ld16(PKp + pr);
-        vr[u] = ld16(PVp + pr);
-      } else {
-        kr[u] = ld16(fresh ? kin : Kp + (int64_t)rr * kHeadDim);
-        vr[u] = ld16(fresh ? vin : Vp + (int64_t)rr * kHeadDim);
+      for (int u = 0; u < U; ++u) {
+        const int row = base + u * G + g;
+        if (row == rn) {
+          kc[u] = knew;
+          vc[u] = vnew;
+          *reinterpret_cast<u32x4*>(Kp + (int64_t)row * kHeadDim) = knew;
+          *reinterpret_cast<u32x4*>(Vp + (int64_t)row * kHeadDim) = vnew;
+        }
       }
     }
-  };
-  if (rb < r1) load(rb, kc, vc);
-  for (; rb < r1; rb += STEP) {
-    u32x4 kn[U], vn[U];
-    const bool more = rb + STEP < r1;
-    if (RSWA_DECODE_PREFETCH && more) load(rb + STEP, kn, vn);
-    float s[U];
-    float mx = -INFINITY;
+    float d[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int row = rb + u * G + g;
-      const float d = group_sum<KV>(partial_dot<KV>(qv, kc[u]));
-      s[u] = row < r1 ? d * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, s[u]);
-      if (row == rnew && row < r1) {  // the new row: store it into its slot
-        *reinterpret_cast<u32x4*>(Kp + (int64_t)row * kHeadDim) = kc[u];
-        *reinterpret_cast<u32x4*>(Vp + (int64_t)row * kHeadDim) = vc[u];
-      }
+    for (int u = 0; u < U; ++u) d[u] = group_sum<KV>(partial_dot<KV>(qv, kc[u]));
+    if (base + G * U > r1) {  // the range ends inside this tile: rows past it do not count, and
+                              // their values (whatever the memory holds) must not reach acc
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (base + u * G + g >= r1) {
+          d[u] = -INFINITY;
+          vc[u] = u32x4{0u, 0u, 0u, 0u};
+        }
     }
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);
-    l_run *= alpha;
+    float mx = d[0];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) acc[i] *= alpha;
+    for (int u = 1; u < U; ++u) mx = fmaxf(mx, d[u]);
+    const float cand = mx * c;
+    if (__builtin_amdgcn_ballot_w64(cand > m_thr)) {
+      const float m_new = fmaxf(m_ref, cand);
+      const float alpha = fast_exp2(m_ref - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] *= alpha;
+      m_ref = m_new;
+      m_thr = m_new + kLazy;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float p = fast_exp2(s[u] - m_new);
+      const float p = fast_exp2(fmaf(d[u], c, -m_ref));
       l_run += p;
       float vf[VEC];
       unpack_v<KV>(vc[u], vf);
 #pragma unroll
       for (int i = 0; i < VEC; ++i) acc[i] = fmaf(p, vf[i], acc[i]);
     }
-    m_run = m_new;
-    if (more) {
-      if (!RSWA_DECODE_PREFETCH) load(rb + STEP, kn, vn);
+  };
+
+  int rb = r0 + wave * (G * U);
+  u32x4 ka[U], va[U], kb[U], vb[U];
+  if (paged) {
+    // Prefix rows looked up in the page table (a tile may straddle the prefix end): a plain loop.
+    const int pend = min(m, r1);
+    for (; rb < pend; rb += STEP) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        kc[u] = kn[u];
-        vc[u] = vn[u];
+        const int rr = min(rb + u * G + g, r1 - 1);
+        if (rr < m) {
+          const int64_t pr = (int64_t)tab[rr] * pool_stride;
+          ka[u] = ld16(PKp + pr);
+          va[u] = ld16(PVp + pr);
+        } else {
+          ka[u] = ld16(Kp + (int64_t)rr * kHeadDim);
+          va[u] = ld16(Vp + (int64_t)rr * kHeadDim);
+        }
       }
+      reduce(rb, ka, va);
+    }
+  }
+  if (rb < r1) {
+    // Cache rows: a scalar tile base plus fixed lane offsets, no clamps. The rows of the last tile
+    // past the range belong to the next range, or to the storage's tail bytes, and are masked.
+    // Two register sets alternate, and the tile after this wave's last is its last again (the
+    // caches hold it), so every load can be issued a tile ahead without a condition.
+    const int last = rb + ((r1 - 1 - rb) / STEP) * STEP;
+    auto load = [&](int base, u32x4* kr, u32x4* vr) {
+      const KV* kt = Kh + (int64_t)base * kHeadDim + lane_el;
+      const KV* vt = Vh + (int64_t)base * kHeadDim + lane_el;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        kr[u] = ld16(kt + u * G * kHeadDim);
+        vr[u] = ld16(vt + u * G * kHeadDim);
+      }
+    };
+    load(rb, ka, va);
+    for (;;) {
+      load(min(rb + STEP, last), kb, vb);
+      reduce(rb, ka, va);
+      rb += STEP;
+      if (rb > last) break;
+      load(min(rb + STEP, last), ka, va);
+      reduce(rb, kb, vb);
+      rb += STEP;
+      if (rb > last) break;
     }
   }
 
@@ -359,7 +429,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int h, 
 #pragma unroll
   for (int i = 0; i < VEC; ++i) s_acc[gid * kHeadDim + li * VEC + i] = acc[i];
   if (li == 0) {
-    s_m[gid] = m_run;
+    s_m[gid] = m_ref;
     s_l[gid] = l_run;
   }
   __syncthreads();
@@ -377,11 +447,28 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int h, 
     if (direct) {
       store_out(reinterpret_cast<OUT*>(a.out) + bh * kHeadDim + tid, num / lsum);
     } else {
-      a.ws_acc[slot * kHeadDim + tid] = num;
-      if (tid == 0) a.ws_ml[slot] = make_float2(M, lsum);
+      st_dev(a.ws_acc + slot * kHeadDim + tid, num);
+      if (tid == 0) {
+        st_dev(a.ws_ml + 2 * slot, M);
+        st_dev(a.ws_ml + 2 * slot + 1, lsum);
+      }
+      wait_stores();
     }
   }
+  if (direct) {
+    __syncthreads();
+    return false;
+  }
+  __syncthreads();  // every store of the partial is complete
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(a.ws_cnt + bh, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == np - 1;
+    if (last) __hip_atomic_store(a.ws_cnt + bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = last;
+  }
   __syncthreads();
+  return *s_flag != 0;
 }
 
 template <typename KV, typename OUT, int U>
@@ -389,6 +476,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
   __shared__ float s_m[kMaxGroups], s_l[kMaxGroups];
   __shared__ float s_acc[kMaxGroups * kHeadDim];
+  __shared__ float s_w[kMergeChunk], s_lw[kMergeChunk];
+  __shared__ float s_red[kHeadDim / kWave];
+  __shared__ int s_flag;
   int64_t* s_cum = reinterpret_cast<int64_t*>(s_dyn);
   int* s_len = reinterpret_cast<int*>(s_cum + a.batch + 1);
   int* s_new = s_len + a.batch;
@@ -400,15 +490,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const int s = blockIdx.x;
     const int b = s / H, h = s - (s / H) * H;
     if (b >= a.batch || s_len[b] == 0) return;
-    decode_range<KV, OUT, U>(a, b, h, 0, s_len[b], s_new[b], true, 0, s_m, s_l, s_acc);
+    decode_range<KV, OUT, U>(a, b, h, 0, s_len[b], s_new[b], true, 0, 1, s_m, s_l, s_acc,
+                             &s_flag);
     return;
   }
 
   const int64_t W = piece_rows(a, total);
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    for (int b = 0; b <= a.batch; ++b) a.ws_cum[b] = s_cum[b];
-    a.ws_cum[a.batch + 1] = W;
-  }
   int64_t pos = (int64_t)blockIdx.x * W;
   const int64_t end = min(pos + W, total);
   while (pos < end) {
@@ -425,28 +512,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const int r1 = (int)min((int64_t)L, r0 + (end - pos));
     const int s = b * H + h;
     const int64_t A = s_cum[b] + (int64_t)h * L;
-    const bool direct = A / W == (A + L - 1) / W;
-    decode_range<KV, OUT, U>(a, b, h, r0, r1, s_new[b], direct, (int64_t)blockIdx.x + s, s_m,
-                             s_l, s_acc);
+    const int64_t f = A / W, l = (A + L - 1) / W;  // pieces that hold rows of this range
+    const bool direct = f == l;
+    if (decode_range<KV, OUT, U>(a, b, h, r0, r1, s_new[b], direct, (int64_t)blockIdx.x + s,
+                                 (int)(l - f + 1), s_m, s_l, s_acc, &s_flag))
+      merge_range<OUT>(a, s, f, (int)(l - f + 1), s_w, s_lw, s_red);
     pos += r1 - r0;
   }
-}
-
-// One workgroup per (b, h): combine the partials of a range split over several pieces.
-template <typename OUT>
-__global__ __launch_bounds__(kHeadDim) void decode_merge_kernel(DecodeArgs a) {
-  __shared__ float s_w[kMergeChunk], s_l[kMergeChunk];
-  __shared__ float s_red[kHeadDim / kWave];
-  const int s = blockIdx.x;
-  const int b = s / a.heads, h = s - (s / a.heads) * a.heads;
-  const int64_t c0 = a.ws_cum[b], c1 = a.ws_cum[b + 1];
-  const int64_t L = (c1 - c0) / a.heads;
-  if (L == 0) return;
-  const int64_t W = a.ws_cum[a.batch + 1];
-  const int64_t A = c0 + h * L;
-  const int64_t f = A / W, l = (A + L - 1) / W;
-  if (f == l) return;  // written directly by the decode kernel
-  merge_range<OUT>(a, s, f, (int)(l - f + 1), s_w, s_l, s_red);
 }
 
 #ifndef RSWA_DECODE_ROWS
@@ -455,20 +527,11 @@ __global__ __launch_bounds__(kHeadDim) void decode_merge_kernel(DecodeArgs a) {
 constexpr int kRowsPerLane = RSWA_DECODE_ROWS;  // U: rows each lane group loads per tile
 
 template <typename KV, typename OUT>
-hipError_t launch_typed(const DecodeArgs& a, int grid, bool need_merge, hipStream_t s) {
-  const size_t smem = decode_lds_bytes(a.batch);
-  if (grid > 0) {
-    hipLaunchKernelGGL((decode_kernel<KV, OUT, kRowsPerLane>), dim3(grid), dim3(kThreads), smem,
-                       s, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (need_merge) {
-    hipLaunchKernelGGL((decode_merge_kernel<OUT>), dim3(a.batch * a.heads), dim3(kHeadDim), 0, s,
-                       a);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+hipError_t launch_typed(const DecodeArgs& a, int grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((decode_kernel<KV, OUT, kRowsPerLane>), dim3(grid), dim3(kThreads),
+                     decode_lds_bytes(a.batch), s, a);
+  return hipGetLastError();
 }
 
 template <typename KV, typename OUT>
@@ -483,13 +546,13 @@ int occupancy_typed(int batch) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int kv_f32, int out_f32, int grid_blocks,
-                         bool need_merge, hipStream_t s) {
+                         hipStream_t s) {
   if (kv_f32) {
-    return out_f32 ? launch_typed<float, float>(a, grid_blocks, need_merge, s)
-                   : launch_typed<float, uint16_t>(a, grid_blocks, need_merge, s);
+    return out_f32 ? launch_typed<float, float>(a, grid_blocks, s)
+                   : launch_typed<float, uint16_t>(a, grid_blocks, s);
   }
-  return out_f32 ? launch_typed<uint16_t, float>(a, grid_blocks, need_merge, s)
-                 : launch_typed<uint16_t, uint16_t>(a, grid_blocks, need_merge, s);
+  return out_f32 ? launch_typed<uint16_t, float>(a, grid_blocks, s)
+                 : launch_typed<uint16_t, uint16_t>(a, grid_blocks, s);
 }
 
 size_t decode_lds_bytes(int batch) {

@@ -47,8 +47,9 @@ struct DecodeArgs {
   void* out;                // [B][H][D]
   const uint8_t* active;    // [B] or nullptr
   float* ws_acc;            // [slots][D] partial numerators
-  float2* ws_ml;            // [slots] partial (max, sum), log2 domain
-  int64_t* ws_cum;          // [B + 2]: row prefix sums (stream-K plan) and rows per workgroup
+  float* ws_ml;             // [slots][2] partial (max, sum), log2 domain
+  int32_t* ws_cnt;          // [B * H] pieces of each split range done in this launch (zero
+                            // between launches: the last piece resets it)
   int32_t batch;
   int32_t heads;
   int32_t full_causal;
@@ -112,7 +113,7 @@ struct BwdArgs {
 hipError_t launch_prefix_copy(const PrefixCopyArgs& a, int kv_f32, int max_rows, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, int batch, int kv_f32, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int kv_f32, int out_f32, int grid_blocks,
-                         bool need_merge, hipStream_t s);
+                         hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int out_f32, hipStream_t s);
 // Sets *bad = 1 if any of the n table entries lies outside [0, pool_rows).
 hipError_t launch_table_check(const int32_t* table, int64_t n, int64_t pool_rows, int32_t* bad,

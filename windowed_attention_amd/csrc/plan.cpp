@@ -62,7 +62,7 @@ rswa_status make_plan(const rswa_cache_desc* d, Plan* p, std::string* why) {
       return bad(RSWA_E_INVALID, "cache too large");
     off += elems;
   }
-  p->bytes = (uint64_t)off * (uint64_t)p->elem;
+  p->bytes = (uint64_t)off * (uint64_t)p->elem + kStorageTailBytes;
   return RSWA_OK;
 }
 
@@ -89,7 +89,7 @@ DecodePlan plan_decode(const std::vector<int64_t>& live_rows, int32_t heads, int
   const int64_t w_min = min_rows > 0 ? min_rows : 64;
   p.rows_per_piece = std::max<int64_t>(w_min, (total + g_req - 1) / g_req);
   p.grid = (total + p.rows_per_piece - 1) / p.rows_per_piece;
-  p.need_merge = true;
+  p.stream_k = true;
   return p;
 }
 

@@ -14,6 +14,9 @@ namespace rswa {
 constexpr int32_t kMaxBatch = 2048;
 constexpr int32_t kMaxHeads = 1024;
 constexpr int32_t kPlanHeadDim = 128;
+// Bytes after the last row of the storage that the decode kernel may read but never uses: its
+// loads cover whole row tiles, and the last tile of the last range can pass the final row.
+constexpr uint64_t kStorageTailBytes = 4096;
 
 struct Plan {
   std::vector<int64_t> seq_off;   // element offset of sequence b's K block
@@ -35,7 +38,7 @@ struct DecodePlan {
   bool aligned = false;  // one workgroup per (b, h) key range
   int64_t grid = 0;      // workgroups to launch (0: nothing to do)
   int64_t rows_per_piece = 0;  // stream-K piece size for the host's row counts
-  bool need_merge = false;
+  bool stream_k = false;    // ranges cut into pieces (split ranges merged in the same launch)
 };
 
 // live_rows: per-sequence live rows (upper bounds) after the launch's append; resident: decode

@@ -89,8 +89,8 @@ struct rswa_cache {
   int64_t* prefix_row0_dev = nullptr;
   void* ws_dev = nullptr;
   float* ws_acc = nullptr;
-  float2* ws_ml = nullptr;
-  int64_t* ws_cum = nullptr;
+  float* ws_ml = nullptr;
+  int32_t* ws_cnt = nullptr;
   int32_t grid_max = 0;  // stream-K workgroups the workspace is sized for
   int32_t min_rows = 0;  // user setting (0 = automatic)
   int32_t grid_user = 0; // user setting (0 = automatic)
@@ -297,9 +297,9 @@ rswa_status create_cache(const rswa_cache_desc* desc, const void* prefix_k_dev,
     c->grid_max = std::max(1, c->num_cus * std::max(c->blocks_per_cu, 8));
     const size_t ws_slots = (size_t)c->grid_max + (size_t)B * c->H;
     const size_t ws_acc_bytes = align_up(ws_slots * rswa::kPlanHeadDim * sizeof(float), 256);
-    const size_t ws_ml_bytes = align_up(ws_slots * sizeof(float2), 256);
-    const size_t ws_cum_bytes = align_up(((size_t)B + 2) * sizeof(int64_t), 256);
-    const size_t ws_bytes = ws_acc_bytes + ws_ml_bytes + ws_cum_bytes;
+    const size_t ws_ml_bytes = align_up(ws_slots * 2 * sizeof(float), 256);
+    const size_t ws_cnt_bytes = align_up((size_t)B * c->H * sizeof(int32_t), 256);
+    const size_t ws_bytes = ws_acc_bytes + ws_ml_bytes + ws_cnt_bytes;
     e = hipMalloc(&c->ws_dev, ws_bytes);
     if (e != hipSuccess) {
       c->ws_dev = nullptr;
@@ -308,8 +308,14 @@ rswa_status create_cache(const rswa_cache_desc* desc, const void* prefix_k_dev,
     }
     unsigned char* wb = reinterpret_cast<unsigned char*>(c->ws_dev);
     c->ws_acc = reinterpret_cast<float*>(wb);
-    c->ws_ml = reinterpret_cast<float2*>(wb + ws_acc_bytes);
-    c->ws_cum = reinterpret_cast<int64_t*>(wb + ws_acc_bytes + ws_ml_bytes);
+    c->ws_ml = reinterpret_cast<float*>(wb + ws_acc_bytes);
+    c->ws_cnt = reinterpret_cast<int32_t*>(wb + ws_acc_bytes + ws_ml_bytes);
+    // the split-range counters start at zero; every launch leaves them at zero
+    e = hipMemsetAsync(c->ws_cnt, 0, ws_cnt_bytes, st);
+    if (e != hipSuccess) {
+      release(c);
+      return hip_fail(e, "hipMemsetAsync(workspace counters)");
+    }
 
     if (paged) {
       // every page-table entry must name a pool row: checked once here, so decode never reads
@@ -456,7 +462,7 @@ rswa_status decode_launch(rswa_cache* c, const void* q_dev, const void* k_dev, c
     a.active = active_dev;
     a.ws_acc = c->ws_acc;
     a.ws_ml = c->ws_ml;
-    a.ws_cum = c->ws_cum;
+    a.ws_cnt = c->ws_cnt;
     a.batch = c->B;
     a.heads = c->H;
     a.full_causal = c->full();
@@ -467,11 +473,8 @@ rswa_status decode_launch(rswa_cache* c, const void* q_dev, const void* k_dev, c
     const rswa::DecodePlan plan = rswa::plan_decode(L, c->H, resident, c->grid_max, c->min_rows,
                                                     c->grid_user, active_dev != nullptr);
     a.aligned = plan.aligned ? 1 : 0;
-    const int64_t grid = plan.grid;
-    const bool need_merge = plan.need_merge;
     const hipError_t e = rswa::launch_decode(a, c->kv_dtype == RSWA_F32, out_dtype == RSWA_F32,
-                                             (int)grid, need_merge,
-                                             reinterpret_cast<hipStream_t>(stream));
+                                             (int)plan.grid, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, what);
     if (append) {
       c->cur ^= 1;
@@ -671,7 +674,7 @@ rswa_status rswa_cache_decode_plan(const rswa_cache* c, int32_t appending, int32
         rswa::plan_decode(L, c->H, (int64_t)c->num_cus * c->blocks_per_cu, c->grid_max,
                           c->min_rows, c->grid_user, false);
     if (grid_blocks) *grid_blocks = (int32_t)plan.grid;
-    if (launches) *launches = (plan.grid > 0 ? 1 : 0) + (plan.need_merge ? 1 : 0);
+    if (launches) *launches = plan.grid > 0 ? 1 : 0;
     return RSWA_OK;
   } catch (...) {
     return fail(RSWA_E_INTERNAL, "exception in rswa_cache_decode_plan");
