@@ -225,6 +225,23 @@ rswa_status rswa_prefill_bwd(const void* q_dev, const void* k_dev, const void* v
                              int32_t head_dim, int32_t max_seqlen, int32_t prefix_causal,
                              float softmax_scale, void* stream);
 
+/* rswa_prefill_bwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops, harnesses that forbid hipMalloc): the same computation, results and errors,
+ * without the work array. Its work rows live in a device array inside the library (held by each
+ * device the library runs on until the process ends; nothing is allocated or freed by the call),
+ * so total_tokens * num_heads must not exceed 1048576 (RSWA_E_INVALID otherwise, checked before
+ * anything is enqueued). Every call on one device uses that device's array: calls that overlap on
+ * one device (other streams, other threads) race and must be ordered by the caller. */
+rswa_status rswa_prefill_bwd_noalloc(const void* q_dev, const void* k_dev, const void* v_dev,
+                                     const void* out_dev, int32_t out_dtype, const void* dout_dev,
+                                     const float* lse_dev, void* dq_dev, void* dk_dev,
+                                     void* dv_dev, int32_t grad_dtype,
+                                     const int32_t* cu_seqlens_dev,
+                                     const int32_t* prefix_len_dev, const int32_t* window_dev,
+                                     int32_t nseq, int32_t total_tokens, int32_t num_heads,
+                                     int32_t head_dim, int32_t max_seqlen,
+                                     int32_t prefix_causal, float softmax_scale, void* stream);
+
 /* Graph-captured step loop (fused append + decode steps replayed from a HIP graph). Capture
  * `steps` consecutive rswa_decode_step launches of `cache` (no active mask) into a HIP graph:
  * step i of a replay reads q / k / v from slot i of q_slots / k_slots / v_slots (each [steps][B][H]

@@ -29,7 +29,8 @@ EXPORTS = ("rswa_cache_plan", "rswa_cache_bytes", "rswa_cache_create", "rswa_cac
            "rswa_prefill_bwd", "rswa_cache_steps", "rswa_cache_info",
            "rswa_cache_set_decode_split", "rswa_cache_decode_plan", "rswa_cache_destroy",
            "rswa_step_graph_create", "rswa_step_graph_launch", "rswa_step_graph_destroy",
-           "rswa_cache_query", "rswa_prefill_check", "rswa_status_str",
+           "rswa_cache_query", "rswa_prefill_check", "rswa_prefill_bwd_noalloc",
+           "rswa_status_str",
            "rswa_last_error")
 
 
@@ -82,6 +83,8 @@ def _load():
         "rswa_step_graph_launch": (i32, [vp, vp]),
         "rswa_step_graph_destroy": (i32, [vp]),
         "rswa_cache_query": (i32, [vp, ctypes.POINTER(vp), pi64, pi64, pi32, pi32, vp]),
+        "rswa_prefill_bwd_noalloc": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp,
+                                           vp, i32, i32, i32, i32, i32, i32, f32, vp]),
         "rswa_prefill_check": (i32, [vp]),
         "rswa_status_str": (ctypes.c_char_p, [i32]),
         "rswa_last_error": (ctypes.c_char_p, []),
@@ -492,6 +495,32 @@ def rswa_prefill_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: tor
         _dev(prefix_len, "prefix_len", torch.int32, (nseq,)),
         _dev(window, "window", torch.int32, (nseq,)), nseq, total, H, D, max_seqlen,
         int(bool(prefix_causal)), ctypes.c_float(scale), _stream(stream)), "rswa_prefill_bwd")
+    return dq, dk, dv
+
+
+def rswa_prefill_bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                             out: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor,
+                             cu_seqlens: torch.Tensor, prefix_len: torch.Tensor,
+                             window: torch.Tensor, *, dq, dk, dv, prefix_causal: bool = False,
+                             scale: float = 0.0, max_seqlen: int, stream=None):
+    """rswa_prefill_bwd without a work array (the library's device-resident one is used); the
+    gradient tensors must be given. Allocates nothing."""
+    total, H, D = q.shape
+    nseq = prefix_len.numel()
+    shape = (total, H, D)
+    if not (dq.dtype == dk.dtype == dv.dtype):
+        raise TypeError("dq, dk and dv must share one dtype")
+    _check(_lib.rswa_prefill_bwd_noalloc(
+        _dev(q, "q", torch.bfloat16, shape), _dev(k, "k", torch.bfloat16, shape),
+        _dev(v, "v", torch.bfloat16, shape), _dev(out, "out", None, shape),
+        _dtype_code(out.dtype), _dev(dout, "dout", torch.bfloat16, shape),
+        _dev(lse, "lse", torch.float32, (total, H)),
+        _dev(dq, "dq", None, shape), _dev(dk, "dk", None, shape), _dev(dv, "dv", None, shape),
+        _dtype_code(dq.dtype), _dev(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,)),
+        _dev(prefix_len, "prefix_len", torch.int32, (nseq,)),
+        _dev(window, "window", torch.int32, (nseq,)), nseq, total, H, D, int(max_seqlen),
+        int(bool(prefix_causal)), ctypes.c_float(scale), _stream(stream)),
+        "rswa_prefill_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -48,9 +48,36 @@ struct DeviceGuard {
 // the variable's name (which is only a host-side stand-in).
 __device__ __align__(256) int32_t g_prefill_err;
 
+// Work array of rswa_prefill_bwd_noalloc: lse * log2(e) and -delta of every (token, head) row,
+// kNoAllocRows rows each (8 MiB), held by each device the library runs on until the process ends.
+// Host code uses the address hipGetSymbolAddress gives for the current device (kept per device in
+// g_scratch_ptr), never the array's name.
+constexpr int64_t kNoAllocRows = int64_t{1} << 20;
+__device__ __align__(256) float scratch[2 * kNoAllocRows];
+
 constexpr int kMaxDevices = 64;
 int32_t* g_prefill_err_ptr[kMaxDevices] = {};
+float* g_scratch_ptr[kMaxDevices] = {};
 std::mutex g_statics_mutex;
+
+// Device address of the current device's scratch array, or nullptr (reason in *e).
+float* scratch_ptr(hipError_t* e) {
+  int dev = -1;
+  *e = hipGetDevice(&dev);
+  if (*e != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *e = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_statics_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    *e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (*e != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = reinterpret_cast<float*>(ptr);
+  }
+  return g_scratch_ptr[dev];
+}
 
 // Device address of the current device's error word, or nullptr (reason in *e).
 int32_t* prefill_err_word(hipError_t* e) {
@@ -809,6 +836,76 @@ rswa_status rswa_prefill_fwd(const void* q_dev, const void* k_dev, const void* v
                          prefix_causal, softmax_scale, stream, "exception in rswa_prefill_fwd");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Shared body of rswa_prefill_bwd (caller's work array) and rswa_prefill_bwd_noalloc (the
+// library's scratch array).
+rswa_status prefill_backward(const void* q_dev, const void* k_dev, const void* v_dev,
+                             const void* out_dev, int32_t out_dtype, const void* dout_dev,
+                             const float* lse_dev, float* work_dev, void* dq_dev, void* dk_dev,
+                             void* dv_dev, int32_t grad_dtype, const int32_t* cu_seqlens_dev,
+                             const int32_t* prefix_len_dev, const int32_t* window_dev,
+                             int32_t nseq, int32_t total_tokens, int32_t num_heads,
+                             int32_t head_dim, int32_t max_seqlen, int32_t prefix_causal,
+                             float softmax_scale, void* stream) {
+  const float scale = resolve_scale(softmax_scale, head_dim);
+  rswa::BwdArgs a{};
+  a.q = reinterpret_cast<const uint16_t*>(q_dev);
+  a.k = reinterpret_cast<const uint16_t*>(k_dev);
+  a.v = reinterpret_cast<const uint16_t*>(v_dev);
+  a.out = out_dev;
+  a.dout = reinterpret_cast<const uint16_t*>(dout_dev);
+  a.lse = lse_dev;
+  a.work = work_dev;
+  a.rows = (int64_t)total_tokens * num_heads;
+  a.dq = dq_dev;
+  a.dk = dk_dev;
+  a.dv = dv_dev;
+  a.cu_seqlens = cu_seqlens_dev;
+  a.prefix_len = prefix_len_dev;
+  a.window = window_dev;
+  a.nseq = nseq;
+  a.heads = num_heads;
+  a.max_seqlen = max_seqlen;
+  a.prefix_causal = prefix_causal;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = hipSuccess;
+  a.err = prefill_err_word(&e);
+  if (!a.err) return hip_fail(e, "hipGetSymbolAddress(error word)");
+  e = rswa::launch_prefill_bwd(a, out_dtype == RSWA_F32, grad_dtype == RSWA_F32,
+                               reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prefill backward launch");
+  return RSWA_OK;
+}
+
+// Host-checkable arguments of the backward entry points (the work array checked by the caller).
+rswa_status check_backward(const void* q_dev, const void* k_dev, const void* v_dev,
+                           const void* out_dev, int32_t out_dtype, const void* dout_dev,
+                           const float* lse_dev, void* dq_dev, void* dk_dev, void* dv_dev,
+                           int32_t grad_dtype, const int32_t* cu_seqlens_dev,
+                           const int32_t* prefix_len_dev, const int32_t* window_dev,
+                           int32_t nseq, int32_t total_tokens, int32_t num_heads,
+                           int32_t head_dim, int32_t max_seqlen, int32_t prefix_causal,
+                           float softmax_scale) {
+  const rswa_status st = check_prefill(q_dev, k_dev, v_dev, out_dev, out_dtype, cu_seqlens_dev,
+                                       prefix_len_dev, window_dev, nseq, num_heads, head_dim,
+                                       max_seqlen, prefix_causal, softmax_scale);
+  if (st != RSWA_OK) return st;
+  if (!dout_dev || !lse_dev) return fail(RSWA_E_INVALID, "dout/lse pointer is NULL");
+  if (!dq_dev || !dk_dev || !dv_dev) return fail(RSWA_E_INVALID, "dq/dk/dv pointer is NULL");
+  if (grad_dtype != RSWA_BF16 && grad_dtype != RSWA_F32)
+    return fail(RSWA_E_INVALID, "grad_dtype must be RSWA_BF16 or RSWA_F32");
+  if (total_tokens < 0) return fail(RSWA_E_INVALID, "total_tokens must be >= 0");
+  return RSWA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 rswa_status rswa_prefill_bwd(const void* q_dev, const void* k_dev, const void* v_dev,
                              const void* out_dev, int32_t out_dtype, const void* dout_dev,
                              const float* lse_dev, float* work_dev, void* dq_dev, void* dk_dev,
@@ -817,49 +914,51 @@ rswa_status rswa_prefill_bwd(const void* q_dev, const void* k_dev, const void* v
                              int32_t nseq, int32_t total_tokens, int32_t num_heads,
                              int32_t head_dim, int32_t max_seqlen, int32_t prefix_causal,
                              float softmax_scale, void* stream) {
-  const rswa_status st = check_prefill(q_dev, k_dev, v_dev, out_dev, out_dtype, cu_seqlens_dev,
-                                       prefix_len_dev, window_dev, nseq, num_heads, head_dim,
-                                       max_seqlen, prefix_causal, softmax_scale);
+  const rswa_status st = check_backward(q_dev, k_dev, v_dev, out_dev, out_dtype, dout_dev, lse_dev,
+                                        dq_dev, dk_dev, dv_dev, grad_dtype, cu_seqlens_dev,
+                                        prefix_len_dev, window_dev, nseq, total_tokens, num_heads,
+                                        head_dim, max_seqlen, prefix_causal, softmax_scale);
   if (st != RSWA_OK) return st;
-  if (!dout_dev || !lse_dev || !work_dev)
-    return fail(RSWA_E_INVALID, "dout/lse/work pointer is NULL");
-  if (!dq_dev || !dk_dev || !dv_dev) return fail(RSWA_E_INVALID, "dq/dk/dv pointer is NULL");
-  if (grad_dtype != RSWA_BF16 && grad_dtype != RSWA_F32)
-    return fail(RSWA_E_INVALID, "grad_dtype must be RSWA_BF16 or RSWA_F32");
-  if (total_tokens < 0) return fail(RSWA_E_INVALID, "total_tokens must be >= 0");
+  if (!work_dev) return fail(RSWA_E_INVALID, "work pointer is NULL");
   if (max_seqlen == 0 || total_tokens == 0) return RSWA_OK;
   try {
-    const float scale = resolve_scale(softmax_scale, head_dim);
-    rswa::BwdArgs a{};
-    a.q = reinterpret_cast<const uint16_t*>(q_dev);
-    a.k = reinterpret_cast<const uint16_t*>(k_dev);
-    a.v = reinterpret_cast<const uint16_t*>(v_dev);
-    a.out = out_dev;
-    a.dout = reinterpret_cast<const uint16_t*>(dout_dev);
-    a.lse = lse_dev;
-    a.work = work_dev;
-    a.rows = (int64_t)total_tokens * num_heads;
-    a.dq = dq_dev;
-    a.dk = dk_dev;
-    a.dv = dv_dev;
-    a.cu_seqlens = cu_seqlens_dev;
-    a.prefix_len = prefix_len_dev;
-    a.window = window_dev;
-    a.nseq = nseq;
-    a.heads = num_heads;
-    a.max_seqlen = max_seqlen;
-    a.prefix_causal = prefix_causal;
-    a.scale = scale;
-    a.scale_log2 = scale * 1.4426950408889634f;
-    hipError_t e = hipSuccess;
-    a.err = prefill_err_word(&e);
-    if (!a.err) return hip_fail(e, "hipGetSymbolAddress(error word)");
-    e = rswa::launch_prefill_bwd(a, out_dtype == RSWA_F32, grad_dtype == RSWA_F32,
-                                 reinterpret_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "prefill backward launch");
-    return RSWA_OK;
+    return prefill_backward(q_dev, k_dev, v_dev, out_dev, out_dtype, dout_dev, lse_dev, work_dev,
+                            dq_dev, dk_dev, dv_dev, grad_dtype, cu_seqlens_dev, prefix_len_dev,
+                            window_dev, nseq, total_tokens, num_heads, head_dim, max_seqlen,
+                            prefix_causal, softmax_scale, stream);
   } catch (...) {
     return fail(RSWA_E_INTERNAL, "exception in rswa_prefill_bwd");
+  }
+}
+
+rswa_status rswa_prefill_bwd_noalloc(const void* q_dev, const void* k_dev, const void* v_dev,
+                                     const void* out_dev, int32_t out_dtype, const void* dout_dev,
+                                     const float* lse_dev, void* dq_dev, void* dk_dev,
+                                     void* dv_dev, int32_t grad_dtype,
+                                     const int32_t* cu_seqlens_dev,
+                                     const int32_t* prefix_len_dev, const int32_t* window_dev,
+                                     int32_t nseq, int32_t total_tokens, int32_t num_heads,
+                                     int32_t head_dim, int32_t max_seqlen,
+                                     int32_t prefix_causal, float softmax_scale, void* stream) {
+  const rswa_status st = check_backward(q_dev, k_dev, v_dev, out_dev, out_dtype, dout_dev, lse_dev,
+                                        dq_dev, dk_dev, dv_dev, grad_dtype, cu_seqlens_dev,
+                                        prefix_len_dev, window_dev, nseq, total_tokens, num_heads,
+                                        head_dim, max_seqlen, prefix_causal, softmax_scale);
+  if (st != RSWA_OK) return st;
+  if ((int64_t)total_tokens * num_heads > kNoAllocRows)
+    return fail(RSWA_E_INVALID, "total_tokens * num_heads exceeds the scratch array of "
+                                "rswa_prefill_bwd_noalloc (1048576 rows)");
+  if (max_seqlen == 0 || total_tokens == 0) return RSWA_OK;
+  try {
+    hipError_t e = hipSuccess;
+    float* work = scratch_ptr(&e);
+    if (!work) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    return prefill_backward(q_dev, k_dev, v_dev, out_dev, out_dtype, dout_dev, lse_dev, work,
+                            dq_dev, dk_dev, dv_dev, grad_dtype, cu_seqlens_dev, prefix_len_dev,
+                            window_dev, nseq, total_tokens, num_heads, head_dim, max_seqlen,
+                            prefix_causal, softmax_scale, stream);
+  } catch (...) {
+    return fail(RSWA_E_INTERNAL, "exception in rswa_prefill_bwd_noalloc");
   }
 }
 
