@@ -34,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "R-SWA decode tok/s + HBM GB/s vs T (1 GPU); masked prefill TFLOP/s"
+LEGS = ("growth", "batched", "single", "ragged", "shared", "graph", "prefill", "backward", "cpu")
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 H, D = 16, 128
@@ -72,6 +73,9 @@ def parse():
                     default="multipage")
     ap.add_argument("--headline-only", action="store_true",
                     help="only the headline decode (for counter runs of its kernel)")
+    ap.add_argument("--legs", default="all",
+                    help="comma list of the other measurements to run: growth, batched, single, "
+                         "ragged, shared, graph, prefill, backward, cpu (default all)")
     ap.add_argument("--mode", choices=["rswa", "full"], default="rswa")
     ap.add_argument("--chunk", type=int, default=0, help="decode rows per split (0 = automatic)")
     ap.add_argument("--grid", type=int, default=0, help="decode workgroups (0 = automatic)")
@@ -715,7 +719,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     res = dict(metric=METRIC, n_gpus=1, higher_is_better=True, scaling="weak", vs_baseline=None,
                data="synthetic")
-    legs_on = not args.headline_only
+    wanted = set(LEGS if args.legs == "all" else args.legs.split(","))
+    unknown = wanted - set(LEGS)
+    if unknown:
+        raise SystemExit(f"unknown legs: {sorted(unknown)}")
+    on = {leg: (not args.headline_only) and leg in wanted for leg in LEGS}
     wl = None
     if not args.no_decode:
         t0 = time.perf_counter()
@@ -772,44 +780,45 @@ def main():
         keep = np.linspace(0, len(lat) - 1, min(len(lat), 40)).round().astype(int)
         res["latency_vs_t"] = [[int(lat[i][0]), round(float(lat[i][1]), 3)] for i in keep]
         res["flatness"] = flatness(lat, n, int(wl.T))
-        if legs_on and not args.no_growth and args.workload == "multipage" and not full:
+        if on["growth"] and not args.no_growth and args.workload == "multipage" and not full:
             res["growth"] = growth_curve(args, wl, lat)
     if args.copy_calibration:
         res["copy_calibration"] = copy_calibration()
         log(f"[bench] 1 GiB copy: {res['copy_calibration']['gbs']:.0f} GB/s")
-    if legs_on and not args.no_decode:
+    if on["batched"] and not args.no_decode:
         res["batched_mall_resident"] = b = steady_leg(args, "batched", 2000, 100)
         b["note"] = ("effective GB/s: the 211 MB step working set fits the 256 MB Infinity Cache, "
                      "so rows are partly served from it rather than from HBM")
         log(f"[bench] batched (MALL-resident): {b['us_per_step']:.2f} us/step, "
             f"{b['step_gbs']:.0f} GB/s effective")
+    if on["single"] and not args.no_decode:
         res["single_fp32"] = s1 = steady_leg(args, "single", 64, 64)
         s1["note"] = "latency-bound (6.6 MB per step, cache-resident); GB/s effective"
         log(f"[bench] single-page fp32 B=1: {s1['us_per_step']:.2f} us/step")
-    if legs_on and not args.no_decode and not args.no_ragged:
+    if on["ragged"] and not args.no_decode and not args.no_ragged:
         res["ragged"] = ragged_decode(args)
         log(f"[bench] ragged: {res['ragged']['us_per_step']:.1f} us/step, "
             f"{res['ragged']['step_gbs']:.0f} GB/s")
-    if legs_on and not args.no_decode and not args.no_shared:
+    if on["shared"] and not args.no_decode and not args.no_shared:
         res["shared_documents"] = sd = shared_documents(args)
         log(f"[bench] shared documents: paged {sd['paged']['us_per_step']:.1f} us/step, "
             f"copied {sd['copied']['us_per_step']:.1f} us/step ({sd['speedup']:.2f}x)")
-    if legs_on and not args.no_decode and not args.no_graph:
+    if on["graph"] and not args.no_decode and not args.no_graph:
         res["graph_loop"] = gl = graph_loop(args)
         for k2, r2 in gl.items():
             log(f"[bench] graph loop {k2}: eager {r2['eager_us_per_step']:.2f} us/step, "
                 f"graph {r2['graph_us_per_step']:.2f} us/step")
-    if legs_on and not args.no_prefill:
+    if on["prefill"] and not args.no_prefill:
         p = run_prefill(args)
         if p is not None:
             res["prefill"] = p
             log(f"[bench] prefill: {p['ms']:.3f} ms, {p['tflops']:.1f} TFLOP/s")
-    if legs_on and not args.no_backward:
+    if on["backward"] and not args.no_backward:
         bw = run_backward(args)
         res["backward"] = bw
         log(f"[bench] training pass: forward {bw['fwd_ms']:.3f} ms, backward {bw['bwd_ms']:.3f} ms "
             f"({bw['bwd_tflops']:.1f} TFLOP/s), fwd+bwd {bw['train_tflops']:.1f} TFLOP/s")
-    if wl is not None and legs_on and not args.no_cpu_baseline:
+    if wl is not None and on["cpu"] and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(res))
 

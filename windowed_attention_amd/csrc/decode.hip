@@ -67,12 +67,13 @@ struct SeqState {
 
 __device__ __forceinline__ SeqState seq_state(const DecodeArgs& a, int b) {
   SeqState st;
-  const bool act = !a.active || a.active[b];
-  st.t = a.steps_in[b];
-  const int cap = a.meta.cap[b];
+  const bool uni = a.uni_t >= 0;
+  const bool act = uni || !a.active || a.active[b];
+  st.t = uni ? a.uni_t : a.steps_in[b];
+  const int cap = uni ? a.uni_cap : a.meta.cap[b];
   st.app = act && a.k_new != nullptr && (!a.full_causal || st.t < cap);
   const int t_after = st.app ? st.t + 1 : st.t;
-  st.L = act ? a.meta.prefix_len[b] + min(t_after, cap) : 0;
+  st.L = act ? (uni ? a.uni_m : a.meta.prefix_len[b]) + min(t_after, cap) : 0;
   return st;
 }
 
@@ -95,13 +96,14 @@ __device__ void build_work_table(const DecodeArgs& a, int* s_len, int* s_new, in
       s_len[b] = st.L;
       rows = (int64_t)a.heads * st.L;
       int rnew = -1;
-      const int m = a.meta.prefix_len[b];
-      if (st.app) rnew = a.full_causal ? m + st.t : m + st.t % a.meta.cap[b];
+      const bool uni = a.uni_t >= 0;
+      const int m = uni ? a.uni_m : a.meta.prefix_len[b];
+      const int cap = uni ? a.uni_cap : a.meta.cap[b];
+      if (st.app) rnew = a.full_causal ? m + st.t : m + st.t % cap;
       s_new[b] = rnew;
       if (blockIdx.x == 0) {
         if (a.steps_out) a.steps_out[b] = st.app ? st.t + 1 : st.t;
-        if (a.k_new && a.full_causal && (!a.active || a.active[b]) && st.t >= a.meta.cap[b])
-          *a.meta.err = 1;
+        if (a.k_new && a.full_causal && (!a.active || a.active[b]) && st.t >= cap) *a.meta.err = 1;
       }
     }
     int64_t x = rows;
@@ -270,6 +272,18 @@ __device__ __forceinline__ void merge_range(const DecodeArgs& a, int64_t s, int6
   __syncthreads();
 }
 
+// The four workgroups that share a CU do not progress evenly: the oldest waves win the issue
+// arbitration, so some pieces finish early and the rest then run with a quarter of the CU's waves
+// in flight. A wave lowers its issue priority as its piece progresses (done of total rows), which
+// hands issue slots to the pieces that are behind.
+__device__ __forceinline__ void yield_by_progress(int64_t done, int64_t total) {
+  const int64_t lvl = (4 * done) / total;
+  if (lvl <= 0) asm volatile("s_setprio 3");
+  else if (lvl == 1) asm volatile("s_setprio 2");
+  else if (lvl == 2) asm volatile("s_setprio 1");
+  else asm volatile("s_setprio 0");
+}
+
 // Stream rows [r0, r1) of range (b, h); finish with the group merge through LDS, then either the
 // output (the range is not split) or a partial in workspace slot `slot`, published at device
 // scope. Returns (in every thread) whether this piece is the last of the range's np pieces to
@@ -277,20 +291,23 @@ __device__ __forceinline__ void merge_range(const DecodeArgs& a, int64_t s, int6
 template <typename KV, typename OUT, int U>
 __device__ __forceinline__ bool decode_range(const DecodeArgs& a, int b, int h, int r0, int r1,
                                              int rnew, bool direct, int64_t slot, int np,
-                                             float* s_m, float* s_l, float* s_acc, int* s_flag) {
+                                             float* s_m, float* s_l, float* s_acc, int* s_flag,
+                                             int64_t done0, int64_t piece) {
   constexpr int VEC = Lanes<KV>::VEC, GL = Lanes<KV>::GL, G = kWave / GL, NG = kWaves * G;
   constexpr int STEP = kWaves * G * U;
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // tile decisions are scalar
   const int g = lane / GL, li = lane % GL;
   const int H = a.heads;
-  const int64_t R = a.meta.rows[b];
-  const int m = a.meta.prefix_len[b];
+  const bool uni = a.uni_t >= 0;
+  const int64_t R = uni ? a.uni_rows : a.meta.rows[b];
+  const int m = uni ? a.uni_m : a.meta.prefix_len[b];
   // Cache row r lives at Kh + r * D; with a paged prefix the storage starts at row m, and rows
   // r < m are pool rows found through the page table (one 4-byte lookup per row and group).
   const bool paged = a.meta.table != nullptr;
   const int64_t shift = paged ? m : 0;
-  KV* seq = reinterpret_cast<KV*>(a.storage) + a.meta.seq_off[b];
+  KV* seq = reinterpret_cast<KV*>(a.storage) +
+            (uni ? (int64_t)b * 2 * H * R * kHeadDim : a.meta.seq_off[b]);
   KV* Kh = seq + ((int64_t)h * R - shift) * kHeadDim;
   KV* Vh = seq + ((int64_t)(H + h) * R - shift) * kHeadDim;
   KV* Kp = Kh + li * VEC;
@@ -422,6 +439,7 @@ __device__ __forceinline__ bool decode_range(const DecodeArgs& a, int b, int h, 
       reduce(rb, kb, vb);
       rb += STEP;
       if (rb > last) break;
+      yield_by_progress(done0 + (rb - r0), piece);
     }
   }
 
@@ -491,12 +509,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const int b = s / H, h = s - (s / H) * H;
     if (b >= a.batch || s_len[b] == 0) return;
     decode_range<KV, OUT, U>(a, b, h, 0, s_len[b], s_new[b], true, 0, 1, s_m, s_l, s_acc,
-                             &s_flag);
+                             &s_flag, 0, s_len[b]);
     return;
   }
 
   const int64_t W = piece_rows(a, total);
-  int64_t pos = (int64_t)blockIdx.x * W;
+  const int64_t pos0 = (int64_t)blockIdx.x * W;
+  int64_t pos = pos0;
   const int64_t end = min(pos + W, total);
   while (pos < end) {
     int lo = 0, hi = a.batch - 1;  // last b with s_cum[b] <= pos
@@ -515,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const int64_t f = A / W, l = (A + L - 1) / W;  // pieces that hold rows of this range
     const bool direct = f == l;
     if (decode_range<KV, OUT, U>(a, b, h, r0, r1, s_new[b], direct, (int64_t)blockIdx.x + s,
-                                 (int)(l - f + 1), s_m, s_l, s_acc, &s_flag))
+                                 (int)(l - f + 1), s_m, s_l, s_acc, &s_flag, pos - pos0, W))
       merge_range<OUT>(a, s, f, (int)(l - f + 1), s_w, s_lw, s_red);
     pos += r1 - r0;
   }

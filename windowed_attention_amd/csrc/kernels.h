@@ -56,6 +56,13 @@ struct DecodeArgs {
   int32_t aligned;          // 1: one workgroup per (b, h) key range; 0: balanced stream-K ranges
   int32_t min_rows;         // stream-K: fewest rows a workgroup takes
   float scale_log2;         // softmax scale * log2(e)
+  // Host-known plan: when every sequence has the same m, capacity and step count and no active
+  // mask is involved, the host passes them (uni_t >= 0) and the kernel reads no per-sequence
+  // metadata; uni_t < 0: everything comes from the device arrays (graph replays, masks, ragged).
+  int32_t uni_t;            // t_b before this launch
+  int32_t uni_m;            // m_b
+  int32_t uni_cap;          // cap_b
+  int32_t uni_rows;         // R_b (storage rows per head)
 };
 
 struct PrefixCopyArgs {
