@@ -84,7 +84,7 @@ def parse():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-shared", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the headline decode")
     ap.add_argument("--kernel-events", action="store_true",
                     help="diagnostic: record HIP events around every launch (adds GPU time)")
     ap.add_argument("--unfused", action="store_true",
@@ -785,25 +785,25 @@ def main():
     if args.copy_calibration:
         res["copy_calibration"] = copy_calibration()
         log(f"[bench] 1 GiB copy: {res['copy_calibration']['gbs']:.0f} GB/s")
-    if on["batched"] and not args.no_decode:
+    if on["batched"]:
         res["batched_mall_resident"] = b = steady_leg(args, "batched", 2000, 100)
         b["note"] = ("effective GB/s: the 211 MB step working set fits the 256 MB Infinity Cache, "
                      "so rows are partly served from it rather than from HBM")
         log(f"[bench] batched (MALL-resident): {b['us_per_step']:.2f} us/step, "
             f"{b['step_gbs']:.0f} GB/s effective")
-    if on["single"] and not args.no_decode:
+    if on["single"]:
         res["single_fp32"] = s1 = steady_leg(args, "single", 64, 64)
         s1["note"] = "latency-bound (6.6 MB per step, cache-resident); GB/s effective"
         log(f"[bench] single-page fp32 B=1: {s1['us_per_step']:.2f} us/step")
-    if on["ragged"] and not args.no_decode and not args.no_ragged:
+    if on["ragged"] and not args.no_ragged:
         res["ragged"] = ragged_decode(args)
         log(f"[bench] ragged: {res['ragged']['us_per_step']:.1f} us/step, "
             f"{res['ragged']['step_gbs']:.0f} GB/s")
-    if on["shared"] and not args.no_decode and not args.no_shared:
+    if on["shared"] and not args.no_shared:
         res["shared_documents"] = sd = shared_documents(args)
         log(f"[bench] shared documents: paged {sd['paged']['us_per_step']:.1f} us/step, "
             f"copied {sd['copied']['us_per_step']:.1f} us/step ({sd['speedup']:.2f}x)")
-    if on["graph"] and not args.no_decode and not args.no_graph:
+    if on["graph"] and not args.no_graph:
         res["graph_loop"] = gl = graph_loop(args)
         for k2, r2 in gl.items():
             log(f"[bench] graph loop {k2}: eager {r2['eager_us_per_step']:.2f} us/step, "
