@@ -123,22 +123,26 @@ __device__ __forceinline__ uint32_t lds_addr(const void* lds) {
   return __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds);
 }
+// The DMA takes its LDS address from M0; a scalar write of M0 needs one wait state before an LDS
+// DMA reads it (the `s_nop 0`, which the compiler would insert between instructions it knows).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved; it is set right here
 __device__ __forceinline__ void dma16(const void* g, void* lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr(lds))
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
+               "s"(lds_addr(lds))
                : "memory", "m0");
 }
 // The same copy from a wave-uniform base address (SGPR pair) plus a per-lane 32-bit byte offset:
 // the address arithmetic of a tile then runs on the scalar unit.
 // `lds` is an LDS byte address (lds_addr of the destination), wave-uniform.
 __device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
-               "s"(lds)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off),
+               "s"(base), "s"(lds)
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* g, void* lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_addr(lds))
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g),
+               "s"(lds_addr(lds))
                : "memory", "m0");
 }
 #pragma clang diagnostic pop

@@ -38,11 +38,15 @@ constexpr float kLog2e = 1.4426950408889634f;
 // v_mfma_f32_32x32x16_bf16 with its accumulator in VGPRs (the vector ALU reads S and dP) and its B
 // operand in AGPRs. Written as inline assembly because the compiler gives every MFMA of a kernel
 // that uses AGPRs an AGPR accumulator and then copies S and dP out register by register. The
-// hazards the compiler cannot see are covered by construction: a chain accumulates in place (same
-// opcode, exact overlap: no wait states); the vector ALU reads the result only after the other
-// product half of the step (16 MFMAs, far beyond the 11 wait states an 8-pass result needs); a
-// start value written by the vector ALU gets two wait states (mfma_vacc_first); LDS-loaded operands
-// are covered by the compiler's lgkmcnt waits on the asm inputs.
+// compiler does not see these as MFMAs, so the wait states their hazards need are provided here:
+// a chain accumulates in place (same opcode, exact overlap: none needed); a start value written by
+// the vector ALU gets two before the first MFMA reads it (mfma_vacc_first); gfx950 needs 12 wait
+// states between an MFMA and any other instruction that reads or writes its result, which the
+// 16 MFMAs of the step's other product half provide where the results stay in place, and
+// mfma_vacc_last2 (the last MFMAs of the S and dP chains issued together, then 12 wait states)
+// where the compiler moves them to other registers right away. LDS-loaded operands are covered
+// by the compiler's lgkmcnt waits on the asm inputs. A test checks every distance on the
+// compiled assembly.
 __device__ __forceinline__ void mfma_vacc_zero(floatx16& d, const u32x4& a, const u32x4& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
 }
@@ -50,7 +54,18 @@ __device__ __forceinline__ void mfma_vacc(floatx16& d, const u32x4& a, const u32
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
 __device__ __forceinline__ void mfma_vacc_first(floatx16& d, const u32x4& a, const u32x4& b) {
-  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+struct Guarded { static constexpr bool value = true; };
+struct Unguarded { static constexpr bool value = false; };
+__device__ __forceinline__ void mfma_vacc_last2(floatx16& d0, const u32x4& a0, const u32x4& b0,
+                                                floatx16& d1, const u32x4& a1, const u32x4& b1) {
+  asm volatile(
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %4, %5, %1\n\t"
+      "s_nop 7\n\ts_nop 3"
+      : "+v"(d0), "+v"(d1)
+      : "v"(a0), "a"(b0), "v"(a1), "a"(b1));
 }
 
 // ------------------------------------------------------------------------------------------
@@ -380,8 +395,12 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
 
   // One step: S and dP - delta of the next block (rows rn of tile buffers qn / gn / dn_) into
   // sn / dn under P, dS of the current block (scores sc, dc; rows rc of qc / gc / lc), then
-  // dV^T += dO^T P and dK^T += Q^T dS for the current block.
-  auto step = [&](floatx16& sc, floatx16& dc, floatx16& sn, floatx16& dn, const uint16_t* qn,
+  // dV^T += dO^T P and dK^T += Q^T dS for the current block. With the Guarded tag, the last S and
+  // dP MFMAs are followed by the wait states their results need: the compiler moves sn / dn to
+  // other registers right after them in the single-tile loop and at the unrolled loop's back
+  // edge. Elsewhere they stay in place until the next step reads them, 16 MFMAs later.
+  auto step = [&](auto guard, floatx16& sc, floatx16& dc, floatx16& sn, floatx16& dn,
+                  const uint16_t* qn,
                   const uint16_t* gn, const float* dn_, int rn, const uint16_t* qc,
                   const uint16_t* gc, const float* lc, int rc) {
     float4 l4[4], d4[4];
@@ -411,9 +430,11 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
       if (i == 0) {
         mfma_vacc_zero(sn, fq[0], kf[0]);
         mfma_vacc_first(dn, fg[0], vf[0]);
-      } else {
+      } else if (i < 7 || !decltype(guard)::value) {
         mfma_vacc(sn, fq[i % 3], kf[i]);
         mfma_vacc(dn, fg[i % 3], vf[i]);
+      } else {
+        mfma_vacc_last2(sn, fq[i % 3], kf[i], dn, fg[i % 3], vf[i]);
       }
       if (i + 3 < 8) {
         fq[i % 3] = swz_ld_a(qn, sl_, rn, i + 3);
@@ -493,12 +514,16 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
       const int b = u, bn = (u + 1) & 3;
       const uint16_t* q_j = sQ + b * Q_TILE;
       const uint16_t* g_j = sG + b * Q_TILE;
-      step(s0, d0, s1, d1, q_j, g_j, sD + b * BMQ, 32, q_j, g_j, sL + b * BMQ, 0);
+      step(Unguarded{}, s0, d0, s1, d1, q_j, g_j, sD + b * BMQ, 32, q_j, g_j, sL + b * BMQ, 0);
       mask_block(s1, 2 * (j + u) + 1);
       dma_wait_barrier<kKvPieces>();
       issue_to(j + u + 3, (u + 3) & 3);
-      step(s1, d1, s0, d0, sQ + bn * Q_TILE, sG + bn * Q_TILE, sD + bn * BMQ, 0, q_j, g_j,
-           sL + b * BMQ, 32);
+      if (u < 3)
+        step(Unguarded{}, s1, d1, s0, d0, sQ + bn * Q_TILE, sG + bn * Q_TILE, sD + bn * BMQ, 0,
+             q_j, g_j, sL + b * BMQ, 32);
+      else  // the loop's last step: its results cross the loop's back edge
+        step(Guarded{}, s1, d1, s0, d0, sQ + bn * Q_TILE, sG + bn * Q_TILE, sD + bn * BMQ, 0, q_j,
+             g_j, sL + b * BMQ, 32);
       mask_block(s0, 2 * (j + u) + 2);
     }
   }
@@ -506,7 +531,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
     const int b = j & 3, bn = (j + 1) & 3;
     const uint16_t* q_j = sQ + b * Q_TILE;
     const uint16_t* g_j = sG + b * Q_TILE;
-    step(s0, d0, s1, d1, q_j, g_j, sD + b * BMQ, 32, q_j, g_j, sL + b * BMQ, 0);
+    step(Guarded{}, s0, d0, s1, d1, q_j, g_j, sD + b * BMQ, 32, q_j, g_j, sL + b * BMQ, 0);
     mask_block(s1, 2 * j + 1);
     // tile j + 1 must have landed (tile j + 2's copy may still be in flight); past this barrier
     // every wave is done with tile j - 1, whose buffers take tile j + 3
@@ -515,8 +540,8 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
     else
       dma_wait_barrier<0>();
     if (j + 3 < ntiles) issue(j + 3);
-    step(s1, d1, s0, d0, sQ + bn * Q_TILE, sG + bn * Q_TILE, sD + bn * BMQ, 0, q_j, g_j,
-         sL + b * BMQ, 32);
+    step(Guarded{}, s1, d1, s0, d0, sQ + bn * Q_TILE, sG + bn * Q_TILE, sD + bn * BMQ, 0, q_j,
+         g_j, sL + b * BMQ, 32);
     if (j + 1 < ntiles) mask_block(s0, 2 * j + 2);
   }
 
