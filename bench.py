@@ -500,7 +500,7 @@ def run_backward(args):
     S = int(pw.cu_seqlens[-1])
     out = torch.empty((S, H, D), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((S, H), dtype=torch.float32, device="cuda")
-    work = torch.empty((2, S, H), dtype=torch.float32, device="cuda")
+    work = torch.empty((2, H, S), dtype=torch.float32, device="cuda")
     grads = [torch.empty((S, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
 
     def fwd():

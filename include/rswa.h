@@ -207,7 +207,7 @@ rswa_status rswa_prefill_fwd(const void* q_dev, const void* k_dev, const void* v
  * q/k/v_dev, dout_dev: [total][H][D] bf16; out_dev: the forward output [total][H][D] of out_dtype;
  * lse_dev: float32 [total][H] from rswa_prefill_fwd with the same arguments.
  * work_dev: caller-owned float32 work array of 2 * total_tokens * H values, overwritten with
- * [0][token][h] = lse * log2(e) and [1][token][h] = -delta (delta = the row sum of dO * O).
+ * [0][h][token] = lse * log2(e) and [1][h][token] = -delta (delta = the row sum of dO * O).
  * dq/dk/dv_dev: [total][H][D] of grad_dtype, overwritten on every row of every segment (rows
  * beyond cu_seqlens[nseq] are not touched). total_tokens (host) = rows of these arrays, at least
  * cu_seqlens[nseq]; the work array covers all of them.

@@ -178,9 +178,10 @@ def test_backward_packed_training_row_sampled(wa):
 
 
 def test_work_array_holds_log2_lse_and_negated_delta(wa):
-    """The work array the backward fills: [0] = lse * log2(e) and [1] = -delta, with delta the
-    row sum of dO * O over the forward output as passed, checked against that definition on the
-    host (float64 sums of the same bf16 values; the kernel sums 128 products in float32)."""
+    """The work array the backward fills, head-major: [0][h][token] = lse * log2(e) and
+    [1][h][token] = -delta, with delta the row sum of dO * O over the forward output as passed,
+    checked against that definition on the host (float64 sums of the same bf16 values; the kernel
+    sums 128 products in float32)."""
     pw = W.make_prefill("work", 4, [300, 90], [100, 0], [32, 16], seed=63)
     g = W.make_output_grad(pw, seed=63)
     q, k, v = upload(pw.q, "bf16"), upload(pw.k, "bf16"), upload(pw.v, "bf16")
@@ -190,14 +191,14 @@ def test_work_array_holds_log2_lse_and_negated_delta(wa):
     n = torch.tensor(pw.window, dtype=torch.int32, device="cuda")
     out, lse = wa.rswa_prefill_fwd(q, k, v, cu, m, n, out_dtype=torch.bfloat16)
     total, heads, _ = q.shape
-    work = torch.full((2, total, heads), float("nan"), dtype=torch.float32, device="cuda")
+    work = torch.full((2, heads, total), float("nan"), dtype=torch.float32, device="cuda")
     wa.rswa_prefill_bwd(q, k, v, out, dout, lse, cu, m, n, work=work)
     torch.cuda.synchronize()
     o = out.double().cpu().numpy()
     d = dout.double().cpu().numpy()
     delta = (o * d).sum(-1)
     scale = (np.abs(o) * np.abs(d)).sum(-1).max()
-    w = work.double().cpu().numpy()
+    w = work.double().cpu().numpy().transpose(0, 2, 1)  # [2][token][h]
     assert np.abs(w[1] + delta).max() <= 1e-5 * scale
     lse64 = lse.double().cpu().numpy()
     np.testing.assert_allclose(w[0], lse64 * np.log2(np.e), rtol=1e-6, atol=1e-6)

@@ -474,7 +474,7 @@ def rswa_prefill_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: tor
                      prefix_causal: bool = False, scale: float = 0.0,
                      max_seqlen: int | None = None, stream=None):
     """Gradients (dq, dk, dv) of the R-SWA-masked prefill; dout bf16 [total][H][D], out and lse
-    from rswa_prefill_fwd. `work` ([2][total][H] float32) is a work array, allocated if absent."""
+    from rswa_prefill_fwd. `work` ([2][H][total] float32) is a work array, allocated if absent."""
     total, H, D = q.shape
     nseq = prefix_len.numel()
     max_seqlen = _max_seqlen(cu_seqlens, max_seqlen)
@@ -482,14 +482,14 @@ def rswa_prefill_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: tor
     mk = lambda t: torch.empty(shape, dtype=grad_dtype, device=q.device) if t is None else t
     dq, dk, dv = mk(dq), mk(dk), mk(dv)
     if work is None:
-        work = torch.empty((2, total, H), dtype=torch.float32, device=q.device)
+        work = torch.empty((2, H, total), dtype=torch.float32, device=q.device)
     if not (dq.dtype == dk.dtype == dv.dtype):
         raise TypeError("dq, dk and dv must share one dtype")
     _check(_lib.rswa_prefill_bwd(
         _dev(q, "q", torch.bfloat16, shape), _dev(k, "k", torch.bfloat16, shape),
         _dev(v, "v", torch.bfloat16, shape), _dev(out, "out", None, shape),
         _dtype_code(out.dtype), _dev(dout, "dout", torch.bfloat16, shape),
-        _dev(lse, "lse", torch.float32, (total, H)), _dev(work, "work", torch.float32, (2, total, H)),
+        _dev(lse, "lse", torch.float32, (total, H)), _dev(work, "work", torch.float32, (2, H, total)),
         _dev(dq, "dq", None, shape), _dev(dk, "dk", None, shape), _dev(dv, "dv", None, shape),
         _dtype_code(dq.dtype), _dev(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,)),
         _dev(prefix_len, "prefix_len", torch.int32, (nseq,)),

@@ -99,7 +99,7 @@ struct BwdArgs {
   const void* out;          // [total][H][D] forward output (bf16 or float32)
   const uint16_t* dout;     // [total][H][D] bf16 gradient of the output
   const float* lse;         // [total][H] natural log-sum-exp from the forward
-  float* work;              // [2][total][H] written: lse * log2(e), then rowsum(dout * out)
+  float* work;              // [2][H][total] written: lse * log2(e), then -rowsum(dout * out)
   int64_t rows;             // total * H
   void* dq;                 // [total][H][D] gradients (bf16 or float32)
   void* dk;

@@ -87,26 +87,37 @@ __device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8]) {
   }
 }
 
-// Also converts the forward's natural-log lse to the log2 domain the other kernels use:
-// work[0][row] = lse * log2(e), work[1][row] = -delta (the dP chains start from it).
+// Also converts the forward's natural-log lse to the log2 domain the other kernels use. The work
+// array is head-major, so that a tile of consecutive queries of one head reads its lse and delta
+// from one contiguous run: work[0][h][token] = lse * log2(e), work[1][h][token] = -delta (the dP
+// chains start from it). A workgroup takes 32 consecutive tokens of one head (two 16-token passes
+// of its 16 lane groups), so its work values fill whole 128-byte lines; heads run fastest across
+// workgroups, so the workgroups in flight read one contiguous run of O and dO rows.
 template <typename OT>
 __global__ __launch_bounds__(256) void delta_kernel(const OT* __restrict__ out,
                                                     const uint16_t* __restrict__ dout,
                                                     const float* __restrict__ lse,
-                                                    float* __restrict__ work, int64_t rows) {
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+                                                    float* __restrict__ work, int64_t total,
+                                                    int heads) {
+  const int h = (int)(blockIdx.x % (unsigned)heads);
+  const int64_t t0 = (int64_t)(blockIdx.x / (unsigned)heads) * 32;
+  const int64_t rows = total * heads;
   const int c = threadIdx.x & 15;
-  const int64_t rr = row < rows ? row : rows - 1;
-  float o[8], g[8];
-  load8(out + rr * kHeadDim + c * 8, o);
-  load8(dout + rr * kHeadDim + c * 8, g);
-  float acc = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc = fmaf(o[i], g[i], acc);
-  acc = row16_sum(acc);
-  if (row < rows) {
-    if (c == 0) work[rows + row] = -acc;
-    if (c == 1) work[row] = lse[row] * kLog2e;
+  for (int u = 0; u < 2; ++u) {
+    const int64_t t = t0 + 16 * u + (threadIdx.x >> 4);
+    const int64_t row = (t < total ? t : total - 1) * heads + h;
+    float o[8], g[8];
+    load8(out + row * kHeadDim + c * 8, o);
+    load8(dout + row * kHeadDim + c * 8, g);
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fmaf(o[i], g[i], acc);
+    acc = row16_sum(acc);
+    if (t < total) {
+      if (c == 0) work[rows + h * total + t] = -acc;
+      if (c == 1) work[h * total + t] = lse[row] * kLog2e;
+    }
   }
 }
 
@@ -131,9 +142,9 @@ constexpr int kKvPieces = 2 * kGroupsPerWave;         // 16-byte DMA loads per w
 __device__ __forceinline__ void dma_qtile(uint16_t* sq, uint16_t* sg, float* sl, float* sd,
                                           const uint16_t* qbase, const uint16_t* gbase,
                                           const float* lse, const float* dlt, int64_t rs,
-                                          int heads, int p0, int pmax, int wave, int lane) {
-  if (wave == 0) dma4(lse + (int64_t)min(p0 + lane, pmax) * heads, sl);
-  if (wave == 1) dma4(dlt + (int64_t)min(p0 + lane, pmax) * heads, sd);
+                                          int p0, int pmax, int wave, int lane) {
+  if (wave == 0) dma4(lse + min(p0 + lane, pmax), sl);
+  if (wave == 1) dma4(dlt + min(p0 + lane, pmax), sd);
 #pragma unroll
   for (int u = 0; u < kGroupsPerWave; ++u) {
     const int grp = wave * kGroupsPerWave + u;
@@ -157,11 +168,31 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
   __shared__ __attribute__((aligned(16))) float sL[2 * kKvWaves * BMQ];
   __shared__ __attribute__((aligned(16))) float sD[2 * kKvWaves * BMQ];
 
-  // key blocks outermost across heads: the prefix blocks (long query loops) start first
+  // Block order. Workgroup i runs on XCD i % 8. When the heads split evenly over the 8 XCDs,
+  // each XCD takes heads / 8 heads of a sequence: first the key blocks that hold prefix keys
+  // (their query loops are the long ones), one head after the other, so the blocks running
+  // together on an XCD stream the same head's Q / dO tiles through its L2; then the window blocks.
+  // Otherwise: key blocks outermost across heads, so the prefix blocks still start first.
   const int idx = blockIdx.x;
-  const int h = idx % a.heads;
-  const int kblk = (idx / a.heads) % nkb;
-  const int s = idx / (a.heads * nkb);
+  int h, kblk, s;
+  if (a.heads % 8 == 0) {
+    const int per = a.heads * nkb;
+    s = idx / per;
+    const int i = idx - s * per, x = i % 8, j = i / 8, hg = a.heads / 8;
+    const int P = min(nkb, max(0, (a.prefix_len[s] + BNK - 1) / BNK));
+    if (j < hg * P) {
+      h = x * hg + j / P;
+      kblk = j % P;
+    } else {
+      const int w = nkb - P, jj = j - hg * P;
+      h = x * hg + jj / w;
+      kblk = P + jj % w;
+    }
+  } else {
+    h = idx % a.heads;
+    kblk = (idx / a.heads) % nkb;
+    s = idx / (a.heads * nkb);
+  }
   const int cu0 = a.cu_seqlens[s];
   const int S = a.cu_seqlens[s + 1] - cu0;
   // metadata check, as in the forward: the last key block of the grid covers the sequence end
@@ -182,8 +213,8 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
   const int64_t hoff = ((int64_t)cu0 * a.heads + h) * kHeadDim;
   const uint16_t* qbase = a.q + hoff;
   const uint16_t* gbase = a.dout + hoff;
-  const float* lse = a.work + (int64_t)cu0 * a.heads + h;           // lse * log2(e)
-  const float* dlt = a.work + a.rows + (int64_t)cu0 * a.heads + h;  // -delta
+  const float* lse = a.work + h * (a.rows / a.heads) + cu0;  // lse * log2(e), head-major
+  const float* dlt = lse + a.rows;                            // -delta
 
   const float c = a.scale_log2;
   const SwzLane sl_(lane);
@@ -245,8 +276,8 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
     float* wd = sD + wave * 2 * BMQ;
     auto issue_blk = [&](int b, int buf) {
       const int p0 = slo + 32 * b;
-      dma4(lse + (int64_t)min(p0 + lane, S - 1) * a.heads, wl + buf * BMQ);
-      dma4(dlt + (int64_t)min(p0 + lane, S - 1) * a.heads, wd + buf * BMQ);
+      dma4(lse + min(p0 + lane, S - 1), wl + buf * BMQ);
+      dma4(dlt + min(p0 + lane, S - 1), wd + buf * BMQ);
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
         const int row = 4 * g + (lane >> 4);
@@ -374,7 +405,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(BwdArgs a, int nkb) {
   // copy tile j into buffer set b (= j % 4)
   auto issue_to = [&](int j, int b) {
     dma_qtile(sQ + b * Q_TILE, sG + b * Q_TILE, sL + b * BMQ, sD + b * BMQ, qbase, gbase, lse,
-              dlt, rs, a.heads, qlo + j * BMQ, S - 1, wave, lane);
+              dlt, rs, qlo + j * BMQ, S - 1, wave, lane);
   };
   auto issue = [&](int j) { issue_to(j, j & 3); };
 
@@ -638,7 +669,7 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
     qf[st] = *reinterpret_cast<const u32x4*>(a.q + hoff + pq * rs + st * 16 + half * 8);
     gf[st] = *reinterpret_cast<const u32x4*>(a.dout + hoff + pq * rs + st * 16 + half * 8);
   }
-  const int64_t prow = (int64_t)(cu0 + pq) * a.heads + h;
+  const int64_t prow = h * (a.rows / a.heads) + cu0 + pq;  // head-major work rows
   float lse2 = a.work[prow];
   float dlt = a.work[a.rows + prow];  // -delta
   // Materialise the operands here: the compiler then waits for these loads once, before the
@@ -784,15 +815,17 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
 }  // namespace
 
 hipError_t launch_prefill_bwd(const BwdArgs& a, int out_f32, int grad_f32, hipStream_t s) {
-  const int64_t rows = a.rows;
+  const int64_t rows = a.rows, total = a.rows / a.heads;
   if (rows > 0) {
-    const dim3 g((unsigned)((rows + 15) / 16));
+    const dim3 g((unsigned)((total + 31) / 32 * a.heads));
     if (out_f32)
       hipLaunchKernelGGL(delta_kernel<float>, g, dim3(256), 0, s,
-                         reinterpret_cast<const float*>(a.out), a.dout, a.lse, a.work, rows);
+                         reinterpret_cast<const float*>(a.out), a.dout, a.lse, a.work, total,
+                         a.heads);
     else
       hipLaunchKernelGGL(delta_kernel<uint16_t>, g, dim3(256), 0, s,
-                         reinterpret_cast<const uint16_t*>(a.out), a.dout, a.lse, a.work, rows);
+                         reinterpret_cast<const uint16_t*>(a.out), a.dout, a.lse, a.work, total,
+                         a.heads);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
