@@ -108,8 +108,14 @@ int main() {
     if (dp.aligned) {
       CHECK(!masked && min_rows == 0 && grid_user == 0);
       for (int b = 0; b < B; ++b) CHECK(L[b] == L[0]);
-      CHECK(dp.grid == (int64_t)B * H && !dp.stream_k);
+      CHECK(dp.grid == (int64_t)B * H && !dp.stream_k && dp.split == 0);
       CHECK(dp.grid <= std::min(resident, grid_max));
+    } else if (dp.split > 0) {
+      CHECK(!masked && min_rows == 0 && grid_user == 0 && !dp.stream_k);
+      for (int b = 0; b < B; ++b) CHECK(L[b] == L[0]);
+      CHECK(dp.split >= 2 && dp.grid == (int64_t)B * H * dp.split);
+      CHECK(dp.grid == std::min(resident, grid_max));
+      CHECK(L[0] >= 64 * (int64_t)dp.split);  // every piece holds at least the minimum rows
     } else {
       CHECK(dp.stream_k);
       CHECK(dp.rows_per_piece >= (min_rows > 0 ? min_rows : 64));

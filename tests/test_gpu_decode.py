@@ -194,6 +194,29 @@ def test_decode_small_every_step(wa, dtype, chunk):
     tr.cache.close()
 
 
+def test_split_layout_equal_ranges(wa):
+    """A uniform batch whose 128 ranges divide the resident workgroups (1,024 on MI355X at four
+    per CU) takes the split layout: every range cut into k equal pieces, merged in the launch.
+    Every step against the oracle, fused and unfused, and against a forced stream-K split."""
+    B, T = 8, 40
+    wl = W.make_decode("split", 97, "bf16", [600] * B, [128] * B, [T] * B, seed=7)
+    got = {}
+    for fused in (False, True):
+        tr = Trajectory(wa, wl, wa.MODE_RSWA)
+        grid, launches = tr.cache.decode_plan()
+        assert launches == 1
+        got[fused] = tr.run(range(1, T + 1), t_end=T, fused=fused)
+        tr.cache.close()
+        check_steps(wl, 0, got[fused])
+    tr = Trajectory(wa, wl, wa.MODE_RSWA)
+    tr.cache.set_decode_split(0, 1000)  # a user grid: stream-K
+    sk = tr.run(range(1, T + 1), t_end=T, fused=True)
+    tr.cache.close()
+    for t in range(1, T + 1):
+        np.testing.assert_allclose(got[True][t], sk[t], rtol=0, atol=1e-5)
+        np.testing.assert_allclose(got[False][t], sk[t], rtol=0, atol=1e-5)
+
+
 @pytest.mark.parametrize("grid", [1, 7, 4096])
 def test_decode_grid_sizes(wa, grid):
     m, n, T = [100, 300, 9, 64], [16, 128, 5, 64], [80, 80, 80, 80]

@@ -11,6 +11,9 @@
 // step needs no host sync and no table upload:
 //  * aligned: one 256-thread workgroup per (b, h) key range, used when the batch's ranges are
 //    equal and about fill one round of resident workgroups;
+//  * split: equal ranges whose count divides the resident workgroups are each cut into k equal
+//    pieces (every piece then holds rows of one range only and publishes its partial once, at its
+//    end), merged like the stream-K ranges below;
 //  * stream-K: the concatenation of all (b, h) key ranges is cut into equal contiguous pieces, one
 //    per resident workgroup, so every workgroup streams the same number of rows (no tail round,
 //    balanced for ragged batches). A piece may cover parts of several ranges; a range split over
@@ -500,8 +503,39 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   int64_t* s_cum = reinterpret_cast<int64_t*>(s_dyn);
   int* s_len = reinterpret_cast<int*>(s_cum + a.batch + 1);
   int* s_new = s_len + a.batch;
-  build_work_table(a, s_len, s_new, s_cum);
   const int H = a.heads;
+
+  if (a.uni_t >= 0 && (a.aligned || a.split > 1)) {
+    // Host-known plan over equal ranges: every sequence has the same live rows and new-row slot,
+    // so no work table (and none of its barriers) is needed; block 0 advances the counters.
+    const SeqState st = seq_state(a, 0);
+    const int rnew = st.app ? (a.full_causal ? a.uni_m + st.t : a.uni_m + st.t % a.uni_cap) : -1;
+    if (blockIdx.x == 0)
+      for (int b = threadIdx.x; b < a.batch; b += kThreads) {
+        if (a.steps_out) a.steps_out[b] = st.app ? st.t + 1 : st.t;
+        if (a.k_new && a.full_causal && st.t >= a.uni_cap) *a.meta.err = 1;
+      }
+    if (st.L == 0) return;
+    if (a.aligned) {
+      const int s = blockIdx.x;
+      const int b = s / H, h = s - b * H;
+      if (b >= a.batch) return;
+      decode_range<KV, OUT, U>(a, b, h, 0, st.L, rnew, true, 0, 1, s_m, s_l, s_acc, &s_flag, 0,
+                               st.L);
+      return;
+    }
+    const int k = a.split;
+    const int s = blockIdx.x / k, i = blockIdx.x - s * k;
+    const int b = s / H, h = s - b * H;
+    if (b >= a.batch) return;
+    const int r0 = (int)((int64_t)st.L * i / k), r1 = (int)((int64_t)st.L * (i + 1) / k);
+    if (decode_range<KV, OUT, U>(a, b, h, r0, r1, rnew, false, (int64_t)blockIdx.x + s, k, s_m,
+                                 s_l, s_acc, &s_flag, 0, max(r1 - r0, 1)))
+      merge_range<OUT>(a, s, (int64_t)s * k, k, s_w, s_lw, s_red);
+    return;
+  }
+
+  build_work_table(a, s_len, s_new, s_cum);
   const int64_t total = s_cum[a.batch];
 
   if (a.aligned) {
@@ -510,6 +544,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     if (b >= a.batch || s_len[b] == 0) return;
     decode_range<KV, OUT, U>(a, b, h, 0, s_len[b], s_new[b], true, 0, 1, s_m, s_l, s_acc,
                              &s_flag, 0, s_len[b]);
+    return;
+  }
+
+  if (a.split > 1) {  // piece i of range s: rows [i L / k, (i + 1) L / k)
+    const int k = a.split;
+    const int s = blockIdx.x / k, i = blockIdx.x - s * k;
+    const int b = s / H, h = s - (s / H) * H;
+    if (b >= a.batch || s_len[b] == 0) return;
+    const int L = s_len[b];
+    const int r0 = (int)((int64_t)L * i / k), r1 = (int)((int64_t)L * (i + 1) / k);
+    if (decode_range<KV, OUT, U>(a, b, h, r0, r1, s_new[b], false, (int64_t)blockIdx.x + s, k,
+                                 s_m, s_l, s_acc, &s_flag, 0, max(r1 - r0, 1)))
+      merge_range<OUT>(a, s, (int64_t)s * k, k, s_w, s_lw, s_red);
     return;
   }
 

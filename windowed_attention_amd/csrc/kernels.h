@@ -54,6 +54,8 @@ struct DecodeArgs {
   int32_t heads;
   int32_t full_causal;
   int32_t aligned;          // 1: one workgroup per (b, h) key range; 0: balanced stream-K ranges
+  int32_t split;            // > 1 (and not aligned): workgroup w takes piece w % split of range
+                            // w / split, rows [i L / split, (i + 1) L / split)
   int32_t min_rows;         // stream-K: fewest rows a workgroup takes
   float scale_log2;         // softmax scale * log2(e)
   // Host-known plan: when every sequence has the same m, capacity and step count and no active

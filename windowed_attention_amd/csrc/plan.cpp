@@ -85,8 +85,17 @@ DecodePlan plan_decode(const std::vector<int64_t>& live_rows, int32_t heads, int
     p.rows_per_piece = live_rows[0];
     return p;
   }
-  const int64_t g_req = grid_user > 0 ? std::min<int64_t>(grid_user, grid_max) : resident;
   const int64_t w_min = min_rows > 0 ? min_rows : 64;
+  if (!user && uniform && nseg < resident && resident % nseg == 0) {
+    const int64_t k = resident / nseg;
+    if (k >= 2 && live_rows[0] >= k * w_min) {
+      p.split = (int32_t)k;
+      p.grid = resident;
+      p.rows_per_piece = (live_rows[0] + k - 1) / k;
+      return p;
+    }
+  }
+  const int64_t g_req = grid_user > 0 ? std::min<int64_t>(grid_user, grid_max) : resident;
   p.rows_per_piece = std::max<int64_t>(w_min, (total + g_req - 1) / g_req);
   p.grid = (total + p.rows_per_piece - 1) / p.rows_per_piece;
   p.stream_k = true;

@@ -515,6 +515,7 @@ rswa_status decode_launch(rswa_cache* c, const void* q_dev, const void* k_dev, c
     const rswa::DecodePlan plan = rswa::plan_decode(L, c->H, resident, c->grid_max, c->min_rows,
                                                     c->grid_user, active_dev != nullptr);
     a.aligned = plan.aligned ? 1 : 0;
+    a.split = plan.split;
     const hipError_t e = rswa::launch_decode(a, c->kv_dtype == RSWA_F32, out_dtype == RSWA_F32,
                                              (int)plan.grid, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, what);
