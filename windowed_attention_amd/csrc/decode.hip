@@ -492,9 +492,7 @@ __device__ __forceinline__ bool decode_range(const DecodeArgs& a, int b, int h, 
   return *s_flag != 0;
 }
 
-// FIXED: the aligned or split layout (a fixed piece per workgroup); otherwise stream-K. Separate
-// instantiations, so that each layout's code is compiled on its own.
-template <typename KV, typename OUT, int U, bool FIXED>
+template <typename KV, typename OUT, int U>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
   __shared__ float s_m[kMaxGroups], s_l[kMaxGroups];
@@ -507,63 +505,85 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   int* s_new = s_len + a.batch;
   const int H = a.heads;
 
-  if constexpr (FIXED) {
-    // One workgroup per range (aligned, k = 1) or piece i of k of range s (split): rows
-    // [i L / k, (i + 1) L / k). With a host-known plan every sequence has the same live rows and
-    // new-row slot, so no work table (and none of its barriers) is needed; block 0 advances the
-    // counters.
-    const int k = a.aligned ? 1 : a.split;
+  if (a.uni_t >= 0 && (a.aligned || a.split > 1)) {
+    // Host-known plan over equal ranges: every sequence has the same live rows and new-row slot,
+    // so no work table (and none of its barriers) is needed; block 0 advances the counters.
+    const SeqState st = seq_state(a, 0);
+    const int rnew = st.app ? (a.full_causal ? a.uni_m + st.t : a.uni_m + st.t % a.uni_cap) : -1;
+    if (blockIdx.x == 0)
+      for (int b = threadIdx.x; b < a.batch; b += kThreads) {
+        if (a.steps_out) a.steps_out[b] = st.app ? st.t + 1 : st.t;
+        if (a.k_new && a.full_causal && st.t >= a.uni_cap) *a.meta.err = 1;
+      }
+    if (st.L == 0) return;
+    if (a.aligned) {
+      const int s = blockIdx.x;
+      const int b = s / H, h = s - b * H;
+      if (b >= a.batch) return;
+      decode_range<KV, OUT, U>(a, b, h, 0, st.L, rnew, true, 0, 1, s_m, s_l, s_acc, &s_flag, 0,
+                               st.L);
+      return;
+    }
+    const int k = a.split;
     const int s = blockIdx.x / k, i = blockIdx.x - s * k;
     const int b = s / H, h = s - b * H;
-    int L, rnew;
-    if (a.uni_t >= 0) {
-      const SeqState st = seq_state(a, 0);
-      L = st.L;
-      rnew = st.app ? (a.full_causal ? a.uni_m + st.t : a.uni_m + st.t % a.uni_cap) : -1;
-      if (blockIdx.x == 0)
-        for (int bb = threadIdx.x; bb < a.batch; bb += kThreads) {
-          if (a.steps_out) a.steps_out[bb] = st.app ? st.t + 1 : st.t;
-          if (a.k_new && a.full_causal && st.t >= a.uni_cap) *a.meta.err = 1;
-        }
-    } else {
-      build_work_table(a, s_len, s_new, s_cum);
-      L = b < a.batch ? s_len[b] : 0;
-      rnew = b < a.batch ? s_new[b] : -1;
-    }
-    if (b >= a.batch || L == 0) return;
-    const int r0 = (int)((int64_t)L * i / k), r1 = (int)((int64_t)L * (i + 1) / k);
-    if (decode_range<KV, OUT, U>(a, b, h, r0, r1, rnew, k == 1, (int64_t)blockIdx.x + s, k, s_m,
+    if (b >= a.batch) return;
+    const int r0 = (int)((int64_t)st.L * i / k), r1 = (int)((int64_t)st.L * (i + 1) / k);
+    if (decode_range<KV, OUT, U>(a, b, h, r0, r1, rnew, false, (int64_t)blockIdx.x + s, k, s_m,
                                  s_l, s_acc, &s_flag, 0, max(r1 - r0, 1)))
       merge_range<OUT>(a, s, (int64_t)s * k, k, s_w, s_lw, s_red);
     return;
-  } else {
-    build_work_table(a, s_len, s_new, s_cum);
-    const int64_t total = s_cum[a.batch];
-    const int64_t W = piece_rows(a, total);
-    const int64_t pos0 = (int64_t)blockIdx.x * W;
-    int64_t pos = pos0;
-    const int64_t end = min(pos + W, total);
-    while (pos < end) {
-      int lo = 0, hi = a.batch - 1;  // last b with s_cum[b] <= pos
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_cum[mid] <= pos) lo = mid; else hi = mid - 1;
-      }
-      const int b = lo;
-      const int L = s_len[b];
-      const int64_t off = pos - s_cum[b];
-      const int h = (int)(off / L);
-      const int r0 = (int)(off - (int64_t)h * L);
-      const int r1 = (int)min((int64_t)L, r0 + (end - pos));
-      const int s = b * H + h;
-      const int64_t A = s_cum[b] + (int64_t)h * L;
-      const int64_t f = A / W, l = (A + L - 1) / W;  // pieces that hold rows of this range
-      const bool direct = f == l;
-      if (decode_range<KV, OUT, U>(a, b, h, r0, r1, s_new[b], direct, (int64_t)blockIdx.x + s,
-                                   (int)(l - f + 1), s_m, s_l, s_acc, &s_flag, pos - pos0, W))
-        merge_range<OUT>(a, s, f, (int)(l - f + 1), s_w, s_lw, s_red);
-      pos += r1 - r0;
+  }
+
+  build_work_table(a, s_len, s_new, s_cum);
+  const int64_t total = s_cum[a.batch];
+
+  if (a.aligned) {
+    const int s = blockIdx.x;
+    const int b = s / H, h = s - (s / H) * H;
+    if (b >= a.batch || s_len[b] == 0) return;
+    decode_range<KV, OUT, U>(a, b, h, 0, s_len[b], s_new[b], true, 0, 1, s_m, s_l, s_acc,
+                             &s_flag, 0, s_len[b]);
+    return;
+  }
+
+  if (a.split > 1) {  // piece i of range s: rows [i L / k, (i + 1) L / k)
+    const int k = a.split;
+    const int s = blockIdx.x / k, i = blockIdx.x - s * k;
+    const int b = s / H, h = s - (s / H) * H;
+    if (b >= a.batch || s_len[b] == 0) return;
+    const int L = s_len[b];
+    const int r0 = (int)((int64_t)L * i / k), r1 = (int)((int64_t)L * (i + 1) / k);
+    if (decode_range<KV, OUT, U>(a, b, h, r0, r1, s_new[b], false, (int64_t)blockIdx.x + s, k,
+                                 s_m, s_l, s_acc, &s_flag, 0, max(r1 - r0, 1)))
+      merge_range<OUT>(a, s, (int64_t)s * k, k, s_w, s_lw, s_red);
+    return;
+  }
+
+  const int64_t W = piece_rows(a, total);
+  const int64_t pos0 = (int64_t)blockIdx.x * W;
+  int64_t pos = pos0;
+  const int64_t end = min(pos + W, total);
+  while (pos < end) {
+    int lo = 0, hi = a.batch - 1;  // last b with s_cum[b] <= pos
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_cum[mid] <= pos) lo = mid; else hi = mid - 1;
     }
+    const int b = lo;
+    const int L = s_len[b];
+    const int64_t off = pos - s_cum[b];
+    const int h = (int)(off / L);
+    const int r0 = (int)(off - (int64_t)h * L);
+    const int r1 = (int)min((int64_t)L, r0 + (end - pos));
+    const int s = b * H + h;
+    const int64_t A = s_cum[b] + (int64_t)h * L;
+    const int64_t f = A / W, l = (A + L - 1) / W;  // pieces that hold rows of this range
+    const bool direct = f == l;
+    if (decode_range<KV, OUT, U>(a, b, h, r0, r1, s_new[b], direct, (int64_t)blockIdx.x + s,
+                                 (int)(l - f + 1), s_m, s_l, s_acc, &s_flag, pos - pos0, W))
+      merge_range<OUT>(a, s, f, (int)(l - f + 1), s_w, s_lw, s_red);
+    pos += r1 - r0;
   }
 }
 
@@ -575,19 +595,15 @@ constexpr int kRowsPerLane = RSWA_DECODE_ROWS;  // U: rows each lane group loads
 template <typename KV, typename OUT>
 hipError_t launch_typed(const DecodeArgs& a, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (a.aligned || a.split > 1)
-    hipLaunchKernelGGL((decode_kernel<KV, OUT, kRowsPerLane, true>), dim3(grid), dim3(kThreads),
-                       decode_lds_bytes(a.batch), s, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<KV, OUT, kRowsPerLane, false>), dim3(grid), dim3(kThreads),
-                       decode_lds_bytes(a.batch), s, a);
+  hipLaunchKernelGGL((decode_kernel<KV, OUT, kRowsPerLane>), dim3(grid), dim3(kThreads),
+                     decode_lds_bytes(a.batch), s, a);
   return hipGetLastError();
 }
 
 template <typename KV, typename OUT>
 int occupancy_typed(int batch) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<KV, OUT, kRowsPerLane, false>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<KV, OUT, kRowsPerLane>,
                                                    kThreads, decode_lds_bytes(batch)) != hipSuccess)
     return 1;
   return n > 0 ? n : 1;
