@@ -266,10 +266,14 @@ def run_decode(args, wl, mode_full: bool, steps: int, warmup: int, kernel_events
 
 
 def flatness(lat, n, T):
+    """Median step latency over the last w steps / over the first w steps once the ring is full
+    (t > n), w = max(500, T / 10) capped at half of the steps after the ring fills, so that the
+    late window holds the timed region's sample."""
     ts = np.array([t for t, _ in lat])
     us = np.array([u for _, u in lat])
-    late = us[(ts >= T - 500) & (ts <= T)]
-    early = us[(ts >= n + 1) & (ts <= n + 500)]
+    w = min(max(500, T // 10), max(1, (T - n) // 2))
+    late = us[(ts >= T - w) & (ts <= T)]
+    early = us[(ts >= n + 1) & (ts <= n + w)]
     if late.size == 0 or early.size == 0:
         return None
     return float(np.median(late) / np.median(early))
