@@ -114,7 +114,7 @@ int main() {
       CHECK(!masked && min_rows == 0 && grid_user == 0 && !dp.stream_k);
       for (int b = 0; b < B; ++b) CHECK(L[b] == L[0]);
       CHECK(dp.split >= 2 && dp.grid == (int64_t)B * H * dp.split);
-      CHECK(dp.grid == std::min(resident, grid_max));
+      CHECK(dp.grid <= std::min(resident, grid_max));
       CHECK(L[0] >= 64 * (int64_t)dp.split);  // every piece holds at least the minimum rows
     } else {
       CHECK(dp.stream_k);

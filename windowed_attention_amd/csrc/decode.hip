@@ -11,9 +11,9 @@
 // step needs no host sync and no table upload:
 //  * aligned: one 256-thread workgroup per (b, h) key range, used when the batch's ranges are
 //    equal and about fill one round of resident workgroups;
-//  * split: equal ranges whose count divides the resident workgroups are each cut into k equal
-//    pieces (every piece then holds rows of one range only and publishes its partial once, at its
-//    end), merged like the stream-K ranges below;
+//  * split: fewer equal ranges are each cut into k equal pieces (every piece then holds rows of
+//    one range only and publishes its partial once, at its end), merged like the stream-K ranges
+//    below;
 //  * stream-K: the concatenation of all (b, h) key ranges is cut into equal contiguous pieces, one
 //    per resident workgroup, so every workgroup streams the same number of rows (no tail round,
 //    balanced for ragged batches). A piece may cover parts of several ranges; a range split over

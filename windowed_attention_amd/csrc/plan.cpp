@@ -86,11 +86,11 @@ DecodePlan plan_decode(const std::vector<int64_t>& live_rows, int32_t heads, int
     return p;
   }
   const int64_t w_min = min_rows > 0 ? min_rows : 64;
-  if (!user && uniform && nseg < resident && resident % nseg == 0) {
-    const int64_t k = resident / nseg;
-    if (k >= 2 && live_rows[0] >= k * w_min) {
+  if (!user && uniform && 2 * nseg <= resident) {
+    const int64_t k = std::min(resident / nseg, live_rows[0] / w_min);
+    if (k >= 2) {
       p.split = (int32_t)k;
-      p.grid = resident;
+      p.grid = nseg * k;
       p.rows_per_piece = (live_rows[0] + k - 1) / k;
       return p;
     }

@@ -46,10 +46,10 @@ struct DecodePlan {
 // workgroups that fit the GPU at once; grid_max: workgroups the workspace holds; min_rows /
 // grid_user: user settings (0 = automatic); masked: an active mask is in use (row counts are then
 // only upper bounds, so the aligned and split layouts, which need equal ranges, are not chosen).
-// Equal ranges that fill one round of resident workgroups get one workgroup each (aligned); equal
-// ranges whose count divides the resident workgroups into k >= 2 pieces per range of at least the
-// stream-K minimum rows each are cut k ways (split: every piece holds rows of one range only, so
-// it publishes its partial once, at its end); anything else is cut into equal stream-K pieces.
+// Equal ranges that fill one round of resident workgroups get one workgroup each (aligned); fewer
+// equal ranges are cut into k = min(resident / ranges, rows / minimum rows) >= 2 equal pieces each
+// (split: every piece holds rows of one range only, so it publishes its partial once, at its end);
+// anything else is cut into equal stream-K pieces.
 DecodePlan plan_decode(const std::vector<int64_t>& live_rows, int32_t heads, int64_t resident,
                        int64_t grid_max, int32_t min_rows, int32_t grid_user, bool masked);
 
