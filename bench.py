@@ -768,14 +768,14 @@ def main():
             per_launch_ms = float(r["kern_ms"].mean())
         if per_launch_ms is not None:
             ach = float(r["launch_bytes"].mean()) / (per_launch_ms * 1e-3) / 1e9
-        else:  # decode + merge launches per step: the step is the unit
+        else:  # separate append and decode launches per step: the step is the unit
             ach = step_bytes / (ms_step * 1e-3) / 1e9
         res["roofline"] = dict(bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
                                frac=ach / PEAK_HBM_GBS,
                                traffic=traffic_from_profile("decode", source_hash(DECODE_SOURCES)),
                                kernel=("fused append + decode step" if r["fused"] else
                                        "decode (separate append)")
-                               + ("" if one_launch else " (decode + merge launches)"),
+                               + ("" if one_launch else " (append + decode launches)"),
                                launches_per_step=r["launches_per_step"],
                                workgroups=r["grid_blocks"],
                                avg_launch_us=(per_launch_ms or ms_step) * 1e3,

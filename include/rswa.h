@@ -280,17 +280,20 @@ rswa_status rswa_cache_steps(rswa_cache* cache, int32_t* steps_host, void* strea
 rswa_status rswa_cache_info(const rswa_cache* cache, void** storage_dev,
                             int64_t* seq_offset_host /* [B] */, int32_t* rows_host /* [B] */);
 
-/* Decode work split. By default a batch of equal key ranges that about fills one round of
- * resident workgroups gets one workgroup per (b, h) range; otherwise the concatenated key ranges
- * are cut into equal contiguous pieces, one per resident workgroup, and split ranges are merged in a
- * second kernel. chunk_rows (> 0) sets the fewest rows a piece may hold and grid_blocks (> 0) the
- * number of pieces; either one forces the piece layout. 0 restores the automatic choice. Results
- * depend on these only through float32 summation order. Host only. */
+/* Decode work split. By default, when no active mask has been given and all sequences hold equal
+ * key ranges: a batch whose ranges about fill one round of resident workgroups gets one workgroup
+ * per (b, h) range; a smaller batch has every range cut into k = min(resident workgroups / ranges,
+ * rows / 64) >= 2 equal pieces. Otherwise the concatenated key ranges are cut into equal
+ * contiguous pieces, one per resident workgroup. A range split over pieces is merged inside the
+ * same launch by its last piece to finish. chunk_rows (> 0) sets the fewest rows a piece may hold
+ * and grid_blocks (> 0) the number of pieces; either one forces the contiguous-piece layout. 0
+ * restores the automatic choice. Results depend on these only through float32 summation order.
+ * Host only. */
 rswa_status rswa_cache_set_decode_split(rswa_cache* cache, int32_t chunk_rows, int32_t grid_blocks);
 
 /* What the next decode launch on this cache does when no active mask is given (appending = 1 for
  * rswa_decode_step, 0 for rswa_decode_attn): the workgroups of the decode kernel and the number of
- * kernel launches (1, or 2 when split ranges need the merge kernel). Host only. */
+ * kernel launches (1; 0 when there is nothing to decode). Host only. */
 rswa_status rswa_cache_decode_plan(const rswa_cache* cache, int32_t appending,
                                    int32_t* grid_blocks, int32_t* launches);
 

@@ -1,7 +1,7 @@
 """GPU checks of the graph-captured step loop (rswa_step_graph_*): every replay, with eager work
 (input-slot copies) and a synchronization between replays, must give bit for bit what the same
-fused steps give when launched one by one, including when the captured steps carry the stream-K
-split and its merge launch, and the step counters must advance by the captured count.
+fused steps give when launched one by one, including when the captured steps split ranges over
+pieces and merge them inside the launch, and the step counters must advance by the captured count.
 """
 import numpy as np
 import pytest
