@@ -102,6 +102,25 @@ uint64_t rswa_cache_bytes(const rswa_cache_desc* desc);
 rswa_status rswa_cache_create(const rswa_cache_desc* desc, const void* prefix_k_dev,
                               const void* prefix_v_dev, void* stream, rswa_cache** out);
 
+/* Create a cache from a packed prefill batch, so that decoding continues where a prefill /
+ * teacher-forced pass over the same sequences ended (the prefill-to-cache fill). Sequence b is
+ * the segment [cu_seqlens_host[b], cu_seqlens_host[b + 1]) of k_dev / v_dev: its first m_b rows
+ * are the prefix and the remaining t_b = S_b - m_b rows its outputs so far, in order (the layout
+ * rswa_prefill_attn reads). The cache equals one made by rswa_cache_create from the prefixes
+ * followed by t_b appends of those outputs, bit for bit: prefix rows [0, m_b); in RSWA mode the
+ * last min(n_b, t_b) outputs in their ring slots (output j in row m_b + (j mod n_b); the cache
+ * holds the prefix plus the previous n outputs: deep dive "Unlimited-OCR", N(t) code block); in
+ * FULL_CAUSAL mode all t_b outputs in rows m_b + j; step counter t_b. Rows beyond those are not
+ * touched. k_dev / v_dev: packed token-major [total][H][D] of kv_dtype, 16-byte aligned;
+ * cu_seqlens_host: host [batch + 1], cu_seqlens_host[0] >= 0, S_b >= m_b. desc->prefix_paged
+ * must be 0. Enqueued on `stream`; the call returns once that stream has finished the copies.
+ * Errors as rswa_cache_create, plus RSWA_E_INVALID (cu_seqlens, a segment shorter than its
+ * prefix, prefix_paged) and RSWA_E_CAPACITY (FULL_CAUSAL: t_b > max_steps). On error *out is
+ * NULL. */
+rswa_status rswa_cache_create_from_prefill(const rswa_cache_desc* desc, const void* k_dev,
+                                           const void* v_dev, const int32_t* cu_seqlens_host,
+                                           void* stream, rswa_cache** out);
+
 /* Create a cache whose prefixes live in a shared, token-granular page pool (paged / shared prefix
  * KV: the SGLang server that the deep dive "Unlimited-OCR" shows infer.py launching runs with a
  * page size of one token, and GeekNews "Unlimited OCR", limitations and future work, plans a pool
@@ -179,7 +198,9 @@ rswa_status rswa_decode_step(rswa_cache* cache, const void* q_dev, const void* k
  * Errors: RSWA_E_INVALID (host-checkable arguments), RSWA_E_UNSUPPORTED (head_dim), RSWA_E_HIP.
  * Device-side metadata cannot be checked before the launch. The kernels check it on the device:
  * a sequence longer than max_seqlen (its rows past max_seqlen are then not written), m_s > S_s,
- * S_s < 0 or n_s < 1 sets a per-device error word that rswa_prefill_check() reports. */
+ * S_s < 0 or n_s < 1 sets a per-device error word that rswa_prefill_check() reports.
+ * No decode cache is written here: rswa_cache_create_from_prefill builds one from the same k / v
+ * and cu_seqlens (host copy), so decoding can continue after the pass. */
 rswa_status rswa_prefill_attn(const void* q_dev, const void* k_dev, const void* v_dev,
                               void* out_dev, int32_t out_dtype, const int32_t* cu_seqlens_dev,
                               const int32_t* prefix_len_dev, const int32_t* window_dev,

@@ -177,6 +177,39 @@ def test_paged_create_checks_arguments_before_device_work(wa):
     assert h.value is None
 
 
+def test_prefill_fill_checks_arguments_before_device_work(wa):
+    lib = wa._lib
+    null, one = ctypes.c_void_p(None), ctypes.c_void_p(16)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+
+    def create(d, k, v, cu):
+        h = ctypes.c_void_p(None)
+        arr = None if cu is None else np.asarray(cu, dtype=np.int32)
+        st = lib.rswa_cache_create_from_prefill(
+            ctypes.byref(d), k, v, None if arr is None else arr.ctypes.data_as(i32p), null,
+            ctypes.byref(h))
+        assert h.value is None
+        return st
+
+    d, keep = wa._desc(np.array([5, 3]), np.array([4, 4]), None, 16, 128, wa.torch.bfloat16,
+                       wa.MODE_RSWA)
+    assert create(d, one, one, None) == -1                 # no cu_seqlens
+    assert create(d, one, one, [-1, 6, 10]) == -1          # negative start
+    assert create(d, one, one, [0, 4, 10]) == -1           # segment 0 shorter than m_0 = 5
+    assert b"shorter than its prefix" in lib.rswa_last_error()
+    assert create(d, one, one, [0, 9, 8]) == -1            # decreasing offsets
+    assert create(d, null, one, [0, 9, 15]) == -1          # rows but no K
+    assert create(d, ctypes.c_void_p(8), one, [0, 9, 15]) == -1  # misaligned K
+    d.prefix_paged = 1
+    assert create(d, one, one, [0, 9, 15]) == -1
+    assert b"prefix_paged" in lib.rswa_last_error()
+    # full causal: a segment with more outputs than max_steps
+    d, keep = wa._desc(np.array([5, 3]), None, np.array([4, 4]), 16, 128, wa.torch.bfloat16,
+                       wa.MODE_FULL_CAUSAL)
+    assert create(d, one, one, [0, 10, 15]) == -3
+    assert b"max_steps" in lib.rswa_last_error()
+
+
 def test_step_graph_arguments_are_checked_before_device_work(wa):
     lib = wa._lib
     null, one = ctypes.c_void_p(None), ctypes.c_void_p(16)

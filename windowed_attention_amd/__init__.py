@@ -28,6 +28,7 @@ EXPORTS = ("rswa_cache_plan", "rswa_cache_bytes", "rswa_cache_create", "rswa_cac
            "rswa_decode_attn", "rswa_decode_step", "rswa_prefill_attn", "rswa_prefill_fwd",
            "rswa_prefill_bwd", "rswa_cache_steps", "rswa_cache_info",
            "rswa_cache_set_decode_split", "rswa_cache_decode_plan", "rswa_cache_destroy",
+           "rswa_cache_create_from_prefill",
            "rswa_step_graph_create", "rswa_step_graph_launch", "rswa_step_graph_destroy",
            "rswa_cache_query", "rswa_prefill_check", "rswa_prefill_bwd_noalloc",
            "rswa_status_str",
@@ -65,6 +66,7 @@ def _load():
         "rswa_cache_create": (i32, [pdesc, vp, vp, vp, ctypes.POINTER(vp)]),
         "rswa_cache_create_paged": (i32, [pdesc, vp, vp, ctypes.c_int64, vp, vp,
                                           ctypes.POINTER(vp)]),
+        "rswa_cache_create_from_prefill": (i32, [pdesc, vp, vp, pi32, vp, ctypes.POINTER(vp)]),
         "rswa_append_kv": (i32, [vp, vp, vp, vp, vp]),
         "rswa_decode_attn": (i32, [vp, vp, vp, i32, f32, vp, vp]),
         "rswa_decode_step": (i32, [vp, vp, vp, vp, vp, i32, f32, vp, vp]),
@@ -194,16 +196,21 @@ class RswaCache:
     With `pool_k`, `pool_v` ([pool_rows][H][D]) and `prefix_table` (int32 [sum m_b], device) the
     prefixes are not copied: sequence b's prefix token j is pool row prefix_table[M_b + j]
     (rswa_cache_create_paged); prefix_k / prefix_v must then be None. The pools must stay alive
-    and unchanged while the cache is used (the object keeps a reference)."""
+    and unchanged while the cache is used (the object keeps a reference).
+
+    With `prefill_k`, `prefill_v` ([total][H][D]) and `cu_seqlens` (host sequence of B + 1 ints)
+    the cache is filled from a packed prefill batch (rswa_cache_create_from_prefill): segment b
+    holds sequence b's prefix then its outputs so far, and decoding continues after them."""
 
     def __init__(self, prefix_k: torch.Tensor | None, prefix_v: torch.Tensor | None, prefix_len,
                  window=None, *, mode=MODE_RSWA, max_steps=None, num_heads=16, head_dim=128,
                  kv_dtype=None, storage: torch.Tensor | None = None, pool_k=None, pool_v=None,
-                 prefix_table=None, stream=None):
+                 prefix_table=None, prefill_k=None, prefill_v=None, cu_seqlens=None, stream=None):
         m = np.asarray(prefix_len, dtype=np.int64).reshape(-1)
         paged = prefix_table is not None
+        filled = cu_seqlens is not None
         if kv_dtype is None:
-            src = pool_k if paged else prefix_k
+            src = pool_k if paged else (prefill_k if filled else prefix_k)
             if src is None:
                 raise ValueError("kv_dtype is required when there is no prefix tensor")
             kv_dtype = src.dtype
@@ -213,7 +220,20 @@ class RswaCache:
         d, keep = _desc(m, window, max_steps, num_heads, head_dim, kv_dtype, mode, storage,
                         paged=paged)
         h = ctypes.c_void_p(None)
-        if paged:
+        if filled:
+            if paged or prefix_k is not None or prefix_v is not None:
+                raise ValueError("a cache filled from a prefill takes prefill_k / prefill_v only")
+            cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32).reshape(-1))
+            if cu.size != m.size + 1:
+                raise ValueError(f"cu_seqlens must have {m.size + 1} entries")
+            total = int(prefill_k.shape[0])
+            shape = (total, num_heads, head_dim)
+            _check(_lib.rswa_cache_create_from_prefill(
+                ctypes.byref(d), _dev(prefill_k, "prefill_k", kv_dtype, shape),
+                _dev(prefill_v, "prefill_v", kv_dtype, shape),
+                cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _stream(stream),
+                ctypes.byref(h)), "rswa_cache_create_from_prefill")
+        elif paged:
             if prefix_k is not None or prefix_v is not None:
                 raise ValueError("a paged cache takes pool_k / pool_v, not prefix_k / prefix_v")
             rows = int(pool_k.shape[0])
@@ -333,6 +353,14 @@ class RswaCache:
 
 def rswa_cache_create(prefix_k, prefix_v, prefix_len, window=None, **kw) -> RswaCache:
     return RswaCache(prefix_k, prefix_v, prefix_len, window, **kw)
+
+
+def rswa_cache_create_from_prefill(k, v, cu_seqlens, prefix_len, window=None,
+                                   **kw) -> RswaCache:
+    """Cache filled from a packed prefill batch k / v ([total][H][D]): segment b of the host
+    sequence cu_seqlens holds prefix_len[b] prefix rows then that sequence's outputs so far."""
+    return RswaCache(None, None, prefix_len, window, prefill_k=k, prefill_v=v,
+                     cu_seqlens=cu_seqlens, **kw)
 
 
 def rswa_append_kv(cache: RswaCache, k: torch.Tensor, v: torch.Tensor,

@@ -83,6 +83,40 @@ __global__ __launch_bounds__(kThreads) void prefix_copy_kernel(PrefixCopyArgs a)
   }
 }
 
+// The live output rows of a cache filled from a packed prefill batch, written as the appends of
+// the sequence's t outputs would have left them: in R-SWA mode ring slot q (storage row m + q,
+// q < min(n, t)) holds the latest output j < t with j mod n = q, j = t - 1 - ((t - 1 - q) mod n);
+// in full-causal mode row m + j holds output j.
+template <int ELEM>
+__global__ __launch_bounds__(kThreads) void fill_outputs_kernel(FillArgs a) {
+  const int b = blockIdx.y;
+  const int64_t m = a.meta.prefix_len[b];
+  const int t = a.steps[b];
+  const int n = a.meta.cap[b];
+  const int live = a.full_causal ? t : min(t, n);
+  const int64_t R = a.meta.rows[b];
+  constexpr int CH = kHeadDim * ELEM / 16;
+  const int H = a.heads;
+  const int64_t total = (int64_t)live * H * CH;
+  const int64_t out0 = a.row0[b] + m;  // packed row of output 0
+  char* seq = reinterpret_cast<char*>(a.storage) + a.meta.seq_off[b] * ELEM;
+  const char* pk = reinterpret_cast<const char*>(a.k);
+  const char* pv = reinterpret_cast<const char*>(a.v);
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * kThreads) {
+    const int q = (int)(i / (H * CH));
+    const int rem = (int)(i - (int64_t)q * (H * CH));
+    const int h = rem / CH, c = rem - (rem / CH) * CH;
+    const int j = a.full_causal ? q : t - 1 - (t - 1 - q) % n;
+    const int64_t src = ((out0 + j) * H + h) * kHeadDim * ELEM + c * 16;
+    const int64_t r = m + q;
+    const int64_t dk = ((int64_t)h * R + r) * kHeadDim * ELEM + c * 16;
+    const int64_t dv = ((int64_t)(H + h) * R + r) * kHeadDim * ELEM + c * 16;
+    *reinterpret_cast<uint4*>(seq + dk) = *reinterpret_cast<const uint4*>(pk + src);
+    *reinterpret_cast<uint4*>(seq + dv) = *reinterpret_cast<const uint4*>(pv + src);
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void table_check_kernel(const int32_t* table, int64_t n,
                                                                int64_t pool_rows, int32_t* bad) {
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
@@ -122,6 +156,21 @@ hipError_t launch_prefix_copy(const PrefixCopyArgs& a, int kv_f32, int max_rows,
     hipLaunchKernelGGL(prefix_copy_kernel<4>, dim3((unsigned)gx, a.batch), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL(prefix_copy_kernel<2>, dim3((unsigned)gx, a.batch), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_outputs(const FillArgs& a, int kv_f32, int max_rows, hipStream_t s) {
+  if (max_rows <= 0) return hipSuccess;
+  const int elem = kv_f32 ? 4 : 2;
+  const int64_t pieces = (int64_t)max_rows * a.heads * (kHeadDim * elem / 16);
+  int64_t gx = (pieces + kThreads - 1) / kThreads;
+  if (gx > 4096) gx = 4096;
+  if (kv_f32)
+    hipLaunchKernelGGL(fill_outputs_kernel<4>, dim3((unsigned)gx, a.batch), dim3(kThreads), 0, s,
+                       a);
+  else
+    hipLaunchKernelGGL(fill_outputs_kernel<2>, dim3((unsigned)gx, a.batch), dim3(kThreads), 0, s,
+                       a);
   return hipGetLastError();
 }
 

@@ -77,6 +77,20 @@ struct PrefixCopyArgs {
   int32_t batch;
 };
 
+// Output rows of a cache filled from a packed prefill batch: sequence b's segment starts at packed
+// row row0[b] (its prefix), its outputs follow at row0[b] + m_b, and it holds steps[b] of them.
+struct FillArgs {
+  void* storage;
+  CacheMeta meta;
+  const void* k;            // [total][H][D], kv dtype
+  const void* v;
+  const int64_t* row0;      // [B]
+  const int32_t* steps;     // [B] t_b
+  int32_t heads;
+  int32_t batch;
+  int32_t full_causal;
+};
+
 struct PrefillArgs {
   const uint16_t* q;        // [total][H][D] bf16
   const uint16_t* k;
@@ -120,6 +134,8 @@ struct BwdArgs {
 
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_prefix_copy(const PrefixCopyArgs& a, int kv_f32, int max_rows, hipStream_t s);
+// max_rows: the most output rows any sequence holds (min(n_b, t_b), or t_b in full-causal mode).
+hipError_t launch_fill_outputs(const FillArgs& a, int kv_f32, int max_rows, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, int batch, int kv_f32, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int kv_f32, int out_f32, int grid_blocks,
                          hipStream_t s);

@@ -106,6 +106,8 @@ struct rswa_cache {
   std::vector<int64_t> calls;  // appends enqueued per sequence: an upper bound of t_b
   bool masked = false;         // an active mask has been used: calls[] may overstate t_b, so the
                                // full-causal capacity check is left to the device
+  bool equal_t = true;         // every t_b is the same (false after a fill from sequences of
+                               // unequal output counts); the host-known decode plan needs it
   int graphs = 0;              // live step graphs that reference this cache
   void* storage = nullptr;
   bool owns_storage = false;
@@ -205,9 +207,16 @@ struct PagedPrefix {
   const int32_t* table = nullptr;
 };
 
+// rswa_cache_create_from_prefill: packed prefix + output segments of a prefill batch.
+struct PrefillSource {
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const int32_t* cu = nullptr;  // host [B + 1]
+};
+
 rswa_status create_cache(const rswa_cache_desc* desc, const void* prefix_k_dev,
                          const void* prefix_v_dev, const PagedPrefix* pg, void* stream,
-                         rswa_cache** out) {
+                         rswa_cache** out, const PrefillSource* fill = nullptr) {
   if (!out) return fail(RSWA_E_INVALID, "out is NULL");
   *out = nullptr;
   rswa_cache* c = nullptr;
@@ -228,8 +237,35 @@ rswa_status create_cache(const rswa_cache_desc* desc, const void* prefix_k_dev,
       if ((reinterpret_cast<uintptr_t>(pg->pool_k) % 16) != 0 ||
           (reinterpret_cast<uintptr_t>(pg->pool_v) % 16) != 0)
         return fail(RSWA_E_INVALID, "pool_k / pool_v must be 16-byte aligned");
-    } else if (p.total_prefix_rows > 0 && (!prefix_k_dev || !prefix_v_dev)) {
+    } else if (!fill && p.total_prefix_rows > 0 && (!prefix_k_dev || !prefix_v_dev)) {
       return fail(RSWA_E_INVALID, "prefix_k_dev / prefix_v_dev are NULL but some m_b > 0");
+    }
+    // a fill from a prefill batch: sequence b is the segment [cu[b], cu[b + 1]), its first m_b
+    // rows the prefix, the other t_b rows its outputs
+    std::vector<int32_t> fill_t;
+    int64_t fill_rows = 0;
+    int fill_live = 0;
+    if (fill) {
+      if (!fill->cu) return fail(RSWA_E_INVALID, "cu_seqlens_host is NULL");
+      if (fill->cu[0] < 0) return fail(RSWA_E_INVALID, "cu_seqlens[0] < 0");
+      fill_t.resize(desc->batch);
+      for (int b = 0; b < desc->batch; ++b) {
+        const int64_t S = (int64_t)fill->cu[b + 1] - fill->cu[b];
+        if (S < p.prefix[b])
+          return fail(RSWA_E_INVALID, "a segment of cu_seqlens is shorter than its prefix");
+        const int64_t t = S - p.prefix[b];
+        if (desc->mode == RSWA_MODE_FULL_CAUSAL && t > p.cap[b])
+          return fail(RSWA_E_CAPACITY, "a segment holds more outputs than max_steps");
+        fill_t[b] = (int32_t)t;
+        fill_rows += S;
+        const int live = desc->mode == RSWA_MODE_FULL_CAUSAL ? (int)t : (int)std::min<int64_t>(t, p.cap[b]);
+        fill_live = std::max(fill_live, live);
+      }
+      if (fill_rows > 0 && (!fill->k || !fill->v))
+        return fail(RSWA_E_INVALID, "k_dev / v_dev are NULL but the segments hold rows");
+      if ((reinterpret_cast<uintptr_t>(fill->k) % 16) != 0 ||
+          (reinterpret_cast<uintptr_t>(fill->v) % 16) != 0)
+        return fail(RSWA_E_INVALID, "k_dev / v_dev must be 16-byte aligned");
     }
     if (desc->storage_dev && desc->storage_bytes < p.bytes)
       return fail(RSWA_E_CAPACITY, "storage_bytes smaller than rswa_cache_bytes()");
@@ -287,7 +323,14 @@ rswa_status create_cache(const rswa_cache_desc* desc, const void* prefix_k_dev,
     const size_t meta_bytes = off_err + 256;
     std::vector<unsigned char> host(meta_bytes, 0);
     std::memcpy(host.data() + off_i64, p.seq_off.data(), 8 * (size_t)B);
-    std::memcpy(host.data() + off_row0, p.prefix_row0.data(), 8 * (size_t)B);
+    if (fill) {
+      std::vector<int64_t> row0(B);
+      for (int b = 0; b < B; ++b) row0[b] = fill->cu[b];
+      std::memcpy(host.data() + off_row0, row0.data(), 8 * (size_t)B);
+      std::memcpy(host.data() + off_steps, fill_t.data(), 4 * (size_t)B);
+    } else {
+      std::memcpy(host.data() + off_row0, p.prefix_row0.data(), 8 * (size_t)B);
+    }
     std::memcpy(host.data() + off_rows, p.rows.data(), 4 * (size_t)B);
     std::memcpy(host.data() + off_pref, p.prefix.data(), 4 * (size_t)B);
     std::memcpy(host.data() + off_cap, p.cap.data(), 4 * (size_t)B);
@@ -360,8 +403,8 @@ rswa_status create_cache(const rswa_cache_desc* desc, const void* prefix_k_dev,
       rswa::PrefixCopyArgs pa{};
       pa.storage = c->storage;
       pa.meta = c->meta;
-      pa.pk = prefix_k_dev;
-      pa.pv = prefix_v_dev;
+      pa.pk = fill ? fill->k : prefix_k_dev;
+      pa.pv = fill ? fill->v : prefix_v_dev;
       pa.prefix_row0 = c->prefix_row0_dev;
       pa.heads = c->H;
       pa.batch = B;
@@ -369,6 +412,27 @@ rswa_status create_cache(const rswa_cache_desc* desc, const void* prefix_k_dev,
       if (e != hipSuccess) {
         release(c);
         return hip_fail(e, "prefix copy launch");
+      }
+      if (fill) {
+        rswa::FillArgs fa{};
+        fa.storage = c->storage;
+        fa.meta = c->meta;
+        fa.k = fill->k;
+        fa.v = fill->v;
+        fa.row0 = c->prefix_row0_dev;
+        fa.steps = c->steps_dev[0];
+        fa.heads = c->H;
+        fa.batch = B;
+        fa.full_causal = c->full() ? 1 : 0;
+        e = rswa::launch_fill_outputs(fa, c->kv_dtype == RSWA_F32, fill_live, st);
+        if (e != hipSuccess) {
+          release(c);
+          return hip_fail(e, "fill launch");
+        }
+        for (int b = 0; b < B; ++b) {
+          c->calls[b] = fill_t[b];
+          if (fill_t[b] != fill_t[0]) c->equal_t = false;
+        }
       }
     }
     // the host metadata buffer must outlive the async copy
@@ -407,6 +471,18 @@ extern "C" {
 rswa_status rswa_cache_create(const rswa_cache_desc* desc, const void* prefix_k_dev,
                               const void* prefix_v_dev, void* stream, rswa_cache** out) {
   return create_cache(desc, prefix_k_dev, prefix_v_dev, nullptr, stream, out);
+}
+
+rswa_status rswa_cache_create_from_prefill(const rswa_cache_desc* desc, const void* k_dev,
+                                           const void* v_dev, const int32_t* cu_seqlens_host,
+                                           void* stream, rswa_cache** out) {
+  if (desc && desc->prefix_paged)
+    return fail(RSWA_E_INVALID, "a cache filled from a prefill holds its prefixes (prefix_paged = 0)");
+  PrefillSource src;
+  src.k = k_dev;
+  src.v = v_dev;
+  src.cu = cu_seqlens_host;
+  return create_cache(desc, nullptr, nullptr, nullptr, stream, out, &src);
 }
 
 rswa_status rswa_cache_create_paged(const rswa_cache_desc* desc, const void* pool_k_dev,
@@ -499,7 +575,7 @@ rswa_status decode_launch(rswa_cache* c, const void* q_dev, const void* k_dev, c
     // every sequence); with equal m and capacity the plan then needs no metadata loads. Captured
     // launches are replayed at later steps, so they always read the device counters.
     a.uni_t = -1;
-    if (c->uniform && !c->masked && !active_dev && !capturing) {
+    if (c->uniform && c->equal_t && !c->masked && !active_dev && !capturing) {
       a.uni_t = (int32_t)c->calls[0];
       a.uni_m = c->plan.prefix[0];
       a.uni_cap = c->plan.cap[0];
