@@ -133,7 +133,10 @@ rswa_status rswa_cache_create_from_prefill(const rswa_cache_desc* desc, const vo
  * (the ring, or the full-causal rows) are per sequence in the cache storage as usual. Entries
  * outside [0, pool_rows) are rejected with RSWA_E_INVALID (checked on the device at creation; the
  * call blocks until the check is done). Decode results equal those of rswa_cache_create with the
- * gathered prefixes, bit for bit. */
+ * gathered prefixes, bit for bit, when both cut the key ranges alike: always while a step's live
+ * rows fit the last-level cache (256 MiB), and under the same rswa_cache_set_decode_split grid.
+ * Beyond it the copying cache streams its rows with fewer workgroups per CU (see
+ * rswa_cache_set_decode_split), and the two agree to float32 summation order. */
 rswa_status rswa_cache_create_paged(const rswa_cache_desc* desc, const void* pool_k_dev,
                                     const void* pool_v_dev, int64_t pool_rows,
                                     const int32_t* prefix_table_dev, void* stream,
@@ -306,8 +309,12 @@ rswa_status rswa_cache_info(const rswa_cache* cache, void** storage_dev,
  * per (b, h) range; a smaller batch has every range cut into k = min(resident workgroups / ranges,
  * rows / 64) >= 2 equal pieces. Otherwise the concatenated key ranges are cut into equal
  * contiguous pieces, one per resident workgroup. A range split over pieces is merged inside the
- * same launch by its last piece to finish. chunk_rows (> 0) sets the fewest rows a piece may hold
- * and grid_blocks (> 0) the number of pieces; either one forces the contiguous-piece layout. 0
+ * same launch by its last piece to finish. A step whose live rows exceed the last-level cache
+ * (256 MiB on MI355X; none of them would still be there at the next step) reads them with
+ * non-temporal loads and counts at most three resident workgroups per CU, unless the cache has a
+ * paged prefix (its shared pool rows are reused). chunk_rows (> 0) sets the fewest rows a piece
+ * may hold and grid_blocks (> 0) the number of pieces; either one forces the contiguous-piece
+ * layout. 0
  * restores the automatic choice. Results depend on these only through float32 summation order.
  * Host only. */
 rswa_status rswa_cache_set_decode_split(rswa_cache* cache, int32_t chunk_rows, int32_t grid_blocks);

@@ -100,7 +100,13 @@ def test_page_table_entry_outside_pool_is_rejected(wa):
 def test_shared_documents_full_size_sampled(wa):
     """Four 20-page documents (m = 5155) decoded by 16 sequences each (B = 64) over a scattered
     token pool, in the launch configuration the benchmark times; sampled steps and sequences
-    against the oracle, and bit-equality with the copied-prefix cache at those steps."""
+    against the oracle.
+
+    At this size the copied-prefix cache reads 2.8 GB per step and streams its rows with three
+    workgroups per CU, while the paged cache (its pool reads need the latency cover) keeps four:
+    their key ranges are cut differently, so in the default launches the two agree to rounding
+    (max-abs 1e-5 on outputs of order 0.05). Given the same grid, both cut the ranges alike and
+    agree bit for bit."""
     wl, pp = W.shared_document_config(seed=1, T=260)
     n = 128
     steps = sample_steps(wl.T, n, int(wl.prefix_len[0]), seed=2, extra=4, crossings=4)
@@ -108,7 +114,14 @@ def test_shared_documents_full_size_sampled(wa):
     ref = Trajectory(wa, wl, wa.MODE_RSWA).run(steps, fused=True, raw=True)
     rng = np.random.default_rng(3)
     for t in steps:
-        assert torch.equal(got[t].view(torch.int32), ref[t].view(torch.int32)), t
+        assert float((got[t] - ref[t]).abs().max()) <= 1e-5, t
         for b in rng.choice(wl.batch, size=3, replace=False):
             err = float(np.abs(got[t][b].cpu().numpy() - oracle_paged(wl, pp, t, b)).max())
             assert err <= TOL, f"t={t} b={b}: {err}"
+    same = []
+    for paged in (pp, None):
+        tr = Trajectory(wa, wl, wa.MODE_RSWA, paged=paged)
+        tr.cache.set_decode_split(0, 1000)
+        same.append(tr.run(steps, fused=True, raw=True))
+    for t in steps:
+        assert torch.equal(same[0][t].view(torch.int32), same[1][t].view(torch.int32)), t

@@ -178,7 +178,38 @@ __device__ __forceinline__ void unpack_v<float>(const u32x4& v, float* f) {
   for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
 }
 
-__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// Global-memory load (the explicit address space keeps it a global load where the pointer has
+// been through readfirstlane, which hides where it points from the compiler).
+typedef const __attribute__((address_space(1))) u32x4* gptr16;
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *(gptr16)p; }
+// Non-temporal loads (cache policy bit `nt`): the lines are not kept in the caches for reuse. A
+// step that reads more than the last-level cache holds finds none of its rows there at the next
+// step anyway, and streaming them avoids evicting what does get reused. They are issued as buffer
+// loads from a resource over one wave's tile (base = the tile's first row, in scalar registers),
+// a different instruction from the plain global load, so the compiler cannot merge the two
+// variants of a tile load into one (merging drops the non-temporal mark).
+constexpr int kCachePolicyNT = 2;            // aux bit of the buffer-load builtin: nt
+constexpr int kBufferRsrcWord3 = 0x00020000; // raw (unformatted) 32-bit data, no swizzle
+// A pointer that is the same in every lane, passed through readfirstlane so that the compiler
+// sees it and keeps it (and what is computed from it) in scalar registers; a buffer resource built
+// from a value it cannot prove uniform makes it wrap every load in a loop over lane values.
+template <typename T>
+__device__ __forceinline__ T* wave_uniform(T* ptr) {
+  const uint64_t p = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(wave_uniform(const_cast<void*>(base)), (short)0, bytes,
+                                           kBufferRsrcWord3);
+}
+struct Plain { static constexpr bool value = false; };
+struct Streamed { static constexpr bool value = true; };
+__device__ __forceinline__ u32x4 ld16_stream(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0,
+                                                                          kCachePolicyNT));
+}
 
 // Device-scope (agent) accesses of the merge workspace: coherent across the XCDs' L2 caches
 // without a cache write-back or invalidate.
@@ -190,6 +221,7 @@ __device__ __forceinline__ float ld_dev(const float* p) {
 }
 // Wait until this thread's stores are complete (device-scope stores: visible to every XCD).
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Combine the np partials of range s stored at workspace slots f + s .. f + s + np - 1 and write
 // the output; threads [0, 128) hold one output dim each. Partial (max, sum) pairs sit at
@@ -423,27 +455,54 @@ __device__ __forceinline__ bool decode_range(const DecodeArgs& a, int b, int h, 
     // Two register sets alternate, and the tile after this wave's last is its last again (the
     // caches hold it), so every load can be issued a tile ahead without a condition.
     const int last = rb + ((r1 - 1 - rb) / STEP) * STEP;
-    auto load = [&](int base, u32x4* kr, u32x4* vr) {
-      const KV* kt = Kh + (int64_t)base * kHeadDim + lane_el;
-      const KV* vt = Vh + (int64_t)base * kHeadDim + lane_el;
+    // Streamed (non-temporal) loads: a buffer resource over the wave's tile of K and of V. The loop
+    // is compiled once per load kind and the launch picks one, so no tile tests the choice.
+    constexpr int RB = kHeadDim * (int)sizeof(KV);  // bytes per row
+    const int lane_b = lane_el * (int)sizeof(KV);
+    // The tile loop addresses rows from scalar bases (the same in every lane).
+    const KV* const Ks = wave_uniform(Kh);
+    const KV* const Vs = wave_uniform(Vh);
+    auto tile_loop = [&](auto kind) {
+      auto load = [&](int base, u32x4* kr, u32x4* vr) {
+        const KV* kt = Ks + (int64_t)base * kHeadDim;
+        const KV* vt = Vs + (int64_t)base * kHeadDim;
+        if constexpr (decltype(kind)::value) {
+          const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kt, U * G * RB);
+          const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(vt, U * G * RB);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        kr[u] = ld16(kt + u * G * kHeadDim);
-        vr[u] = ld16(vt + u * G * kHeadDim);
+          for (int u = 0; u < U; ++u) {
+            kr[u] = ld16_stream(krs, lane_b + u * G * RB);
+            vr[u] = ld16_stream(vrs, lane_b + u * G * RB);
+          }
+          // Wait for these loads (the next tile's) before reducing the current tile: with fewer
+          // requests in flight per wave the streamed step ran 1.9 % faster (57.3 vs 58.4 us for
+          // 346 MB) than with the current tile's loads alone waited for.
+          wait_loads();
+        } else {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            kr[u] = ld16(kt + lane_el + u * G * kHeadDim);
+            vr[u] = ld16(vt + lane_el + u * G * kHeadDim);
+          }
+        }
+      };
+      load(rb, ka, va);
+      for (;;) {
+        load(min(rb + STEP, last), kb, vb);
+        reduce(rb, ka, va);
+        rb += STEP;
+        if (rb > last) break;
+        load(min(rb + STEP, last), ka, va);
+        reduce(rb, kb, vb);
+        rb += STEP;
+        if (rb > last) break;
+        yield_by_progress(done0 + (rb - r0), piece);
       }
     };
-    load(rb, ka, va);
-    for (;;) {
-      load(min(rb + STEP, last), kb, vb);
-      reduce(rb, ka, va);
-      rb += STEP;
-      if (rb > last) break;
-      load(min(rb + STEP, last), ka, va);
-      reduce(rb, kb, vb);
-      rb += STEP;
-      if (rb > last) break;
-      yield_by_progress(done0 + (rb - r0), piece);
-    }
+    if (a.stream_loads)
+      tile_loop(Streamed{});
+    else
+      tile_loop(Plain{});
   }
 
   const int gid = wave * G + g;

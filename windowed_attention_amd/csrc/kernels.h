@@ -57,6 +57,8 @@ struct DecodeArgs {
   int32_t split;            // > 1 (and not aligned): workgroup w takes piece w % split of range
                             // w / split, rows [i L / split, (i + 1) L / split)
   int32_t min_rows;         // stream-K: fewest rows a workgroup takes
+  int32_t stream_loads;     // 1: cache rows are read with non-temporal loads (the step's rows do
+                            // not fit the last-level cache, so keeping them there gains nothing)
   float scale_log2;         // softmax scale * log2(e)
   // Host-known plan: when every sequence has the same m, capacity and step count and no active
   // mask is involved, the host passes them (uni_t >= 0) and the kernel reads no per-sequence

@@ -17,6 +17,9 @@ constexpr int32_t kPlanHeadDim = 128;
 // Bytes after the last row of the storage that the decode kernel may read but never uses: its
 // loads cover whole row tiles, and the last tile of the last range can pass the final row.
 constexpr uint64_t kStorageTailBytes = 4096;
+// MI355X's last-level cache (Infinity Cache, shared by all XCDs): a decode step whose rows exceed
+// it reads them with non-temporal loads.
+constexpr int64_t kLastLevelCacheBytes = 256LL << 20;
 
 struct Plan {
   std::vector<int64_t> seq_off;   // element offset of sequence b's K block
