@@ -360,6 +360,29 @@ def test_cfg_ragged_sampled(wa):
     tr.cache.close()
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("dtype,batch,m", [("f32", 4, 5155), ("bf16", 32, 1100)])
+def test_streamed_steps_sampled(wa, dtype, batch, m):
+    """Steps whose live rows exceed the 256 MiB last-level cache read them with non-temporal
+    loads over three workgroups per CU: float32 rows in the split layout (4 sequences, 338-346 MB
+    per step) and bf16 rows in the aligned layout (512 ranges, 289-297 MB), against the oracle at
+    sampled steps, ring wrap included."""
+    n, T = 128, 140
+    wl = W.make_decode(f"streamed-{dtype}", 87, dtype, [m] * batch, [n] * batch, [T] * batch,
+                       seed=27)
+    tr = Trajectory(wa, wl, wa.MODE_RSWA)
+    ranges = batch * 16
+    grid, launches = tr.cache.decode_plan(appending=True)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if ranges <= 3 * cus:  # the streamed plan: at most three resident workgroups per CU
+        k = min(3 * cus // ranges, (m + 1) // 64)
+        assert (grid, launches) == ((ranges, 1) if 2 * ranges >= 3 * cus else (ranges * k, 1))
+    got = tr.run([1, 2, 64, 128, 129, 140], fused=True)
+    worst = check_steps(wl, 0, got, seqs_per_step=3)
+    print(f"streamed {dtype}: worst max-abs error {worst:.3e}")
+    tr.cache.close()
+
+
 # ---------------------------------------------------------------------------------------------
 # the comparison modes of the pages: vanilla sliding window and sink tokens
 # ---------------------------------------------------------------------------------------------
