@@ -138,7 +138,7 @@ def append_bytes(wl, t: int) -> int:
 
 
 def run_decode(args, wl, mode_full: bool, steps: int, warmup: int, kernel_events: bool = False,
-               paged=None, setup: int = 0, block: int = 64):
+               paged=None, setup: int = 0, block: int = 64, series_block: int = 0):
     """Run decode steps t = 1 .. setup + warmup + steps of one workload through the C ABI.
 
     Steps 1 .. setup build the cache state (the ring fills, the full-causal cache grows); they are
@@ -146,7 +146,8 @@ def run_decode(args, wl, mode_full: bool, steps: int, warmup: int, kernel_events
     curve. After a synchronization, `warmup` untimed steps, another synchronization, then the
     `steps` timed steps between two events (nothing recorded in between) and a synchronization.
     `paged` (workloads.PagedPrefix): the cache reads the prefixes from the shared token pool
-    through the page table instead of holding copies."""
+    through the page table instead of holding copies. `series_block` > 0 also records an event
+    every that many timed steps (a per-block latency series of the timed region)."""
     import torch
     import windowed_attention_amd as wa
     lib = wa._lib
@@ -232,8 +233,12 @@ def run_decode(args, wl, mode_full: bool, steps: int, warmup: int, kernel_events
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev_ser = []
     start.record()
     for i in range(steps):
+        if series_block and i % series_block == 0 and i:
+            ev_ser.append((i, torch.cuda.Event(enable_timing=True)))
+            ev_ser[-1][1].record()
         o, a = step(t_first + i)
         if kernel_events:
             ev_k[i][0].record()
@@ -249,6 +254,11 @@ def run_decode(args, wl, mode_full: bool, steps: int, warmup: int, kernel_events
     cache.close()
 
     kern_ms = np.array([a.elapsed_time(b) for a, b in ev_k]) if kernel_events else None
+    series = []
+    if ev_ser:
+        marks = [(0, start)] + ev_ser + [(steps, end)]
+        for (i0, e0), (i1, e1) in zip(marks[:-1], marks[1:]):
+            series.append((t_first + i0, t_first + i1 - 1, e0.elapsed_time(e1) * 1e3 / (i1 - i0)))
     if steps:
         lat.append((t_first + steps // 2, elapsed_ms * 1e3 / steps))
     out_elem = out.element_size()
@@ -262,7 +272,7 @@ def run_decode(args, wl, mode_full: bool, steps: int, warmup: int, kernel_events
                 dec_bytes=dec_bytes, app_bytes=app_bytes, launch_bytes=launch_bytes,
                 tokens=tokens, fused=fused, steps_done=steps_done.tolist(),
                 launches_per_step=launches, grid_blocks=grid_blocks,
-                timed_t=[t_first, t_first + steps - 1])
+                timed_t=[t_first, t_first + steps - 1], series=series)
 
 
 def flatness(lat, n, T):
@@ -448,6 +458,24 @@ def visible_pairs(S: int, m: int, n: int, prefix_causal: bool = False) -> int:
     return pre + outs * m + win
 
 
+def tile_issued_pairs(S: int, m: int, n: int, prefix_causal: bool = False, bm: int = 256,
+                      bn: int = 64) -> int:
+    """(query, key) pairs the prefill kernel's MFMAs compute for one sequence and head: every
+    workgroup of bm queries visits the bn-key tiles over the prefix [0, m) (over [0, q_end) for a
+    causal prefix tile that ends inside it) and over the window [max(m, max(q0, m) - n + 1),
+    q_end), all bm x bn pairs of each, masked ones included."""
+    pairs = 0
+    for q0 in range(0, S, bm):
+        q1 = min(q0 + bm, S)
+        pre_end = q1 if (prefix_causal and q1 <= m) else m
+        tiles = (pre_end + bn - 1) // bn
+        if q1 > m:
+            ws = max(m, max(q0, m) - n + 1)
+            tiles += (q1 - ws + bn - 1) // bn
+        pairs += bm * bn * tiles
+    return pairs
+
+
 def run_prefill(args):
     import torch
     import windowed_attention_amd as wa
@@ -478,9 +506,13 @@ def run_prefill(args):
         times.append(a.elapsed_time(b))
     med_ms = float(np.median(times))
     pairs = visible_pairs(S, int(pw.prefix_len[0]), int(pw.window[0]))
+    issued = tile_issued_pairs(S, int(pw.prefix_len[0]), int(pw.window[0]))
     flops = 4.0 * D * H * pairs
     tflops = flops / (med_ms * 1e-3) / 1e12
-    return dict(workload=pw.name, ms=med_ms, tflops=tflops, flop=flops, visible_pairs_per_head=pairs,
+    return dict(workload=pw.name, ms=med_ms, runs=args.prefill_runs, warmup_runs=3,
+                tflops=tflops, flop=flops, visible_pairs_per_head=pairs,
+                tile_issued_flop=4.0 * D * H * issued, tile_issued_over_algorithmic=issued / pairs,
+                exp_count=H * pairs,
                 roofline=dict(bound="mfma", achieved=tflops, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                               frac=tflops / PEAK_BF16_TFLOPS,
                               traffic=traffic_from_profile("prefill",
@@ -697,12 +729,24 @@ def ragged_decode(args, steps=3000):
     wl = decode_workload("ragged")
     a = types.SimpleNamespace(chunk=args.chunk, grid=args.grid, unfused=args.unfused)
     warm = 300
-    r = run_decode(a, wl, False, steps, warm, False)
+    r = run_decode(a, wl, False, steps, warm, False, series_block=250)
     ms = r["elapsed_ms"] / steps
     gbs = float((r["dec_bytes"] + r["app_bytes"]).mean()) / (ms * 1e-3) / 1e9
+    # per block of 250 timed steps: first t, last t, us/step, sequences still decoding at the
+    # block's middle step, GB/s over the block's algorithmic bytes
+    byts = r["dec_bytes"] + r["app_bytes"]
+    t0 = r["timed_t"][0]
+    vs_t = []
+    for lo, hi, us in r["series"]:
+        mid = (lo + hi) // 2
+        active = int((wl.steps >= mid).sum())
+        blk_gbs = float(byts[lo - t0:hi - t0 + 1].mean()) / (us * 1e-6) / 1e9
+        vs_t.append([lo, hi, round(us, 2), active, round(blk_gbs)])
     return dict(workload=wl.name, steps=steps, timed_t=[warm + 1, warm + steps],
                 tok_s=r["tokens"] / (r["elapsed_ms"] * 1e-3), us_per_step=ms * 1e3,
-                step_gbs=gbs, frac=gbs / PEAK_HBM_GBS, launches_per_step=r["launches_per_step"])
+                step_gbs=gbs, frac=gbs / PEAK_HBM_GBS, launches_per_step=r["launches_per_step"],
+                vs_t=vs_t, vs_t_columns=["t_first", "t_last", "us_per_step", "active_sequences",
+                                         "gbs"])
 
 
 def main():
