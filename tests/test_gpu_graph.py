@@ -97,6 +97,27 @@ def test_replays_equal_eager_steps_split_layout(wa):
         assert float(np.abs(got[t][b].cpu().numpy() - o).max()) <= 1e-2
 
 
+@pytest.mark.slow
+def test_replays_equal_eager_steps_streamed(wa):
+    """Eight sequences of 5155 prefix rows (338-340 MB per step, beyond the last-level cache): eager
+    and captured steps both stream the rows (non-temporal loads, three workgroups per CU) in the
+    split layout; replays must match eager steps bit for bit, and the oracle."""
+    B, T, G = 8, 48, 8
+    wl = W.make_decode("graph-streamed", 10, "bf16", [5155] * B, [32] * B, [T] * B, seed=16)
+    ref = eager(wa, wl, T, wa.MODE_RSWA)
+    got, steps = replayed(wa, wl, T, G, wa.MODE_RSWA)
+    np.testing.assert_array_equal(steps, T)
+    for t in range(1, T + 1):
+        assert torch.equal(got[t].view(torch.int32), ref[t].view(torch.int32)), t
+    for t in (1, 33, 48):
+        b = t % wl.batch
+        pk, pv = wl.prefix(b)
+        o, _ = O.decode_step(to_f64(wl.q[t - 1, b], "bf16"), to_f64(pk, "bf16"),
+                             to_f64(pv, "bf16"), to_f64(wl.k[:t, b], "bf16"),
+                             to_f64(wl.v[:t, b], "bf16"), t, 32)
+        assert float(np.abs(got[t][b].cpu().numpy() - o).max()) <= 1e-2
+
+
 def test_replays_bf16_output_and_full_causal_capacity(wa):
     wl = W.make_decode("graph-full", 10, "bf16", [40, 40], [8, 8], [20, 20], seed=12)
     ref = eager(wa, wl, 20, wa.MODE_FULL_CAUSAL, split=(0, 16), out_dtype=torch.bfloat16)
