@@ -618,9 +618,9 @@ __device__ __forceinline__ void dma_ktile(uint16_t* sk, uint16_t* sv, const uint
 
 template <typename OUT>
 __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
-  // three buffer pairs: the DMA for tile j + 2 runs while tile j is computed
-  __shared__ __attribute__((aligned(16))) uint16_t sK[3 * K_TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[3 * K_TILE];
+  // four buffer pairs: the DMA for tile j + 3 runs while tile j is computed
+  __shared__ __attribute__((aligned(16))) uint16_t sK[4 * K_TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[4 * K_TILE];
 
   // XCD-aware tile order (as in the forward): workgroup i runs on XCD i % 8, so each XCD takes a
   // contiguous run of (query tile, head) pairs and one head's K / V tiles stay in its L2.
@@ -697,18 +697,20 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
   for (int db = 0; db < 4; ++db) zero16(dq[db]);
   const SwzLane sl_(lane);
 
-  // copy tile j into buffer pair b (= j % 3)
+  // copy tile j into buffer pair b (= j % 4)
   auto issue_to = [&](int j, int b) {
     dma_ktile(sK + b * K_TILE, sV + b * K_TILE, kbase, vbase, rs, tstart(j), S - 1, wave, lane);
   };
-  auto issue = [&](int j) { issue_to(j, j % 3); };
+  auto issue = [&](int j) { issue_to(j, j % 4); };
   issue(0);
-  if (ntiles > 1) {
-    issue(1);
+  if (ntiles > 1) issue(1);
+  if (ntiles > 2) issue(2);
+  if (ntiles > 2)
+    dma_wait_barrier<2 * kDqPieces>();
+  else if (ntiles > 1)
     dma_wait_barrier<kDqPieces>();
-  } else {
+  else
     dma_wait_barrier<0>();
-  }
 
   // One 32-key block of the tile in LDS buffers (sk, sv): S^T = K Q^T and dP^T = V dO^T (keys in
   // accumulator rows, this lane's query in the column), dS^T in registers, dQ^T += K^T dS^T.
@@ -765,32 +767,32 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
   // causal prefix) run a loop without mask tests or end-of-loop cases.
   int n_plain = min(m / BN, n_pre);
   if (pc && q0 < m) n_plain = min(n_plain, (q0 + 1) / BN);
-  const int j_plain = min(n_plain, ntiles - 2);
+  const int j_plain = min(n_plain, ntiles - 3);
   int j = 0;
-  // three tiles per iteration, so that every LDS buffer offset is a constant
-  for (; j + 3 <= j_plain; j += 3) {
+  // four tiles per iteration, so that every LDS buffer offset is a constant
+  for (; j + 4 <= j_plain; j += 4) {
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      issue_to(j + u + 2, (u + 2) % 3);
+    for (int u = 0; u < 4; ++u) {
+      issue_to(j + u + 3, (u + 3) % 4);
       const uint16_t* sk = sK + u * K_TILE;
       const uint16_t* sv = sV + u * K_TILE;
       kblock(sk, sv, 0, 0, 0, 0, false);
       kblock(sk, sv, 1, 0, 0, 0, false);
-      dma_wait_barrier<kDqPieces>();
+      dma_wait_barrier<2 * kDqPieces>();
     }
   }
   for (; j < j_plain; ++j) {
-    const int buf = j % 3;
-    issue(j + 2);
+    const int buf = j % 4;
+    issue(j + 3);
     const uint16_t* sk = sK + buf * K_TILE;
     const uint16_t* sv = sV + buf * K_TILE;
     kblock(sk, sv, 0, 0, 0, 0, false);
     kblock(sk, sv, 1, 0, 0, 0, false);
-    dma_wait_barrier<kDqPieces>();
+    dma_wait_barrier<2 * kDqPieces>();
   }
   for (; j < ntiles; ++j) {
-    const int buf = j % 3;
-    if (j + 2 < ntiles) issue(j + 2);
+    const int buf = j % 4;
+    if (j + 3 < ntiles) issue(j + 3);
     const uint16_t* sk = sK + buf * K_TILE;
     const uint16_t* sv = sV + buf * K_TILE;
     const int k0 = tstart(j);
@@ -801,7 +803,9 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdArgs a) {
     const bool masked = is_pre ? (k0 + BN > m || (pc && q0 < m && k0 + BN - 1 > q0)) : true;
     kblock(sk, sv, 0, k0, lo, hi, masked);
     kblock(sk, sv, 1, k0, lo, hi, masked);
-    if (j + 2 < ntiles)
+    if (j + 3 < ntiles)
+      dma_wait_barrier<2 * kDqPieces>();
+    else if (j + 2 < ntiles)
       dma_wait_barrier<kDqPieces>();
     else
       dma_wait_barrier<0>();
