@@ -105,6 +105,33 @@ def test_fill_unequal_outputs(wa, dtype, full):
     run_case(wa, wl, fill, wa.MODE_FULL_CAUSAL if full else wa.MODE_RSWA)
 
 
+def test_fill_into_library_storage(wa):
+    """The same fill with storage the library allocates: counters and every later decode step
+    equal those of the appended cache, and the query hook reports the same layout."""
+    m, n, fill = [64, 0, 200], [16, 8, 32], [40, 9, 77]
+    wl = W.make_decode("fill-lib", 9, "bf16", m, n, np.asarray(fill) + 6, seed=13)
+    k_all, v_all, cu = packed_batch(wl, fill)
+    a = wa.rswa_cache_create_from_prefill(upload(k_all, "bf16"), upload(v_all, "bf16"), cu,
+                                          wl.prefix_len, wl.window, kv_dtype=torch.bfloat16)
+    b = wa.rswa_cache_create(upload(wl.prefix_k, "bf16"), upload(wl.prefix_v, "bf16"),
+                             wl.prefix_len, wl.window, kv_dtype=torch.bfloat16)
+    for s_ in range(max(fill)):
+        act = torch.from_numpy((np.asarray(fill) > s_).astype(np.uint8)).cuda()
+        b.append(upload(wl.k[s_], "bf16"), upload(wl.v[s_], "bf16"), active=act)
+    _, ka, va, ra, sa = a.query()
+    _, kb, vb, rb, sb = b.query()
+    np.testing.assert_array_equal(ka, kb)
+    np.testing.assert_array_equal(va, vb)
+    np.testing.assert_array_equal(ra, rb)
+    np.testing.assert_array_equal(sa, fill)
+    np.testing.assert_array_equal(sb, fill)
+    for s_ in range(6):
+        q, k, v = next_inputs(wl, fill, s_)
+        assert torch.equal(a.step(q, k, v).view(torch.int32), b.step(q, k, v).view(torch.int32))
+    a.close()
+    b.close()
+
+
 @pytest.mark.parametrize("full", [False, True])
 def test_fill_equal_outputs(wa, full):
     # equal m, n and t: decode after the fill takes the host-known plan (split pieces per range)
