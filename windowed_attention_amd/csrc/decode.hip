@@ -39,6 +39,12 @@
 // q.k partial dot products are summed across the group with DPP row operations. At the end of a
 // range the group states are merged through LDS.
 //
+// Streamed steps. When a step's live rows exceed the last-level cache (the host decides from the
+// row counts; paged caches excepted), none of them is still cached at the next step, so a second
+// copy of the tile loop reads them with non-temporal loads, two tiles a round, both waited for
+// before both are reduced (fewer requests in flight per wave), and the host plans such a step over
+// three workgroups per CU instead of four.
+//
 // Fused append (K1 inside K2). When the launch carries the new k/v rows, the new row's slot
 // r = m_b + (t_b mod n_b) (or m_b + t_b) is part of the live range after the append; the lane group
 // that meets this row in its piece takes k/v from the input instead of the cache and writes them
