@@ -23,6 +23,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import hashlib
+import re
 import json
 import os
 import sys
@@ -57,10 +58,18 @@ def log(*a):
 
 
 def source_hash(paths) -> str:
+    """Hash of the sources a kernel is compiled from, comments and blank space left out, so that a
+    traffic record stays valid across edits that do not change the code."""
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            text = f.read()
+        if p.endswith(".py"):
+            text = re.sub(r"#[^\n]*", "", text)
+        else:
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", "", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -42,3 +42,14 @@ def test_flatness_of_a_flat_and_a_growing_series():
     assert bench.flatness(lat, 128, 20000) == pytest.approx(1.0)
     grow = [(t, 50.0 + t * 1e-3) for t in range(1, 20001, 64)]
     assert bench.flatness(grow, 128, 20000) > 1.2
+
+
+def test_source_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    src = tmp_path / "k.hip"
+    src.write_text("// header\nint f(int x) { return x + 1; }  /* note */\n")
+    h0 = bench.source_hash(["k.hip"])
+    src.write_text("// another header\n\nint f(int x) {\n  return x + 1;  // same code\n}\n")
+    assert bench.source_hash(["k.hip"]) == h0
+    src.write_text("int f(int x) { return x + 2; }\n")
+    assert bench.source_hash(["k.hip"]) != h0
