@@ -111,7 +111,8 @@ rswa_status rswa_cache_create(const rswa_cache_desc* desc, const void* prefix_k_
  * last min(n_b, t_b) outputs in their ring slots (output j in row m_b + (j mod n_b); the cache
  * holds the prefix plus the previous n outputs: deep dive "Unlimited-OCR", N(t) code block); in
  * FULL_CAUSAL mode all t_b outputs in rows m_b + j; step counter t_b. Rows beyond those are not
- * touched. k_dev / v_dev: packed token-major [total][H][D] of kv_dtype, 16-byte aligned;
+ * touched. k_dev / v_dev: packed token-major [total][H][D] of kv_dtype, 16-byte aligned, holding
+ * at least cu_seqlens_host[batch] rows (the call has no size to check this against);
  * cu_seqlens_host: host [batch + 1], cu_seqlens_host[0] >= 0, S_b >= m_b. desc->prefix_paged
  * must be 0. Enqueued on `stream`; the call returns once that stream has finished the copies.
  * Errors as rswa_cache_create, plus RSWA_E_INVALID (cu_seqlens, a segment shorter than its

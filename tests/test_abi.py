@@ -210,6 +210,15 @@ def test_prefill_fill_checks_arguments_before_device_work(wa):
     assert b"max_steps" in lib.rswa_last_error()
 
 
+def test_prefill_fill_binding_checks_the_row_count(wa):
+    # the C call cannot see the size of k / v; the binding checks cu_seqlens against it first
+    k = torch.zeros((10, 16, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="holds 10 rows"):
+        wa.rswa_cache_create_from_prefill(k, k, [0, 6, 11], [4, 2], [8, 8])
+    with pytest.raises(ValueError, match="3 entries"):
+        wa.rswa_cache_create_from_prefill(k, k, [0, 6], [4, 2], [8, 8])
+
+
 def test_step_graph_arguments_are_checked_before_device_work(wa):
     lib = wa._lib
     null, one = ctypes.c_void_p(None), ctypes.c_void_p(16)

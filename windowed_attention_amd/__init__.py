@@ -227,6 +227,9 @@ class RswaCache:
             if cu.size != m.size + 1:
                 raise ValueError(f"cu_seqlens must have {m.size + 1} entries")
             total = int(prefill_k.shape[0])
+            if cu.size and int(cu[-1]) > total:
+                raise ValueError(f"cu_seqlens ends at row {int(cu[-1])} but prefill_k holds "
+                                 f"{total} rows")
             shape = (total, num_heads, head_dim)
             _check(_lib.rswa_cache_create_from_prefill(
                 ctypes.byref(d), _dev(prefill_k, "prefill_k", kv_dtype, shape),
