@@ -186,7 +186,9 @@ rswa_status rswa_decode_step(rswa_cache* cache, const void* q_dev, const void* k
  * output token sees only its previous n output tokens (GeekNews "Unlimited OCR", R-SWA section;
  * deep dive "Unlimited-OCR", N(t) code block), over multi-page documents packed into 32K-token
  * sequences (GeekNews "Unlimited OCR", training section).
- * Sequence s occupies token rows [cu_seqlens[s], cu_seqlens[s+1]) of q/k/v/out, its first
+ * Sequence s occupies token rows [cu_seqlens[s], cu_seqlens[s+1]) of q/k/v/out (which must hold
+ * cu_seqlens[nseq] rows: no row count is passed, so neither the host nor the kernels can check
+ * it), its first
  * m_s = prefix_len[s] tokens being the prefix. Query p (position within the sequence) sees key k
  * iff   k < m_s  and (prefix_causal == 0 or p >= m_s or k <= p)          (the reference prefix)
  *    or m_s <= k <= p and p - k < n_s                                   (its own output window)

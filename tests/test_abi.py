@@ -219,6 +219,16 @@ def test_prefill_fill_binding_checks_the_row_count(wa):
         wa.rswa_cache_create_from_prefill(k, k, [0, 6], [4, 2], [8, 8])
 
 
+def test_prefill_binding_checks_sequences_fit_the_rows(wa):
+    q = torch.zeros((10, 16, 128), dtype=torch.bfloat16)
+    cu = torch.tensor([0, 6, 12], dtype=torch.int32)
+    m = torch.tensor([2, 2], dtype=torch.int32)
+    n = torch.tensor([4, 4], dtype=torch.int32)
+    for fn in (wa.rswa_prefill_attn, wa.rswa_prefill_fwd):
+        with pytest.raises(ValueError, match="hold 10 rows"):
+            fn(q, q, q, cu, m, n)
+
+
 def test_step_graph_arguments_are_checked_before_device_work(wa):
     lib = wa._lib
     null, one = ctypes.c_void_p(None), ctypes.c_void_p(16)

@@ -409,12 +409,11 @@ def rswa_prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seql
                       stream=None) -> torch.Tensor:
     """R-SWA-masked attention over packed sequences; q/k/v [total][H][D] bf16 on the device,
     cu_seqlens / prefix_len / window int32 device tensors. max_seqlen defaults to the largest
-    sequence (computed on the host from cu_seqlens, which costs a device sync)."""
+    sequence (computed on the host from cu_seqlens, which costs a device sync; the sequences are
+    then also checked to fit the rows of q)."""
     total, H, D = q.shape
     nseq = prefix_len.numel()
-    if max_seqlen is None:
-        cs = cu_seqlens.cpu().numpy()
-        max_seqlen = int(np.diff(cs).max()) if cs.size > 1 else 0
+    max_seqlen = _max_seqlen(cu_seqlens, max_seqlen, total)
     if out is None:
         out = torch.empty((total, H, D), dtype=out_dtype, device=q.device)
     shape = (total, H, D)
@@ -466,10 +465,15 @@ class StepGraph:
             pass
 
 
-def _max_seqlen(cu_seqlens: torch.Tensor, max_seqlen: int | None) -> int:
+def _max_seqlen(cu_seqlens: torch.Tensor, max_seqlen: int | None, total: int) -> int:
+    """max_seqlen as given, else the longest sequence of cu_seqlens (a host copy, which costs a
+    device sync); with that copy also checks that the sequences fit the `total` rows of q/k/v,
+    which the kernels cannot check."""
     if max_seqlen is not None:
         return int(max_seqlen)
     cs = cu_seqlens.cpu().numpy()
+    if cs.size and int(cs[-1]) > total:
+        raise ValueError(f"cu_seqlens ends at row {int(cs[-1])} but q/k/v hold {total} rows")
     return int(np.diff(cs).max()) if cs.size > 1 else 0
 
 
@@ -481,7 +485,7 @@ def rswa_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqle
     Returns (out [total][H][D], lse [total][H] float32)."""
     total, H, D = q.shape
     nseq = prefix_len.numel()
-    max_seqlen = _max_seqlen(cu_seqlens, max_seqlen)
+    max_seqlen = _max_seqlen(cu_seqlens, max_seqlen, total)
     if out is None:
         out = torch.empty((total, H, D), dtype=out_dtype, device=q.device)
     if lse is None:
@@ -508,7 +512,7 @@ def rswa_prefill_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: tor
     from rswa_prefill_fwd. `work` ([2][H][total] float32) is a work array, allocated if absent."""
     total, H, D = q.shape
     nseq = prefix_len.numel()
-    max_seqlen = _max_seqlen(cu_seqlens, max_seqlen)
+    max_seqlen = _max_seqlen(cu_seqlens, max_seqlen, total)
     shape = (total, H, D)
     mk = lambda t: torch.empty(shape, dtype=grad_dtype, device=q.device) if t is None else t
     dq, dk, dv = mk(dq), mk(dk), mk(dv)
