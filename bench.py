@@ -720,10 +720,12 @@ def steady_leg(args, name: str, steps: int, warmup: int):
     wl = decode_workload(name)
     a = types.SimpleNamespace(chunk=args.chunk, grid=args.grid, unfused=args.unfused)
     setup = int(wl.T) - steps - warmup
-    r = run_decode(a, wl, False, steps, warmup, setup=setup)
+    r = run_decode(a, wl, False, steps, warmup, setup=setup, series_block=250)
     ms = r["elapsed_ms"] / steps
     gbs = float((r["dec_bytes"] + r["app_bytes"]).mean()) / (ms * 1e-3) / 1e9
     lat = r["lat"]
+    if r["series"]:  # the timed steps by blocks instead of one point at their middle
+        lat = lat[:-1] + [((lo + hi) // 2, us) for lo, hi, us in r["series"]]
     keep = np.linspace(0, len(lat) - 1, min(len(lat), 24)).round().astype(int)
     return dict(workload=wl.name, timed_t=r["timed_t"], steps=steps,
                 tok_s=r["tokens"] / (r["elapsed_ms"] * 1e-3), us_per_step=ms * 1e3,
