@@ -337,7 +337,9 @@ rswa_status rswa_cache_destroy(rswa_cache* cache);
 /* Inspection of a live cache in one call (for tests and snapshots): the storage base pointer and,
  * per sequence b, the element offsets of its K block and V block (K[b][h][r][i] at
  * k_offset[b] + (h * R_b + r) * D + i, V likewise from v_offset[b]), R_b, and the step counters
- * t_b. Layout outputs are host-only; when steps_host is not NULL the call BLOCKS until `stream`
+ * t_b. In a paged cache the storage holds output rows only: storage row r is cache row m_b + r
+ * (R_b = n_b or max_steps_b), the prefix rows being in the caller's pool. Layout outputs are
+ * host-only; when steps_host is not NULL the call BLOCKS until `stream`
  * has passed all prior work and returns RSWA_E_CAPACITY as rswa_cache_steps() does. Any output
  * pointer may be NULL. */
 rswa_status rswa_cache_query(rswa_cache* cache, void** storage_dev,
