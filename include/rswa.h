@@ -276,8 +276,12 @@ rswa_status rswa_prefill_bwd_noalloc(const void* q_dev, const void* k_dev, const
  * The caller fills the input slots before each replay. steps must be even (the step counters are
  * double-buffered, so an even count returns them to the same parity) and at most 4096. The work
  * split of each step is fixed at capture; the kernels still derive every row range from the
- * device-side step counters, so replays at any later step are correct. Capture uses a private
- * stream and enqueues nothing; the graph may be launched on any stream of the cache's device.
+ * device-side step counters, so replays at any later step are correct. When all sequences share
+ * m, capacity and step count and no active mask has been used, a second copy of the steps is
+ * captured that reads the one shared count (steps_in[0]) instead of every sequence's and then
+ * follows the plan an eager step takes (no work table); a replay uses it while that still holds,
+ * the general copy after an active mask. Capture uses a private stream and enqueues nothing; the
+ * graph may be launched on any stream of the cache's device.
  * Errors: RSWA_E_INVALID, RSWA_E_HIP (capture or instantiation), RSWA_E_INTERNAL. */
 typedef struct rswa_step_graph rswa_step_graph; /* opaque; owned by the library */
 rswa_status rswa_step_graph_create(rswa_cache* cache, int32_t steps, const void* q_slots_dev,

@@ -118,6 +118,50 @@ def test_replays_equal_eager_steps_streamed(wa):
         assert float(np.abs(got[t][b].cpu().numpy() - o).max()) <= 1e-2
 
 
+def test_replays_switch_to_per_sequence_counts_after_a_masked_step(wa):
+    """A cache whose sequences share their step count gets a graph copy that reads the one shared
+    count; after an eager step with an active mask the counts differ, and later replays must take
+    the copy that reads every sequence's counter. Launch by launch (same inputs, same fixed grid)
+    the outputs and counters equal those of eager steps."""
+    B, G = 4, 2
+    wl = W.make_decode("graph-masked", 10, "bf16", [100] * B, [32] * B, [12] * B, seed=17)
+    tr_ref = Trajectory(wa, wl, wa.MODE_RSWA)
+    tr = Trajectory(wa, wl, wa.MODE_RSWA)
+    for t_ in (tr_ref, tr):
+        t_.cache.set_decode_split(0, 64)
+    g = wa.StepGraph(tr.cache, G)
+    mask = torch.tensor([1, 0, 1, 0], dtype=torch.uint8, device="cuda")
+    plan = ["g", "g", "m", "g", "g"]  # replays of G launches, one masked eager launch
+    out = torch.empty((B, 16, 128), dtype=torch.float32, device="cuda")
+    launch = 0
+    for kind in plan:
+        n = G if kind == "g" else 1
+        q, k, v = tr.q[launch:launch + n], tr.k[launch:launch + n], tr.v[launch:launch + n]
+        refs = []
+        for i in range(n):  # the eager reference of the same launches
+            act = mask if kind == "m" else None
+            refs.append(tr_ref.cache.step(q[i], k[i], v[i], out.clone(), active=act).clone())
+        if kind == "g":
+            g.q.copy_(q)
+            g.k.copy_(k)
+            g.v.copy_(v)
+            g.launch()
+            got = [g.out[i].clone() for i in range(n)]
+        else:
+            got = [tr.cache.step(q[0], k[0], v[0], out.clone(), active=mask).clone()]
+        torch.cuda.synchronize()
+        for i in range(n):
+            act = mask.bool() if kind == "m" else torch.ones(B, dtype=torch.bool, device="cuda")
+            assert torch.equal(got[i][act].view(torch.int32), refs[i][act].view(torch.int32)), \
+                (kind, launch + i)
+        launch += n
+    np.testing.assert_array_equal(tr.cache.steps(), tr_ref.cache.steps())
+    np.testing.assert_array_equal(tr.cache.steps(), [9, 8, 9, 8])
+    g.close()
+    tr.cache.close()
+    tr_ref.cache.close()
+
+
 def test_replays_bf16_output_and_full_causal_capacity(wa):
     wl = W.make_decode("graph-full", 10, "bf16", [40, 40], [8, 8], [20, 20], seed=12)
     ref = eager(wa, wl, 20, wa.MODE_FULL_CAUSAL, split=(0, 16), out_dtype=torch.bfloat16)

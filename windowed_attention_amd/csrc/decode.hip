@@ -572,6 +572,9 @@ __device__ __forceinline__ bool decode_range(const DecodeArgs& a, int b, int h, 
 
 template <typename KV, typename OUT, int U>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+  // A captured step over sequences that share their step count reads it from the counters: the
+  // rest of the launch is the host-known plan's.
+  if (a.uni_t == kUniFromCounters) a.uni_t = __builtin_amdgcn_readfirstlane(a.steps_in[0]);
   extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
   __shared__ float s_m[kMaxGroups], s_l[kMaxGroups];
   __shared__ float s_acc[kMaxGroups * kHeadDim];

@@ -36,6 +36,8 @@ struct AppendArgs {
   int32_t full_causal;
 };
 
+constexpr int32_t kUniFromCounters = -2;
+
 struct DecodeArgs {
   void* storage;
   CacheMeta meta;
@@ -62,7 +64,9 @@ struct DecodeArgs {
   float scale_log2;         // softmax scale * log2(e)
   // Host-known plan: when every sequence has the same m, capacity and step count and no active
   // mask is involved, the host passes them (uni_t >= 0) and the kernel reads no per-sequence
-  // metadata; uni_t < 0: everything comes from the device arrays (graph replays, masks, ragged).
+  // metadata. uni_t = kUniFromCounters: the same, but the shared step count is read from
+  // steps_in[0] on the device (captured steps, replayed at later counts). Otherwise (-1)
+  // everything comes from the device arrays (masks, ragged, unequal counts).
   int32_t uni_t;            // t_b before this launch
   int32_t uni_m;            // m_b
   int32_t uni_cap;          // cap_b

@@ -554,10 +554,15 @@ rswa_status rswa_append_kv(rswa_cache* c, const void* k_dev, const void* v_dev,
 namespace {
 
 // Shared body of rswa_decode_attn (k_dev == NULL) and rswa_decode_step (append fused in).
+// How a decode launch is enqueued: eagerly, or into a step graph that reads every sequence's
+// counter, or into one that reads the step count all sequences share.
+constexpr int kEager = 0, kCaptureGeneral = 1, kCaptureUniform = 2;
+
 rswa_status decode_launch(rswa_cache* c, const void* q_dev, const void* k_dev, const void* v_dev,
                           void* out_dev, int32_t out_dtype, float softmax_scale,
                           const uint8_t* active_dev, void* stream, const char* what,
-                          bool capturing = false) {
+                          int capture = kEager) {
+  const bool capturing = capture != kEager;
   if (!c) return fail(RSWA_E_INVALID, "cache is NULL");
   if (!q_dev || !out_dev) return fail(RSWA_E_INVALID, "q_dev / out_dev is NULL");
   if (out_dtype != RSWA_BF16 && out_dtype != RSWA_F32)
@@ -594,10 +599,12 @@ rswa_status decode_launch(rswa_cache* c, const void* q_dev, const void* k_dev, c
     a.ws_cnt = c->ws_cnt;
     // The host knows every t_b exactly while no active mask has been used (each call appends to
     // every sequence); with equal m and capacity the plan then needs no metadata loads. Captured
-    // launches are replayed at later steps, so they always read the device counters.
+    // launches are replayed at later steps, so they read the step counts from the device: the
+    // shared one (kUniFromCounters) when the graph is captured for a cache in that state, else
+    // every sequence's.
     a.uni_t = -1;
-    if (c->uniform && c->equal_t && !c->masked && !active_dev && !capturing) {
-      a.uni_t = (int32_t)c->calls[0];
+    if (c->uniform && c->equal_t && !c->masked && !active_dev && capture != kCaptureGeneral) {
+      a.uni_t = capture == kCaptureUniform ? rswa::kUniFromCounters : (int32_t)c->calls[0];
       a.uni_m = c->plan.prefix[0];
       a.uni_cap = c->plan.cap[0];
       a.uni_rows = c->plan.rows[0];
@@ -646,8 +653,10 @@ rswa_status rswa_decode_step(rswa_cache* c, const void* q_dev, const void* k_dev
 
 struct rswa_step_graph {
   rswa_cache* c = nullptr;
-  hipGraph_t graph = nullptr;
+  hipGraph_t graph = nullptr;      // steps that read every sequence's counter
   hipGraphExec_t exec = nullptr;
+  hipGraph_t graph_uni = nullptr;  // the same steps reading the one count all sequences share
+  hipGraphExec_t exec_uni = nullptr;  // (captured when the cache was in that state)
   int32_t steps = 0;
   int cur0 = 0;  // counter buffer the captured steps start from (and, steps being even, end in)
 };
@@ -658,8 +667,13 @@ void release_graph(rswa_step_graph* g) {
   if (!g) return;
   if (g->exec) (void)hipGraphExecDestroy(g->exec);
   if (g->graph) (void)hipGraphDestroy(g->graph);
+  if (g->exec_uni) (void)hipGraphExecDestroy(g->exec_uni);
+  if (g->graph_uni) (void)hipGraphDestroy(g->graph_uni);
   delete g;
 }
+
+// All sequences share m, capacity and step count, and no active mask has been used.
+bool shares_counts(const rswa_cache* c) { return c->uniform && c->equal_t && !c->masked; }
 
 }  // namespace
 
@@ -694,38 +708,40 @@ rswa_status rswa_step_graph_create(rswa_cache* c, int32_t steps, const void* q_s
     const size_t elem = c->kv_dtype == RSWA_F32 ? 4 : 2;
     const size_t slot = (size_t)c->B * c->H * c->D;
     const size_t oelem = out_dtype == RSWA_F32 ? 4 : 2;
-    e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
-    if (e != hipSuccess) {
-      (void)hipStreamDestroy(cs);
-      release_graph(g);
-      return hip_fail(e, "hipStreamBeginCapture");
-    }
-    rswa_status st = RSWA_OK;
-    for (int i = 0; i < steps && st == RSWA_OK; ++i) {
-      const char* q = reinterpret_cast<const char*>(q_slots) + i * slot * elem;
-      const char* k = reinterpret_cast<const char*>(k_slots) + i * slot * elem;
-      const char* v = reinterpret_cast<const char*>(v_slots) + i * slot * elem;
-      char* o = reinterpret_cast<char*>(out_slots) + i * slot * oelem;
-      st = decode_launch(c, q, k, v, o, out_dtype, softmax_scale, nullptr, cs,
-                         "rswa_step_graph_create", true);
-    }
-    hipGraph_t graph = nullptr;
-    e = hipStreamEndCapture(cs, &graph);
-    g->graph = graph;
-    // capture enqueues nothing: the host view of the cache stays where it was
-    c->calls = calls;
-    c->cur = cur;
-    if (st != RSWA_OK || e != hipSuccess) {
-      (void)hipStreamDestroy(cs);
-      release_graph(g);
-      return st != RSWA_OK ? st : hip_fail(e, "hipStreamEndCapture");
-    }
-    e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
+    // capture the steps in one mode into (graph, exec)
+    auto capture = [&](int mode, hipGraph_t* graph, hipGraphExec_t* exec) -> rswa_status {
+      hipError_t ce = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+      if (ce != hipSuccess) return hip_fail(ce, "hipStreamBeginCapture");
+      rswa_status st = RSWA_OK;
+      for (int i = 0; i < steps && st == RSWA_OK; ++i) {
+        const char* q = reinterpret_cast<const char*>(q_slots) + i * slot * elem;
+        const char* k = reinterpret_cast<const char*>(k_slots) + i * slot * elem;
+        const char* v = reinterpret_cast<const char*>(v_slots) + i * slot * elem;
+        char* o = reinterpret_cast<char*>(out_slots) + i * slot * oelem;
+        st = decode_launch(c, q, k, v, o, out_dtype, softmax_scale, nullptr, cs,
+                           "rswa_step_graph_create", mode);
+      }
+      ce = hipStreamEndCapture(cs, graph);
+      // capture enqueues nothing: the host view of the cache stays where it was
+      c->calls = calls;
+      c->cur = cur;
+      if (st != RSWA_OK) return st;
+      if (ce != hipSuccess) return hip_fail(ce, "hipStreamEndCapture");
+      ce = hipGraphInstantiate(exec, *graph, nullptr, nullptr, 0);
+      if (ce != hipSuccess) {
+        *exec = nullptr;
+        return hip_fail(ce, "hipGraphInstantiate");
+      }
+      return RSWA_OK;
+    };
+    rswa_status st = capture(kCaptureGeneral, &g->graph, &g->exec);
+    if (st == RSWA_OK && shares_counts(c))
+      st = capture(kCaptureUniform, &g->graph_uni, &g->exec_uni);
     (void)hipStreamDestroy(cs);
-    if (e != hipSuccess) {
-      g->exec = nullptr;
+    cs = nullptr;
+    if (st != RSWA_OK) {
       release_graph(g);
-      return hip_fail(e, "hipGraphInstantiate");
+      return st;
     }
     *out = g;
     c->graphs += 1;
@@ -759,7 +775,9 @@ rswa_status rswa_step_graph_launch(rswa_step_graph* g, void* stream) {
       if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(step counters)");
       c->cur = g->cur0;
     }
-    const hipError_t e = hipGraphLaunch(g->exec, st);
+    // the steps that read the shared count while the cache is still in that state
+    hipGraphExec_t exec = g->exec_uni && shares_counts(c) ? g->exec_uni : g->exec;
+    const hipError_t e = hipGraphLaunch(exec, st);
     if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
     for (int b = 0; b < c->B; ++b) c->calls[b] += g->steps;
     return RSWA_OK;
