@@ -96,7 +96,8 @@ uint64_t rswa_cache_bytes(const rswa_cache_desc* desc);
  * DeepEncoder section: visual tokens are encoded once and stay static), set every step counter
  * t_b to 0. prefix_k_dev / prefix_v_dev: packed token-major [sum_b m_b][H][D] of kv_dtype
  * (sequence b's rows follow sequence b-1's); may be NULL only if every m_b is 0. The prefix is
- * copied, not aliased. Rows beyond the prefix are not touched. Enqueued on `stream`.
+ * copied, not aliased. Rows beyond the prefix are not touched. Enqueued on `stream`; the call
+ * BLOCKS until that stream has finished the copies (its metadata upload is staged in host memory).
  * Errors: RSWA_E_INVALID (desc, pointers), RSWA_E_UNSUPPORTED (head_dim), RSWA_E_CAPACITY
  * (storage_bytes too small), RSWA_E_OOM, RSWA_E_HIP. On error *out is NULL. */
 rswa_status rswa_cache_create(const rswa_cache_desc* desc, const void* prefix_k_dev,
@@ -114,7 +115,7 @@ rswa_status rswa_cache_create(const rswa_cache_desc* desc, const void* prefix_k_
  * touched. k_dev / v_dev: packed token-major [total][H][D] of kv_dtype, 16-byte aligned, holding
  * at least cu_seqlens_host[batch] rows (the call has no size to check this against);
  * cu_seqlens_host: host [batch + 1], cu_seqlens_host[0] >= 0, S_b >= m_b. desc->prefix_paged
- * must be 0. Enqueued on `stream`; the call returns once that stream has finished the copies.
+ * must be 0. Enqueued on `stream`; the call BLOCKS until that stream has finished the copies.
  * Errors as rswa_cache_create, plus RSWA_E_INVALID (cu_seqlens, a segment shorter than its
  * prefix, prefix_paged) and RSWA_E_CAPACITY (FULL_CAUSAL: t_b > max_steps). On error *out is
  * NULL. */
@@ -188,8 +189,8 @@ rswa_status rswa_decode_step(rswa_cache* cache, const void* q_dev, const void* k
  * sequences (GeekNews "Unlimited OCR", training section).
  * Sequence s occupies token rows [cu_seqlens[s], cu_seqlens[s+1]) of q/k/v/out (which must hold
  * cu_seqlens[nseq] rows: no row count is passed, so neither the host nor the kernels can check
- * it), its first
- * m_s = prefix_len[s] tokens being the prefix. Query p (position within the sequence) sees key k
+ * it), its first m_s = prefix_len[s] tokens being the prefix. Query p (position within the
+ * sequence) sees key k
  * iff   k < m_s  and (prefix_causal == 0 or p >= m_s or k <= p)          (the reference prefix)
  *    or m_s <= k <= p and p - k < n_s                                   (its own output window)
  * so prefix queries never see outputs; with n_s >= the sequence length this is causal attention
