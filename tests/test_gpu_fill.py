@@ -138,3 +138,20 @@ def test_fill_equal_outputs(wa, full):
     B, m, n, fill = 8, 600, 128, 300
     wl = W.make_decode("fill-equal", 9, "bf16", [m] * B, [n] * B, [fill + 8] * B, seed=12)
     run_case(wa, wl, [fill] * B, wa.MODE_FULL_CAUSAL if full else wa.MODE_RSWA)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_fill_fuzz(wa, seed):
+    """Seeded random batches: sequence count, prefix lengths (0 included), windows down to 1,
+    output counts from 0 past several ring wraps, both modes and both element types."""
+    rng = np.random.default_rng(1000 + seed)
+    B = int(rng.integers(1, 10))
+    m = rng.integers(0, 200, size=B)
+    n = rng.integers(1, 48, size=B)
+    fill = np.array([int(rng.integers(0, 3 * int(n[b]) + 2)) for b in range(B)])
+    m[0] = max(int(m[0]), 1)  # at least one sequence with a prefix (no empty key set at t = 0)
+    m[(fill == 0) & (m == 0)] = 1
+    dtype = "bf16" if seed % 2 == 0 else "f32"
+    full = seed % 4 >= 2
+    wl = W.make_decode(f"fill-fuzz-{seed}", 9, dtype, m, n, fill + 3, seed=2000 + seed)
+    run_case(wa, wl, fill, wa.MODE_FULL_CAUSAL if full else wa.MODE_RSWA, extra=3)
