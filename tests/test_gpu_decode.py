@@ -383,6 +383,30 @@ def test_streamed_steps_sampled(wa, dtype, batch, m):
     tr.cache.close()
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("seed", range(3))
+def test_streamed_steps_fuzz(wa, seed):
+    """Seeded ragged batches whose live rows exceed the last-level cache (streamed steps over
+    device-derived plans): random prefix lengths, windows and step counts, some sequences
+    stopping early (active mask), both modes; sampled steps against the oracle."""
+    rng = np.random.default_rng(3000 + seed)
+    B = int(rng.integers(3, 5))
+    m = rng.integers(11500, 16000, size=B)
+    n = rng.choice([16, 64, 128, 256], size=B)
+    T = int(rng.integers(40, 90))
+    steps = rng.integers(T // 2, T + 1, size=B)
+    steps[0] = T
+    assert int(m.sum()) * 16 * 512 > 256 << 20  # the steps stream
+    mode = seed % 2
+    wl = W.make_decode(f"streamed-fuzz-{seed}", 88, "bf16", m, n, steps, seed=4000 + seed)
+    tr = Trajectory(wa, wl, mode)
+    got = tr.run(sample_steps(T, int(n.min()), int(m.min()), seed=seed, extra=6, crossings=2),
+                 fused=True)
+    worst = check_steps(wl, mode, got, seqs_per_step=2, seed=seed)
+    print(f"streamed fuzz {seed}: worst max-abs error {worst:.3e}")
+    tr.cache.close()
+
+
 # ---------------------------------------------------------------------------------------------
 # the comparison modes of the pages: vanilla sliding window and sink tokens
 # ---------------------------------------------------------------------------------------------
