@@ -74,11 +74,20 @@ struct SeqState {
   bool app;    // this launch appends for b
 };
 
+// Whether the launch has the plan of sequences that share m, capacity and step count, and that
+// count: passed by the host (uni_t >= 0), or, in a captured step, read from the counters.
+__device__ __forceinline__ bool uni_plan(const DecodeArgs& a) {
+  return a.uni_t >= 0 || a.uni_t == kUniFromCounters;
+}
+__device__ __forceinline__ int uni_count(const DecodeArgs& a) {
+  return a.uni_t >= 0 ? a.uni_t : __builtin_amdgcn_readfirstlane(a.steps_in[0]);
+}
+
 __device__ __forceinline__ SeqState seq_state(const DecodeArgs& a, int b) {
   SeqState st;
-  const bool uni = a.uni_t >= 0;
+  const bool uni = uni_plan(a);
   const bool act = uni || !a.active || a.active[b];
-  st.t = uni ? a.uni_t : a.steps_in[b];
+  st.t = uni ? uni_count(a) : a.steps_in[b];
   const int cap = uni ? a.uni_cap : a.meta.cap[b];
   st.app = act && a.k_new != nullptr && (!a.full_causal || st.t < cap);
   const int t_after = st.app ? st.t + 1 : st.t;
@@ -105,7 +114,7 @@ __device__ void build_work_table(const DecodeArgs& a, int* s_len, int* s_new, in
       s_len[b] = st.L;
       rows = (int64_t)a.heads * st.L;
       int rnew = -1;
-      const bool uni = a.uni_t >= 0;
+      const bool uni = uni_plan(a);
       const int m = uni ? a.uni_m : a.meta.prefix_len[b];
       const int cap = uni ? a.uni_cap : a.meta.cap[b];
       if (st.app) rnew = a.full_causal ? m + st.t : m + st.t % cap;
@@ -340,7 +349,7 @@ __device__ __forceinline__ bool decode_range(const DecodeArgs& a, int b, int h, 
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // tile decisions are scalar
   const int g = lane / GL, li = lane % GL;
   const int H = a.heads;
-  const bool uni = a.uni_t >= 0;
+  const bool uni = uni_plan(a);
   const int64_t R = uni ? a.uni_rows : a.meta.rows[b];
   const int m = uni ? a.uni_m : a.meta.prefix_len[b];
   // Cache row r lives at Kh + r * D; with a paged prefix the storage starts at row m, and rows
@@ -572,9 +581,6 @@ __device__ __forceinline__ bool decode_range(const DecodeArgs& a, int b, int h, 
 
 template <typename KV, typename OUT, int U>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
-  // A captured step over sequences that share their step count reads it from the counters: the
-  // rest of the launch is the host-known plan's.
-  if (a.uni_t == kUniFromCounters) a.uni_t = __builtin_amdgcn_readfirstlane(a.steps_in[0]);
   extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
   __shared__ float s_m[kMaxGroups], s_l[kMaxGroups];
   __shared__ float s_acc[kMaxGroups * kHeadDim];
@@ -586,7 +592,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   int* s_new = s_len + a.batch;
   const int H = a.heads;
 
-  if (a.uni_t >= 0 && (a.aligned || a.split > 1)) {
+  if (uni_plan(a) && (a.aligned || a.split > 1)) {
     // Host-known plan over equal ranges: every sequence has the same live rows and new-row slot,
     // so no work table (and none of its barriers) is needed; block 0 advances the counters.
     const SeqState st = seq_state(a, 0);
