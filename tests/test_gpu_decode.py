@@ -273,6 +273,9 @@ FUSED_CASES = [
     ([100, 9], [16, 5], [200, 200], 0, (64, 7)),             # pieces forced, 7 workgroups
     ([50, 0, 130], [8, 8, 8], [150, 150, 150], 1, (0, 0)),  # full causal
     ([5155], [128], [200], 0, (0, 0)),                       # one long range over many pieces
+    # live rows past the 256 MiB last-level cache: streamed steps (non-temporal loads)
+    ([11000] * 3, [64] * 3, [80] * 3, 0, (0, 0)),            # equal ranges, host-known plan
+    ([15000, 9000, 12000], [16, 128, 64], [70, 50, 60], 1, (0, 0)),  # full causal, masked
 ]
 
 
@@ -288,6 +291,12 @@ def test_fused_step_equals_append_then_decode(wa, case):
     b = Trajectory(wa, wl, mode, storage=sb)
     a.cache.set_decode_split(*split)
     b.cache.set_decode_split(*split)
+    if sum(m) * 16 * 512 > 256 << 20 and len(set(m)) == 1 and mode == 0:
+        # the streamed plan: each range cut into pieces over three workgroups per CU
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        ranges = len(m) * 16
+        k = min(3 * cus // ranges, (m[0] + 1) // 64)
+        assert b.cache.decode_plan(appending=True) == (ranges * k, 1)
     steps = range(1, wl.T + 1)
     ra = a.run(steps, raw=True)
     rb = b.run(steps, fused=True, raw=True)
