@@ -40,7 +40,8 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 H, D = 16, 128
 DECODE_SOURCES = ["windowed_attention_amd/csrc/decode.hip", "windowed_attention_amd/csrc/device.h",
-                  "windowed_attention_amd/csrc/kernels.h"]
+                  "windowed_attention_amd/csrc/kernels.h", "windowed_attention_amd/csrc/plan.h",
+                  "windowed_attention_amd/_build.py"]
 PREFILL_SOURCES = ["windowed_attention_amd/csrc/prefill.hip", "windowed_attention_amd/csrc/mfma.h",
                    "windowed_attention_amd/csrc/device.h", "windowed_attention_amd/csrc/kernels.h",
                    "windowed_attention_amd/_build.py"]  # the build script carries per-source flags

@@ -52,6 +52,7 @@
 // never seen.
 #include "device.h"
 #include "kernels.h"
+#include "plan.h"
 
 namespace rswa {
 namespace {
@@ -678,6 +679,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 #define RSWA_DECODE_ROWS 2
 #endif
 constexpr int kRowsPerLane = RSWA_DECODE_ROWS;  // U: rows each lane group loads per tile
+// A tile is loaded whole, so the last tile of the storage's last range may read up to
+// (rows per wave tile - 1) rows past its final row; the storage's unused tail must hold them.
+template <typename KV>
+constexpr uint64_t tile_overread_bytes() {
+  return (uint64_t)(kWave / Lanes<KV>::GL * kRowsPerLane - 1) * kHeadDim * sizeof(KV);
+}
+static_assert(tile_overread_bytes<uint16_t>() <= kStorageTailBytes &&
+                  tile_overread_bytes<float>() <= kStorageTailBytes,
+              "decode tiles would read past the storage tail");
 
 template <typename KV, typename OUT>
 hipError_t launch_typed(const DecodeArgs& a, int grid, hipStream_t s) {
