@@ -323,9 +323,9 @@ __device__ __forceinline__ void merge_range(const DecodeArgs& a, int64_t s, int6
   __syncthreads();
 }
 
-// The four workgroups that share a CU do not progress evenly: the oldest waves win the issue
-// arbitration, so some pieces finish early and the rest then run with a quarter of the CU's waves
-// in flight. A wave lowers its issue priority as its piece progresses (done of total rows), which
+// The workgroups that share a CU (three or four) do not progress evenly: the oldest waves win the
+// issue arbitration, so some pieces finish early and the rest then run with a fraction of the CU's
+// waves in flight. A wave lowers its issue priority as its piece progresses (done of total rows), which
 // hands issue slots to the pieces that are behind.
 __device__ __forceinline__ void yield_by_progress(int64_t done, int64_t total) {
   const int64_t lvl = (4 * done) / total;
