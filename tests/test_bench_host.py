@@ -53,3 +53,14 @@ def test_source_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
     assert bench.source_hash(["k.hip"]) == h0
     src.write_text("int f(int x) { return x + 2; }\n")
     assert bench.source_hash(["k.hip"]) != h0
+
+
+def test_more_than_one_gpu_is_refused():
+    # the bench measures one GPU; any other count exits with status 2 before touching a device
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
