@@ -88,7 +88,9 @@ typedef struct rswa_cache rswa_cache; /* opaque; owned by the library */
 rswa_status rswa_cache_plan(const rswa_cache_desc* desc, int64_t* seq_offset_host /* [B] */,
                             int32_t* rows_host /* [B] */, uint64_t* storage_bytes_host);
 
-/* Bytes of storage the description needs (0 if the description is invalid). Host only. */
+/* Bytes of storage the description needs (0 if the description is invalid). Host only. The size
+ * ends with 4096 bytes after the last row that no row uses: the decode kernel loads whole row
+ * tiles, so the last tile of the last range may read (never use) up to that many bytes past it. */
 uint64_t rswa_cache_bytes(const rswa_cache_desc* desc);
 
 /* Create a cache: take or allocate storage, copy every sequence's prefix K / V into rows
